@@ -1,0 +1,164 @@
+"""Benchmark: routed tokens/s of the fused batch-invariant router on one MI355X.
+
+Workload (the Qwen3-MoE-like router point): M=8192 tokens, K=2048, E=256,
+top-8; x holds bf16-valued activations ~N(0,1) stored as fp32, W is fp32
+~N(0,0.02).  One step is one dr_route call -- canonical-order fp32 logits,
+top-k with the lowest-index tie-break, softmax weights, margins, and the
+[M,E] fp32 logits written back -- on inputs already resident in HBM.
+
+Printed: one JSON line with the throughput, the roofline of the routing
+kernel (fp32 matrix-core FLOPs of the logits GEMM over the kernel's average
+duration, timed with HIP events on the stream the kernel runs on), HBM traffic
+from the committed rocprofv3 counter summary when it still matches the kernel
+sources, an M-invariance and oracle check on sampled rows, and the CPU oracle
+timed on the same workload as a baseline.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, K, E, TOPK = 8192, 2048, 256, 8
+PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix (and vector) peak
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "route_tiled_M8192_K2048_E256_traffic.json")
+KERNEL_SOURCES = ["route_tiled.hip", "route_common.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "deterministic_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes():
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (rows are independent, "
+              "so data-parallel sharding exchanges nothing and per-GPU throughput is the figure)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import deterministic_gemm_amd as dr
+    import workloads as wl
+
+    dr.load_library()
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    x = wl.sweep_x(M, K)
+    W = wl.router_weights(K, E)
+    xd = torch.from_numpy(x).to(dev)
+    Wd = torch.from_numpy(W).to(dev)
+    out = (torch.empty((M, TOPK), dtype=torch.int32, device=dev),
+           torch.empty((M, TOPK), dtype=torch.float32, device=dev),
+           torch.empty((M, E), dtype=torch.float32, device=dev),
+           torch.empty((M, 4), dtype=torch.int32, device=dev))
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        dr.route(xd, Wd, TOPK, out=out)
+    torch.cuda.synchronize()
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        dr.route(xd, Wd, TOPK, out=out)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    tokens_per_s = M / (ms_step * 1e-3)
+
+    # M-invariance and oracle parity on sampled rows (outside the timed region)
+    ids_full = out[0].cpu().numpy()
+    lg_full = out[2].cpu().numpy()
+    inv = True
+    for m_small in (1, 19, 65, 75, 1024):
+        ids_s, _, lg_s, _ = dr.route(xd[:m_small].contiguous(), Wd, TOPK)
+        torch.cuda.synchronize()
+        inv &= bool(np.array_equal(ids_s.cpu().numpy(), ids_full[:m_small]))
+        inv &= bool(np.array_equal(lg_s.cpu().numpy().view(np.uint32), lg_full[:m_small].view(np.uint32)))
+
+    flops = 2.0 * M * K * E
+    achieved_tflops = flops / (ms_step * 1e-3) / 1e12
+    tb = traffic_bytes()
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(achieved_tflops, 2),
+        "peak": PEAK_FP32_MATRIX_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved_tflops / PEAK_FP32_MATRIX_TFLOPS, 4),
+        "traffic": tb,
+    }
+
+    result = {
+        "metric": "routed tokens/sec at M=8192,K=2048,E=256,k=8 (+% FP32 roofline); M-invariance pass",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "router sweep point M=8192 K=2048 E=256 k=8 (bf16-valued fp32 x, fp32 W)",
+                   "M": M, "K": K, "E": E, "k": TOPK, "outputs": "ids, weights, fp32 logits, margins",
+                   "kernel": dr.auto_variant(M, K, E)},
+        "roofline": roofline,
+        "m_invariance": inv,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        nthreads = min(16, oracle.default_threads())
+        sample = M  # the whole batch: about 9 CPU-seconds of fmaf work
+        t0 = time.perf_counter()
+        rids, rw, rlg, rmg = oracle.route(x[:sample], W, TOPK, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        parity = bool(np.array_equal(rids, ids_full[:sample]) and
+                      np.array_equal(rlg.view(np.uint32), lg_full[:sample].view(np.uint32)))
+        result["cpu_baseline"] = {"value": round(sample / dt, 1), "unit": "tokens/s", "cores": nthreads,
+                                  "kind": "oracle",
+                                  "sample": f"all {sample} tokens of the workload, one oracle call, wall clock"}
+        result["oracle_parity"] = parity
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

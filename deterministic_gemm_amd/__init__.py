@@ -1,0 +1,204 @@
+"""Python binding of libdr.so (include/dr.h): batch-invariant MoE routing on
+MI355X.
+
+Argument marshalling only.  torch supplies device memory and the current HIP
+stream; every step of the computation runs in the library's HIP kernels.
+There is no CPU fallback: if the library is not built, or a tensor is not on
+the GPU, the call raises.
+
+    ids, weights, logits, margins = route(x, W, k)
+
+x is [M,K] float32 or bfloat16 on the GPU, W is [K,E] float32.  The functions
+mirror the C entry points: route -> dr_route, route_variant ->
+dr_route_variant, gate_dot -> dr_gate_dot, gemm_bf16 -> dr_gemm_bf16,
+contract -> dr_contract.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdr.so")
+
+DR_OK, DR_ERR_INVALID, DR_ERR_UNSUPPORTED, DR_ERR_DEVICE = 0, 1, 2, 3
+DR_F32, DR_BF16 = 0, 1
+VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2}
+VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
+DR_ROUTE_RENORMALIZE = 1
+
+# dr_margin, 16 bytes per token
+MARGIN_DTYPE = np.dtype(
+    [("sel_min", "<f4"), ("rej_max", "<f4"), ("sel_min_bf16", "<u2"), ("rej_max_bf16", "<u2"), ("ulps", "<i4")]
+)
+
+EXPORTED = (
+    "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_gate_dot", "dr_gemm_bf16",
+    "dr_contract", "dr_status_string", "dr_last_error",
+)
+
+
+class DrError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: status {status} ({detail})")
+        self.status = status
+
+
+class _Contract(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("version", "kblock", "tree", "acc_bits", "fma", "exp_id", "tie_break", "max_k")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdr.so (build it first with deterministic_gemm_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run python -m deterministic_gemm_amd.build")
+    L = ctypes.CDLL(path)
+    P, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
+    L.dr_route.argtypes = [P, ctypes.c_int, P, i64, i64, i64, i32, ctypes.c_int, P, P, P, P, u32, P]
+    L.dr_route.restype = ctypes.c_int
+    L.dr_route_variant.argtypes = [P, ctypes.c_int, P, i64, i64, i64, i32, ctypes.c_int, P, P, P, P, u32,
+                                   ctypes.c_int, P]
+    L.dr_route_variant.restype = ctypes.c_int
+    L.dr_route_auto_variant.argtypes = [i64, i64, i64]
+    L.dr_route_auto_variant.restype = ctypes.c_int
+    L.dr_gate_dot.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P, i64, i64, P]
+    L.dr_gate_dot.restype = ctypes.c_int
+    L.dr_gemm_bf16.argtypes = [P, P, P, i64, i64, i64, P]
+    L.dr_gemm_bf16.restype = ctypes.c_int
+    L.dr_contract.argtypes = [ctypes.POINTER(_Contract)]
+    L.dr_contract.restype = None
+    L.dr_status_string.argtypes = [ctypes.c_int]
+    L.dr_status_string.restype = ctypes.c_char_p
+    L.dr_last_error.argtypes = []
+    L.dr_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str):
+    if status != DR_OK:
+        L = load_library()
+        detail = L.dr_last_error().decode() or L.dr_status_string(status).decode()
+        raise DrError(status, where, detail)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(t, name, dtypes):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def contract() -> dict:
+    c = _Contract()
+    load_library().dr_contract(ctypes.byref(c))
+    return {n: getattr(c, n) for n, _ in _Contract._fields_}
+
+
+def auto_variant(M: int, K: int, E: int) -> str:
+    return VARIANT_NAMES[load_library().dr_route_auto_variant(M, K, E)]
+
+
+def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, logits: bool = True,
+          weights: bool = True, margins: bool = True, variant: str = "auto", out=None):
+    """dr_route / dr_route_variant.  Returns (ids [M,k] int32, weights [M,k]
+    float32 or None, logits [M,E] float32/bfloat16 or None, margins [M,4] int32
+    raw dr_margin records or None).  `out` may pass preallocated tensors as a
+    tuple in the same order."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
+    _dev_tensor(W, "W", (torch.float32,))
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[0]:
+        raise ValueError("x must be [M,K] and W [K,E]")
+    M, K = x.shape
+    E = W.shape[1]
+    dev = x.device
+    ldt = {"f32": DR_F32, "bf16": DR_BF16}[logit_dtype]
+    if out is not None:
+        ids_t, w_t, lg_t, mg_t = out
+    else:
+        ids_t = torch.empty((M, k), dtype=torch.int32, device=dev)
+        w_t = torch.empty((M, k), dtype=torch.float32, device=dev) if weights else None
+        lg_t = (torch.empty((M, E), dtype=torch.float32 if ldt == DR_F32 else torch.bfloat16, device=dev)
+                if logits else None)
+        mg_t = torch.empty((M, 4), dtype=torch.int32, device=dev) if margins else None
+    xd = DR_F32 if x.dtype == torch.float32 else DR_BF16
+    flags = DR_ROUTE_RENORMALIZE if renormalize else 0
+    v = VARIANTS[variant]
+    if v == 0:
+        st = L.dr_route(_ptr(x), xd, _ptr(W), M, K, E, k, ldt, _ptr(ids_t), _ptr(w_t), _ptr(lg_t), _ptr(mg_t),
+                        flags, _stream(dev))
+    else:
+        st = L.dr_route_variant(_ptr(x), xd, _ptr(W), M, K, E, k, ldt, _ptr(ids_t), _ptr(w_t), _ptr(lg_t),
+                                _ptr(mg_t), flags, v, _stream(dev))
+    _check(st, "dr_route")
+    return ids_t, w_t, lg_t, mg_t
+
+
+def route_variant(x, W, k: int, variant: str, **kw):
+    return route(x, W, k, variant=variant, **kw)
+
+
+def gate_dot(x, w, *, dot: bool = True, gate: bool = True):
+    """dr_gate_dot: returns (dot [M] float32 or None, gate [M] float32 or None)."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
+    _dev_tensor(w, "w", (torch.float32, torch.bfloat16))
+    M, K = x.shape
+    if w.shape != (K,):
+        raise ValueError("w must be [K]")
+    d = torch.empty((M,), dtype=torch.float32, device=x.device) if dot else None
+    g = torch.empty((M,), dtype=torch.float32, device=x.device) if gate else None
+    st = L.dr_gate_dot(_ptr(x), DR_F32 if x.dtype == torch.float32 else DR_BF16, _ptr(w),
+                       DR_F32 if w.dtype == torch.float32 else DR_BF16, _ptr(d), _ptr(g), M, K, _stream(x.device))
+    _check(st, "dr_gate_dot")
+    return d, g
+
+
+def gemm_bf16(x, W, out=None):
+    """dr_gemm_bf16: x [M,K] bfloat16, W [K,N] bfloat16 -> out [M,N] float32."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.bfloat16,))
+    _dev_tensor(W, "W", (torch.bfloat16,))
+    M, K = x.shape
+    K2, N = W.shape
+    if K != K2:
+        raise ValueError("inner sizes differ")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    st = L.dr_gemm_bf16(_ptr(x), _ptr(W), _ptr(out), M, K, N, _stream(x.device))
+    _check(st, "dr_gemm_bf16")
+    return out
+
+
+def margins_to_numpy(mg: torch.Tensor) -> np.ndarray:
+    """Raw [M,4] int32 dr_margin records -> numpy structured array."""
+    return np.ascontiguousarray(mg.cpu().numpy()).view(MARGIN_DTYPE).reshape(-1)
+
+
+dr_route = route
+dr_route_variant = route_variant
+dr_gate_dot = gate_dot
+dr_gemm_bf16 = gemm_bf16
+dr_contract = contract

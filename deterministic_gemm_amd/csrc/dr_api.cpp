@@ -1,0 +1,171 @@
+// dr_api.cpp -- the C ABI of include/dr.h: argument validation, the choice
+// of kernel family and tile from the shape alone, and the launch on the
+// caller's stream.  No numeric decision is made here: every variant computes
+// the same canonical order.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "../../include/dr.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+dr_status fail(dr_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+dr_status device_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return DR_OK;
+  return fail(DR_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxK = 16384;
+constexpr int32_t kMaxTopK = 32;
+constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
+
+// Batches at or above this size run on the matrix-core kernel.  The value sits
+// inside the 19..80 token m-scan on purpose, so that scan crosses a dispatch
+// change and shows it cannot move a bit.
+constexpr int64_t kTiledMinM = 48;
+
+dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
+                     int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
+                     void *logits, dr_margin *margins, uint32_t flags, dr_variant variant,
+                     void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || M > kMaxM) return fail(DR_ERR_INVALID, "M=%lld out of range", (long long)M);
+  if (K < 1) return fail(DR_ERR_INVALID, "K=%lld must be >= 1", (long long)K);
+  if (E < 1) return fail(DR_ERR_INVALID, "E=%lld must be >= 1", (long long)E);
+  if (k < 1 || k > E) return fail(DR_ERR_INVALID, "k=%d must be in [1, E=%lld]", k, (long long)E);
+  if (x_dtype != DR_F32 && x_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad x_dtype");
+  if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
+  if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (variant != DR_VARIANT_AUTO && variant != DR_VARIANT_ROWWISE && variant != DR_VARIANT_TILED)
+    return fail(DR_ERR_INVALID, "bad variant");
+  if (M > 0 && (!x || !W || !ids)) return fail(DR_ERR_INVALID, "x, W and ids are required");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(ids) || !aligned16(weights) || !aligned16(logits) ||
+      !aligned16(margins))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (!(E == 64 || E == 128 || E == 256 || E == 512 || E == 1024))
+    return fail(DR_ERR_UNSUPPORTED, "E=%lld: supported E are 64, 128, 256, 512, 1024", (long long)E);
+  if (K > kMaxK) return fail(DR_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K, (long long)kMaxK);
+  if (k > kMaxTopK) return fail(DR_ERR_UNSUPPORTED, "k=%d above %d", k, kMaxTopK);
+  if (variant == DR_VARIANT_AUTO) variant = dr_route_auto_variant(M, K, E);
+  if (variant == DR_VARIANT_TILED && !drk::tiled_supports(E, K))
+    return fail(DR_ERR_UNSUPPORTED, "tiled variant does not support E=%lld", (long long)E);
+  if (M == 0) return DR_OK;
+
+  drk::RouteLaunch L;
+  L.xf = x_dtype == DR_F32 ? static_cast<const float *>(x) : nullptr;
+  L.xb = x_dtype == DR_BF16 ? static_cast<const uint16_t *>(x) : nullptr;
+  L.W = W;
+  L.M = M;
+  L.K = K;
+  L.E = E;
+  L.k = k;
+  L.logit_bf16 = logit_dtype == DR_BF16;
+  L.flags = flags;
+  L.ids = ids;
+  L.weights = weights;
+  L.logits = logits;
+  L.margins = margins;
+  L.stream = static_cast<hipStream_t>(stream);
+  const hipError_t e =
+      variant == DR_VARIANT_TILED ? drk::launch_route_tiled(L) : drk::launch_route_rowwise(L);
+  return device_status(e, "route launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E) {
+  if (M >= kTiledMinM && drk::tiled_supports(E, K)) return DR_VARIANT_TILED;
+  return DR_VARIANT_ROWWISE;
+}
+
+dr_status dr_route(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
+                   int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
+                   void *logits, dr_margin *margins, uint32_t flags, void *stream) {
+  return route_impl(x, x_dtype, W, M, K, E, k, logit_dtype, ids, weights, logits, margins, flags,
+                    DR_VARIANT_AUTO, stream);
+}
+
+dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
+                           int64_t K, int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids,
+                           float *weights, void *logits, dr_margin *margins, uint32_t flags,
+                           dr_variant variant, void *stream) {
+  return route_impl(x, x_dtype, W, M, K, E, k, logit_dtype, ids, weights, logits, margins, flags,
+                    variant, stream);
+}
+
+dr_status dr_gate_dot(const void *x, dr_dtype x_dtype, const void *w, dr_dtype w_dtype,
+                      float *dot, float *gate, int64_t M, int64_t K, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || M > kMaxM) return fail(DR_ERR_INVALID, "M=%lld out of range", (long long)M);
+  if (K < 1) return fail(DR_ERR_INVALID, "K=%lld must be >= 1", (long long)K);
+  if ((x_dtype != DR_F32 && x_dtype != DR_BF16) || (w_dtype != DR_F32 && w_dtype != DR_BF16))
+    return fail(DR_ERR_INVALID, "bad dtype");
+  if (M > 0 && (!x || !w)) return fail(DR_ERR_INVALID, "x and w are required");
+  if (M > 0 && !dot && !gate) return fail(DR_ERR_INVALID, "one of dot, gate is required");
+  if (!aligned16(x) || !aligned16(w) || !aligned16(dot) || !aligned16(gate))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (K > kMaxK) return fail(DR_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K, (long long)kMaxK);
+  if (M == 0) return DR_OK;
+  return device_status(drk::launch_gate_dot(x, x_dtype == DR_BF16, w, w_dtype == DR_BF16, dot, gate, M, K,
+                                            static_cast<hipStream_t>(stream)),
+                       "gate_dot launch");
+}
+
+dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K,
+                       int64_t N, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || K < 1 || N < 1) return fail(DR_ERR_INVALID, "bad sizes");
+  if (M > 0 && (!x || !W || !out)) return fail(DR_ERR_INVALID, "x, W and out are required");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(out))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (K % 32 != 0 || N % 128 != 0)
+    return fail(DR_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 128");
+  if (K > (int64_t(1) << 30) || N > (int64_t(1) << 30) || M > int64_t(65535) * 128)
+    return fail(DR_ERR_UNSUPPORTED, "size out of range");
+  if (M == 0) return DR_OK;
+  return device_status(drk::launch_gemm_bf16(x, W, out, M, K, N, static_cast<hipStream_t>(stream)),
+                       "gemm launch");
+}
+
+void dr_contract(dr_contract_info *out) {
+  if (!out) return;
+  out->version = 1;
+  out->kblock = 256;
+  out->tree = 1;
+  out->acc_bits = 32;
+  out->fma = 1;
+  out->exp_id = 1;
+  out->tie_break = 1;
+  out->max_k = kMaxTopK;
+}
+
+const char *dr_status_string(dr_status s) {
+  switch (s) {
+    case DR_OK: return "ok";
+    case DR_ERR_INVALID: return "invalid argument";
+    case DR_ERR_UNSUPPORTED: return "unsupported shape";
+    case DR_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char *dr_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,36 @@
+// launch.h -- host-side description of one validated dr_route call, handed
+// from the C ABI (dr_api.cpp) to the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dr.h"
+
+namespace drk {
+
+struct RouteLaunch {
+  const float *xf;     // x as fp32, or NULL
+  const uint16_t *xb;  // x as bf16 bits, or NULL
+  const float *W;
+  int64_t M, K, E;
+  int k;
+  int logit_bf16;
+  uint32_t flags;
+  int32_t *ids;
+  float *weights;
+  void *logits;
+  dr_margin *margins;
+  hipStream_t stream;
+};
+
+hipError_t launch_route_rowwise(const RouteLaunch &L);
+hipError_t launch_route_tiled(const RouteLaunch &L);
+bool tiled_supports(int64_t E, int64_t K);
+
+hipError_t launch_gate_dot(const void *x, int x_bf16, const void *w, int w_bf16, float *dot,
+                           float *gate, int64_t M, int64_t K, hipStream_t stream);
+hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
+                            int64_t K, int64_t N, hipStream_t stream);
+
+}  // namespace drk

@@ -1,0 +1,241 @@
+// route_tiled.hip -- the batched routing kernel on fp32 matrix cores.
+//
+// gfx950's v_mfma_f32_16x16x1_4b_f32 performs, for four independent 16x16
+// blocks, one step acc[i][j] <- fma(a[i], b[j], acc[i][j]) with a single
+// rounding: the same operation as one step of the canonical fmaf chain (this
+// is checked bit for bit against CPU fmaf chains, subnormals and signed zeros
+// included, by the parity tests).  The kernel uses the four blocks of that
+// instruction for four consecutive K-blocks of the SAME 16x16 (token, expert)
+// tile: slot s of group g runs the chain of K-block 4g+s.  After 256 steps the
+// four partials of a tile sit in the same lane, and the first two levels of
+// the canonical pairwise tree are lane-local adds; groups are then folded by
+// the counter tree.  So every output is produced by exactly the operations of
+// the canonical order -- the tile shape and the token count only decide which
+// lane performs them ("Batch changed the model's mind", section "The fix:
+// m-invariant twins": a batched twin bit-identical per row to the per-row
+// kernel is "a perf seam, not a numeric one").
+//
+// Steps of a chain past the end of K, and slots past the last K-block, are
+// fed x = -0.0 and W = +0.0: fma(-0, +0, c) == c exactly for every c, so the
+// padding changes no bit; an absent slot starts at -0.0, the identity of the
+// tree's additions.
+//
+// Work decomposition (E=256): a workgroup of 8 wavefronts takes 32 tokens
+// and all E experts; wavefront w owns experts 32w..32w+31 as 2x2 tiles of
+// 16x16.  K is walked in chunks of KC steps of all four slots: a chunk of x
+// (4 slots x 32 tokens x KC) and of W (4 slots x KC rows x E) is prefetched
+// into registers while the previous chunk is consumed from LDS.
+#include "route_common.h"
+#include "launch.h"
+
+namespace drk {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int E_, int AT_, int BT_, int KC_>
+struct TiledCfg {
+  static constexpr int E = E_;
+  static constexpr int AT = AT_;             // 16-token sub-tiles per wavefront
+  static constexpr int BT = BT_;             // 16-expert sub-tiles per wavefront
+  static constexpr int KC = KC_;             // chain steps per chunk
+  static constexpr int EW = 16 * BT;         // experts per wavefront
+  static constexpr int NW = E / EW;          // wavefronts per workgroup
+  static constexpr int NT = NW * 64;         // threads per workgroup
+  static constexpr int TT = 16 * AT;         // tokens per workgroup
+  static constexpr int XP = KC + 4;          // x row pitch in LDS (floats)
+  static constexpr int XS = 4 * TT * XP;     // x chunk floats
+  static constexpr int WSLOT = KC * E + 16;  // W slot stride (floats), +16 staggers banks
+  static constexpr int WS = 4 * WSLOT;
+  static constexpr int LGP = E + 4;          // logit row pitch for the epilogue
+  static constexpr int LDS = (XS + WS > TT * LGP) ? XS + WS : TT * LGP;
+  static constexpr int XL = 4 * TT * KC / NT;      // x floats per thread per chunk
+  static constexpr int WL = 4 * KC * (E / 4) / NT; // W float4s per thread per chunk
+  static constexpr int CPG = 256 / KC;             // chunks per group of 4 K-blocks
+  static_assert(XL >= 1 && XL * NT == 4 * TT * KC, "x chunk must split evenly");
+  static_assert(WL >= 1 && WL * NT == 4 * KC * (E / 4), "W chunk must split evenly");
+  static_assert(KC % 4 == 0 && 256 % KC == 0, "chunk length");
+};
+
+template <class C, int MAXL>
+__global__ __launch_bounds__(C::NT) void route_tiled_kernel(const float *__restrict__ xf,
+                                                            const uint16_t *__restrict__ xb,
+                                                            const float *__restrict__ W, int64_t M,
+                                                            int K, EpilogueArgs ea) {
+  constexpr int E = C::E, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, NT = C::NT;
+  __shared__ __attribute__((aligned(16))) float smem[C::LDS];
+  float *xs = smem;
+  float *ws = smem + C::XS;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int s_l = lane >> 4, r_l = lane & 15;
+  const int eb = wave * C::EW;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * TT;
+  const int nb = (K + 255) / 256;
+  const int G = (nb + 3) / 4;
+  const int nchunks = G * C::CPG;
+
+  float xr[C::XL];
+  float4 wr[C::WL];
+
+  auto load_chunk = [&](int ci) {
+    const int g = ci / C::CPG;
+    const int kk0 = (ci % C::CPG) * KC;
+#pragma unroll
+    for (int i = 0; i < C::XL; ++i) {
+      const int idx = t + NT * i;
+      const int c = idx % KC, tok = (idx / KC) % TT, s = idx / (KC * TT);
+      const int blk = 4 * g + s;
+      const int kg = blk * 256 + kk0 + c;
+      const int64_t m = m0 + tok;
+      float v = -0.0f;
+      if (blk < nb && kg < K && m < M) {
+        const int64_t off = m * K + kg;
+        v = xb ? bf16_to_f32(xb[off]) : xf[off];
+      }
+      xr[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < C::WL; ++i) {
+      const int idx = t + NT * i;
+      const int e4 = idx % (E / 4), c = (idx / (E / 4)) % KC, s = idx / ((E / 4) * KC);
+      const int blk = 4 * g + s;
+      const int kg = blk * 256 + kk0 + c;
+      float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (blk < nb && kg < K) v = *reinterpret_cast<const float4 *>(W + static_cast<int64_t>(kg) * E + 4 * e4);
+      wr[i] = v;
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int i = 0; i < C::XL; ++i) {
+      const int idx = t + NT * i;
+      const int c = idx % KC, tok = (idx / KC) % TT, s = idx / (KC * TT);
+      xs[(s * TT + tok) * C::XP + c] = xr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::WL; ++i) {
+      const int idx = t + NT * i;
+      const int e4 = idx % (E / 4), c = (idx / (E / 4)) % KC, s = idx / ((E / 4) * KC);
+      *reinterpret_cast<float4 *>(&ws[s * C::WSLOT + c * E + 4 * e4]) = wr[i];
+    }
+  };
+
+  f32x16 acc[AT][BT];
+  float stk[MAXL][AT * BT * 4];
+
+  load_chunk(0);
+  for (int ci = 0; ci < nchunks; ++ci) {
+    const int g = ci / C::CPG;
+    const int cg = ci % C::CPG;
+    if (cg == 0) {
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float init = (4 * g + s < nb) ? 0.0f : -0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[a][b][4 * s + q] = init;
+          }
+    }
+    __syncthreads();
+    store_chunk();
+    __syncthreads();
+    if (ci + 1 < nchunks) load_chunk(ci + 1);
+
+#pragma unroll
+    for (int c4 = 0; c4 < KC / 4; ++c4) {
+      float4 av[AT];
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+        av[a] = *reinterpret_cast<const float4 *>(&xs[(s_l * TT + a * 16 + r_l) * C::XP + 4 * c4]);
+      float bw[BT][4];
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bw[b][q] = ws[s_l * C::WSLOT + (4 * c4 + q) * E + eb + b * 16 + r_l];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int a = 0; a < AT; ++a)
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            const float aval = (q == 0) ? av[a].x : (q == 1) ? av[a].y : (q == 2) ? av[a].z : av[a].w;
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[b][q], acc[a][b], 0, 0, 0);
+          }
+    }
+
+    if (cg == C::CPG - 1) {
+      // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
+      float qv[AT * BT * 4];
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            qv[(a * BT + b) * 4 + q] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
+      tree_push<MAXL, AT * BT * 4>(stk, qv, g);
+    }
+  }
+
+  float out[AT * BT * 4];
+  tree_final<MAXL, AT * BT * 4>(stk, G, out);
+
+  __syncthreads();
+  float *lg = smem;
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tok = a * 16 + 4 * s_l + q;
+        const int e = eb + b * 16 + r_l;
+        lg[tok * C::LGP + e] = out[(a * BT + b) * 4 + q];
+      }
+  __syncthreads();
+  for (int i = wave; i < TT; i += C::NW) {
+    const int64_t mm = m0 + i;
+    if (mm < M) route_token<E>(lg + i * C::LGP, mm, ea);
+  }
+}
+
+template <class C, int MAXL>
+static hipError_t launch_tiled_cm(const RouteLaunch &L) {
+  const int64_t nblk = (L.M + C::TT - 1) / C::TT;
+  EpilogueArgs ea{L.k, L.logit_bf16, L.flags, L.ids, L.weights, L.logits, L.margins};
+  hipLaunchKernelGGL((route_tiled_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0, L.stream,
+                     L.xf, L.xb, L.W, L.M, static_cast<int>(L.K), ea);
+  return hipGetLastError();
+}
+
+template <class C>
+static hipError_t launch_tiled_c(const RouteLaunch &L) {
+  const int64_t nb = (L.K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  // stack depth = bit length of the number of groups
+  if (G <= 1) return launch_tiled_cm<C, 1>(L);
+  if (G <= 2) return launch_tiled_cm<C, 2>(L);
+  if (G <= 4) return launch_tiled_cm<C, 3>(L);
+  if (G <= 8) return launch_tiled_cm<C, 4>(L);
+  return launch_tiled_cm<C, 5>(L);
+}
+
+bool tiled_supports(int64_t E, int64_t K) {
+  return (E == 64 || E == 128 || E == 256 || E == 512) && K >= 1 && K <= 16384;
+}
+
+hipError_t launch_route_tiled(const RouteLaunch &L) {
+  switch (L.E) {
+    case 64: return launch_tiled_c<TiledCfg<64, 2, 2, 16>>(L);
+    case 128: return launch_tiled_c<TiledCfg<128, 2, 2, 16>>(L);
+    case 256: return launch_tiled_c<TiledCfg<256, 2, 2, 16>>(L);
+    case 512: return launch_tiled_c<TiledCfg<512, 1, 4, 8>>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace drk

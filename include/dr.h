@@ -1,0 +1,162 @@
+/*
+ * dr.h -- batch-invariant MoE routing on MI355X (gfx950): the C ABI.
+ *
+ * The problem, as the pages state it ("Batch changed the model's mind",
+ * sections "m-scan: the staircase" and "The fix: m-invariant twins"): a MoE
+ * router is an fp32 GEMM logits = x[M,K] . W[K,E] feeding top_k(k of E); a
+ * GEMM library that picks its split-K factor, tile or reduction order from M
+ * makes a token's logits -- and, at a near-tie, its expert set -- depend on
+ * how many other tokens share the call.  This library fixes one reduction
+ * order per output that no launch parameter can change:
+ *
+ *   logit[m,e] = T( c_0, ..., c_{nb-1} ),   nb = ceil(K / 256)
+ *   c_b        = fmaf chain from +0 over k = 256b, 256b+1, ... (ascending),
+ *                c <- fmaf(x[m,k], W[k,e], c)
+ *   T          = pairwise tree: adjacent pairs combined level by level, an
+ *                odd last element carried up a level unchanged.
+ *
+ * ("The Illusion of Determinism in Disaggregated Inference", section "The
+ * anatomy of the missing numeric contract": accumulator precision and the
+ * associative grouping of the K reduction are what a numeric contract must
+ * state; dr_contract() reports them.)  Every kernel variant and tile size is a
+ * different schedule of exactly these operations, so results are bit-identical
+ * for every M, every position of a row in the batch and every variant.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers owned by the caller (the library keeps none
+ *    after returning), row-major and contiguous, 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous on that stream and never synchronise the device.
+ *  - The library allocates no device memory and uses no atomics.
+ *  - Arguments are validated before any launch; on a non-OK status no kernel
+ *    was launched and outputs are untouched.  DR_ERR_DEVICE means a launch
+ *    failed; dr_last_error() then holds the HIP error text.
+ *  - M == 0 returns DR_OK without launching anything.
+ */
+#ifndef DR_H
+#define DR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dr_status {
+  DR_OK = 0,
+  DR_ERR_INVALID = 1,      /* NULL required pointer, bad size, k > E, misaligned pointer */
+  DR_ERR_UNSUPPORTED = 2,  /* a shape the GPU path does not implement (see each call) */
+  DR_ERR_DEVICE = 3        /* a HIP call or launch failed */
+} dr_status;
+
+typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+
+/* Kernel families for dr_route.  All produce identical bits; AUTO picks one
+ * from M and E only.  Forcing one is a test seam, never a numeric switch. */
+typedef enum dr_variant {
+  DR_VARIANT_AUTO = 0,
+  DR_VARIANT_ROWWISE = 1, /* few tokens per workgroup, vector FMA (small M) */
+  DR_VARIANT_TILED = 2    /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
+} dr_variant;
+
+/* Divide the k selected weights by their sum (left to right in rank order). */
+#define DR_ROUTE_RENORMALIZE 0x1u
+
+/* Per-token margin, 16 bytes (vllm.cpp PR #2556, section "Why a value tap
+ * could never have said this": the smallest selected and the largest rejected
+ * logit with their raw bf16 bit patterns, and the margin counted in bf16 ULPs
+ * under the sign-magnitude total order -- 0 means the same bf16 value). */
+typedef struct dr_margin {
+  float sel_min;          /* logit of rank k-1 (the value the selection saw)    */
+  float rej_max;          /* logit of rank k; -inf when k == E                  */
+  uint16_t sel_min_bf16;  /* bf16 RNE bits of sel_min                           */
+  uint16_t rej_max_bf16;  /* bf16 RNE bits of rej_max                           */
+  int32_t ulps;           /* ord(sel) - ord(rej), ord(b) = b<0x8000 ? b : -(b&0x7FFF);
+                             INT32_MAX when k == E                              */
+} dr_margin;
+
+/* The numeric contract of this build. */
+typedef struct dr_contract_info {
+  int32_t version;    /* 1 */
+  int32_t kblock;     /* 256: K-block length of each sequential fmaf chain   */
+  int32_t tree;       /* 1: level-by-level adjacent pairs, odd element carried */
+  int32_t acc_bits;   /* 32: fp32 accumulation everywhere                     */
+  int32_t fma;        /* 1: every product-accumulate is one fused multiply-add */
+  int32_t exp_id;     /* 1: Cody-Waite, degree-7 Taylor, exact 2^n scale, t<-87 -> 0 */
+  int32_t tie_break;  /* 1: equal values rank by ascending expert index       */
+  int32_t max_k;      /* largest supported k                                  */
+} dr_contract_info;
+
+/*
+ * dr_route -- the fused router: logits, top-k, softmax weights, margins.
+ *
+ *   x        [M,K] activations; DR_F32, or DR_BF16 bits widened exactly to fp32.
+ *   W        [K,E] router weight, fp32.
+ *   k        experts per token, 1 <= k <= min(E, 32).
+ *   logit_dtype  DR_F32: select on the fp32 logits.  DR_BF16: round each
+ *            logit to bf16 (RNE) first and select on those values, as an
+ *            engine with a bf16 gate does (vllm.cpp PR #2556, section "Why it
+ *            is not a defect").
+ *   ids      [M,k] int32, required: expert ids in rank order -- larger logit
+ *            first, equal logits by ascending expert index (vllm.cpp PR
+ *            #2556, summary: the lowest-index tie-break).  NaN ranks last.
+ *   weights  [M,k] fp32 or NULL: softmax over all E logits (max-subtracted,
+ *            exp as in dr_contract_info.exp_id, denominator summed by the
+ *            pairwise tree in expert order, one IEEE division), gathered at
+ *            ids; renormalised over the k when flags has DR_ROUTE_RENORMALIZE.
+ *   logits   [M,E] of logit_dtype, or NULL: the values the selection saw.
+ *   margins  [M] or NULL.
+ *
+ * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32.
+ * Other shapes return DR_ERR_UNSUPPORTED (no silent change of numeric path).
+ */
+dr_status dr_route(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
+                   int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
+                   void *logits, dr_margin *margins, uint32_t flags, void *stream);
+
+/* dr_route with the kernel family forced.  Same bits as dr_route. */
+dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
+                           int64_t K, int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids,
+                           float *weights, void *logits, dr_margin *margins, uint32_t flags,
+                           dr_variant variant, void *stream);
+
+/* The family AUTO picks for (M, E): a pure function of the shape. */
+dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E);
+
+/*
+ * dr_gate_dot -- shared-expert gate ("Batch changed the model's mind",
+ * section "m-scan: the staircase": a one-output dot that must be m-invariant
+ * like the router).  dot[m] = the canonical order above with E = 1;
+ * gate[m] = sigmoid(dot[m]) = 1/(1+e) for dot >= 0, e/(1+e) otherwise, with
+ * e = exp(-|dot|) from the contract's exp.
+ *   x [M,K] (f32 or bf16), w [K] (f32 or bf16), dot [M] fp32 or NULL,
+ *   gate [M] fp32 or NULL.  1 <= K <= 16384.
+ */
+dr_status dr_gate_dot(const void *x, dr_dtype x_dtype, const void *w, dr_dtype w_dtype,
+                      float *dot, float *gate, int64_t M, int64_t K, void *stream);
+
+/*
+ * dr_gemm_bf16 -- batch-invariant dense GEMM out[M,N] = x[M,K] . W[K,N] on
+ * bf16 matrix cores with fp32 accumulation ("The Illusion of Determinism in
+ * Disaggregated Inference", section "The arithmetic cost of batch-invariant
+ * kernels": a static reduction order regardless of the input shape).  Every
+ * output row is reduced by the same sequence of MFMA instructions over K
+ * whatever M is, so rows are bit-identical across M; the order inside one MFMA
+ * is the hardware's, so the result is within a tolerance of the exact product,
+ * not bit-equal to a CPU fmaf chain.
+ *   x [M,K] bf16 bits, W [K,N] bf16 bits, out [M,N] fp32.
+ *   K % 64 == 0 and N % 64 == 0, else DR_ERR_UNSUPPORTED.
+ */
+dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K,
+                       int64_t N, void *stream);
+
+void dr_contract(dr_contract_info *out);
+const char *dr_status_string(dr_status s);
+/* Text of the last failure on the calling thread ("" if none). */
+const char *dr_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DR_H */

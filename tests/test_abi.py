@@ -1,0 +1,116 @@
+"""The C ABI on the CPU: the library loads, exports every entry point
+include/dr.h declares, and rejects bad arguments with the documented status
+before any device call.  No call here reaches a kernel launch: every one
+either fails validation or has M == 0."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_gemm_amd as dr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dr.h")
+
+OK, INVALID, UNSUPPORTED = dr.DR_OK, dr.DR_ERR_INVALID, dr.DR_ERR_UNSUPPORTED
+A = 0x10000  # a 16-byte aligned stand-in address, never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(dr_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(dr.LIB_PATH):
+        from deterministic_gemm_amd import build
+        build.build()
+    return dr.load_library()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 8, names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(dr.EXPORTED) == set(names)
+
+
+def _route(L, x=A, xd=0, W=A, M=4, K=2048, E=256, k=8, ld=0, ids=A, w=A, lg=A, mg=A, flags=0, variant=None):
+    args = [ctypes.c_void_p(x) if x else None, xd, ctypes.c_void_p(W) if W else None, M, K, E, k, ld,
+            ctypes.c_void_p(ids) if ids else None, ctypes.c_void_p(w) if w else None,
+            ctypes.c_void_p(lg) if lg else None, ctypes.c_void_p(mg) if mg else None, flags]
+    if variant is None:
+        return L.dr_route(*args, None)
+    return L.dr_route_variant(*args, variant, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=0), INVALID),
+    (dict(k=257), INVALID),
+    (dict(M=-1), INVALID),
+    (dict(K=0), INVALID),
+    (dict(E=0), INVALID),
+    (dict(x=0), INVALID),
+    (dict(W=0), INVALID),
+    (dict(ids=0), INVALID),
+    (dict(x=A + 4), INVALID),
+    (dict(mg=A + 8), INVALID),
+    (dict(flags=2), INVALID),
+    (dict(xd=7), INVALID),
+    (dict(ld=3), INVALID),
+    (dict(E=100, k=8), UNSUPPORTED),
+    (dict(E=2048, k=8), UNSUPPORTED),
+    (dict(K=16385), UNSUPPORTED),
+    (dict(E=64, k=33), UNSUPPORTED),
+])
+def test_route_rejects(L, kw, status):
+    assert _route(L, **kw) == status
+    assert L.dr_last_error().decode() != ""
+
+
+def test_route_variant_rejects(L):
+    assert _route(L, variant=9) == INVALID
+    assert _route(L, E=1024, k=8, variant=2) == UNSUPPORTED  # the tiled family stops at E=512
+
+
+def test_empty_batch_returns_ok_without_launch(L):
+    assert _route(L, M=0) == OK
+    assert _route(L, M=0, x=0, W=0, ids=0) == OK
+    assert L.dr_last_error().decode() == ""
+
+
+def test_gate_and_gemm_reject(L):
+    P = ctypes.c_void_p
+    assert L.dr_gate_dot(P(A), 0, P(A), 0, None, None, 4, 64, None) == INVALID   # no output
+    assert L.dr_gate_dot(P(A), 0, P(A), 5, P(A), None, 4, 64, None) == INVALID   # bad dtype
+    assert L.dr_gate_dot(P(A), 0, P(A), 0, P(A), None, 4, 0, None) == INVALID
+    assert L.dr_gate_dot(P(A), 0, P(A), 0, P(A), None, 4, 20000, None) == UNSUPPORTED
+    assert L.dr_gate_dot(P(A), 0, P(A), 0, P(A), None, 0, 64, None) == OK
+    assert L.dr_gemm_bf16(P(A), P(A), P(A), 4, 48, 128, None) == UNSUPPORTED     # K % 32
+    assert L.dr_gemm_bf16(P(A), P(A), P(A), 4, 64, 100, None) == UNSUPPORTED     # N % 128
+    assert L.dr_gemm_bf16(None, P(A), P(A), 4, 64, 128, None) == INVALID
+    assert L.dr_gemm_bf16(P(A), P(A), P(A), 0, 64, 128, None) == OK
+
+
+def test_auto_variant_is_a_function_of_shape(L):
+    picks = [dr.auto_variant(M, 2048, 256) for M in range(19, 81)]
+    assert picks[0] == "rowwise" and picks[-1] == "tiled"
+    # exactly one switch, inside the m-scan range
+    switches = sum(1 for a, b in zip(picks, picks[1:]) if a != b)
+    assert switches == 1
+    assert dr.auto_variant(8192, 2048, 1024) == "rowwise"
+
+
+def test_contract(L):
+    c = dr.contract()
+    assert c == {"version": 1, "kblock": 256, "tree": 1, "acc_bits": 32, "fma": 1, "exp_id": 1,
+                 "tie_break": 1, "max_k": 32}
+
+
+def test_status_strings(L):
+    for s in (0, 1, 2, 3):
+        assert L.dr_status_string(s)

@@ -1,0 +1,90 @@
+"""Batch-invariant dense bf16 GEMM and the shared-expert gate dot on the GPU.
+
+GEMM: rows bit-identical across M in {19, 65, 75, 512, 4096} and across row
+offsets inside a batch; every sampled output within 1e-2 absolute of the
+exact product (the oracle's fp64 evaluation), the tolerance the matrix core's
+internal order allows.  Gate dot: the canonical order with one output, bit
+for bit against the oracle, across M.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import dev, dev_bf16_bits, f32_equal_bits, note, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dense():
+    return wl.dense_x_bits(4096), wl.dense_w_bits(), wl.gate_w_bits()
+
+
+def test_gemm_rows_invariant_across_m_and_close_to_exact(dense):
+    dr = require_gpu()
+    xb, Wb, _ = dense
+    xd, Wd = dev_bf16_bits(xb), dev_bf16_bits(Wb)
+    note("gemm M=4096")
+    full = dr.gemm_bf16(xd, Wd).cpu().numpy()
+    for M in wl.DENSE_MS:
+        note(f"gemm M={M}")
+        out = dr.gemm_bf16(xd[:M].contiguous(), Wd).cpu().numpy()
+        assert f32_equal_bits(out, full[:M]), f"M={M} rows differ from the M=4096 run"
+    rows = np.r_[0:19, 64:76, 511:513, 4000:4096:16]
+    ref = oracle.gemm_bf16_ref(xb[rows], Wb)
+    err = np.abs(full[rows].astype(np.float64) - ref.astype(np.float64))
+    print(f"gemm max |delta| vs exact: {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+def test_gemm_row_offsets(dense):
+    dr = require_gpu()
+    xb, Wb, _ = dense
+    Wd = dev_bf16_bits(Wb)
+    base = dr.gemm_bf16(dev_bf16_bits(xb[:200]), Wd).cpu().numpy()
+    for shift in (1, 5, 16, 33, 127):
+        filler = wl.to_bf16_bits(np.random.default_rng(shift).standard_normal((shift, wl.DENSE_K)).astype(np.float32))
+        xs = np.concatenate([filler, xb[:200]], axis=0)
+        note(f"gemm shift={shift}")
+        out = dr.gemm_bf16(dev_bf16_bits(xs), Wd).cpu().numpy()
+        assert f32_equal_bits(out[shift:shift + 200], base)
+
+
+def test_gemm_small_shapes_close_to_exact():
+    dr = require_gpu()
+    rng = np.random.default_rng(3)
+    for (M, K, N) in ((1, 32, 128), (3, 64, 256), (130, 96, 128)):
+        xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        Wb = wl.to_bf16_bits(rng.standard_normal((K, N)).astype(np.float32))
+        note(f"gemm small {M}x{K}x{N}")
+        out = dr.gemm_bf16(dev_bf16_bits(xb), dev_bf16_bits(Wb)).cpu().numpy()
+        ref = oracle.gemm_bf16_ref(xb, Wb)
+        assert np.abs(out - ref).max() <= TOL * max(1.0, np.abs(ref).max() / 10)
+
+
+def test_gate_dot_bit_exact_and_m_invariant(dense):
+    dr = require_gpu()
+    xb, _, wb = dense
+    ref_dot, ref_gate = oracle.gate_dot(xb, wb)
+    xd, wd = dev_bf16_bits(xb), dev_bf16_bits(wb)
+    for M in wl.DENSE_MS:
+        note(f"gate dot M={M}")
+        d, g = dr.gate_dot(xd[:M].contiguous(), wd)
+        assert f32_equal_bits(d.cpu().numpy(), ref_dot[:M])
+        assert f32_equal_bits(g.cpu().numpy(), ref_gate[:M])
+
+
+def test_gate_dot_f32_and_ragged_k():
+    dr = require_gpu()
+    rng = np.random.default_rng(8)
+    for K in (1, 255, 257, 3000):
+        x = rng.standard_normal((33, K)).astype(np.float32)
+        w = (rng.standard_normal(K) * 0.02).astype(np.float32)
+        note(f"gate dot f32 K={K}")
+        d, g = dr.gate_dot(dev(x), dev(w))
+        rd, rg = oracle.gate_dot(x, w)
+        assert f32_equal_bits(d.cpu().numpy(), rd) and f32_equal_bits(g.cpu().numpy(), rg)

@@ -1,0 +1,214 @@
+"""GPU parity of dr_route against the CPU oracle, bit for bit, and its
+invariance across M, batch position and kernel family.
+
+Workloads: the m-scan (a fixed 19-token request inside batches of 19..80
+tokens, "Batch changed the model's mind", section "m-scan: the staircase"),
+the Qwen3-MoE-like sweep (K=2048, E=256, k=8, M up to 8192), and edge cases:
+ragged K and M tails, every supported E, signed zeros, subnormals, NaN,
+bf16 input storage, renormalised weights, repeated calls.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import (assert_route_equal, dev, f32_equal_bits, gpu_route_np, note, oracle_route,
+                      require_gpu)
+
+pytestmark = pytest.mark.gpu
+
+K, E, TOPK = 2048, 256, 8
+
+
+@pytest.fixture(scope="module")
+def dr():
+    return require_gpu()
+
+
+@pytest.fixture(scope="module")
+def router_w():
+    return wl.router_weights(K, E)
+
+
+# ---------------------------------------------------------------- m-scan
+
+@pytest.fixture(scope="module")
+def mscan_ref(router_w):
+    fx = wl.mscan_fixed_request(K)
+    return oracle_route(fx, router_w, TOPK)
+
+
+@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled"])
+def test_mscan_fixed_rows_bit_identical(dr, router_w, mscan_ref, variant):
+    """Every M in 19..80, the fixed request placed first and last, ascending
+    then descending: the fixed rows equal the oracle's solo run bit for bit."""
+    Wd = dev(router_w)
+    order = list(range(0, 62)) + list(range(61, -1, -1))
+    seen_variants = set()
+    for c in order:
+        for fixed_first in (True, False):
+            x, off = wl.mscan_batch(c, K, fixed_first)
+            M = x.shape[0]
+            note(f"mscan variant={variant} M={M} fixed_first={fixed_first}")
+            seen_variants.add(dr.auto_variant(M, K, E))
+            got = gpu_route_np(dr, dev(x), Wd, TOPK, variant=variant)
+            rows = slice(off, off + 19)
+            assert_route_equal(tuple(None if g is None else g[rows] for g in got), mscan_ref,
+                               what=f"M={M} first={fixed_first}")
+    if variant == "auto":
+        # the dispatch threshold lies inside the scanned range
+        assert seen_variants == {"rowwise", "tiled"}
+
+
+def test_mscan_coarrivals_match_oracle(dr, router_w):
+    """All rows, not only the fixed ones, at a few batch sizes."""
+    Wd = dev(router_w)
+    for c in (0, 29, 45, 46, 61):
+        x, _ = wl.mscan_batch(c, K, True)
+        note(f"mscan all rows M={x.shape[0]}")
+        got = gpu_route_np(dr, dev(x), Wd, TOPK)
+        assert_route_equal(got, oracle_route(x, router_w, TOPK), what=f"M={x.shape[0]}")
+
+
+# ---------------------------------------------------------------- sweep
+
+@pytest.fixture(scope="module")
+def sweep(router_w):
+    x = wl.sweep_x(8192, K)
+    return x, oracle_route(x, router_w, TOPK)
+
+
+def test_sweep_every_m_matches_oracle(dr, router_w, sweep):
+    """M in {1,16,64,65,75,256,1024,4096,8192} on prefixes of one activation
+    matrix: each prefix equals the oracle on every row (so rows are also
+    bit-identical across M)."""
+    x, ref = sweep
+    Wd = dev(router_w)
+    xd = dev(x)
+    for M in wl.SWEEP_MS:
+        note(f"sweep M={M} variant={dr.auto_variant(M, K, E)}")
+        got = gpu_route_np(dr, xd[:M].contiguous(), Wd, TOPK)
+        assert_route_equal(got, tuple(r[:M] for r in ref), what=f"M={M}")
+
+
+@pytest.mark.parametrize("variant", ["rowwise", "tiled"])
+def test_sweep_forced_variants(dr, router_w, sweep, variant):
+    x, ref = sweep
+    Wd = dev(router_w)
+    for M in (1, 65, 1024):
+        note(f"sweep forced {variant} M={M}")
+        got = gpu_route_np(dr, dev(x[:M]), Wd, TOPK, variant=variant)
+        assert_route_equal(got, tuple(r[:M] for r in ref), what=f"{variant} M={M}")
+
+
+def test_bf16_input_storage_is_bit_identical(dr, router_w, sweep):
+    x, ref = sweep
+    Wd = dev(router_w)
+    M = 300
+    xb = dev(x[:M]).to(torch.bfloat16)  # exact: x is bf16-valued
+    for variant in ("rowwise", "tiled"):
+        note(f"bf16 storage {variant}")
+        got = gpu_route_np(dr, xb, Wd, TOPK, variant=variant)
+        assert_route_equal(got, tuple(r[:M] for r in ref), what=f"bf16 x {variant}")
+
+
+def test_repeated_calls_are_identical(dr, router_w, sweep):
+    """Level 0: the same call 100 times gives the same bits."""
+    x, _ = sweep
+    xd, Wd = dev(x[:1024]), dev(router_w)
+    note("repeat x100 M=1024")
+    first = dr.route(xd, Wd, TOPK)
+    for _ in range(100):
+        again = dr.route(xd, Wd, TOPK)
+        for a, b in zip(first, again):
+            assert torch.equal(a.view(torch.int32) if a.dtype == torch.float32 else a,
+                               b.view(torch.int32) if b.dtype == torch.float32 else b)
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("Kx", [1, 100, 255, 256, 257, 1000, 1023, 1025, 4096, 5000])
+def test_ragged_k(dr, Kx):
+    """K tails inside a block, single block, partial groups of blocks."""
+    rng = np.random.default_rng(Kx)
+    W = (rng.standard_normal((Kx, 128)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((70, Kx)).astype(np.float32)
+    ref = oracle_route(x, W, 6)
+    for variant in ("rowwise", "tiled"):
+        note(f"ragged K={Kx} {variant}")
+        got = gpu_route_np(dr, dev(x), dev(W), 6, variant=variant)
+        assert_route_equal(got, ref, what=f"K={Kx} {variant}")
+
+
+@pytest.mark.parametrize("Ex,kx", [(64, 1), (64, 32), (128, 5), (256, 32), (512, 10), (1024, 8), (1024, 32)])
+def test_every_supported_e(dr, Ex, kx):
+    rng = np.random.default_rng(Ex + kx)
+    Kx = 768
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((77, Kx)).astype(np.float32)
+    ref = oracle_route(x, W, kx)
+    for variant in ("auto", "rowwise", "tiled"):
+        if variant == "tiled" and Ex == 1024:
+            continue
+        note(f"E={Ex} k={kx} {variant}")
+        got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
+        assert_route_equal(got, ref, what=f"E={Ex} k={kx} {variant}")
+
+
+@pytest.mark.parametrize("mode", ["bf16_logits", "renormalize"])
+def test_modes(dr, router_w, sweep, mode):
+    x, _ = sweep
+    M = 200
+    kw = {"logit_dtype": "bf16"} if mode == "bf16_logits" else {"renormalize": True}
+    ref = oracle_route(x[:M], router_w, TOPK, logits_bf16=(mode == "bf16_logits"),
+                       renormalize=(mode == "renormalize"))
+    for variant in ("rowwise", "tiled"):
+        note(f"mode {mode} {variant}")
+        got = gpu_route_np(dr, dev(x[:M]), dev(router_w), TOPK, variant=variant, **kw)
+        assert_route_equal(got, ref, what=f"{mode} {variant}")
+
+
+def test_special_values(dr):
+    """Signed zeros, subnormal products, huge cancelling terms, NaN and inf."""
+    rng = np.random.default_rng(99)
+    Kx, Ex, kx = 600, 64, 4
+    x = rng.standard_normal((96, Kx)).astype(np.float32)
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    x[0] = 0.0
+    x[1] = -0.0
+    x[2] *= np.float32(2.0 ** -70)
+    W[:, 5] *= np.float32(2.0 ** -70)          # subnormal products on row 2 / column 5
+    x[3, :300] = 1e8
+    x[3, 300:] = -1e8                          # cancellation across blocks
+    x[4, 17] = np.nan                          # a NaN row
+    x[5, 3] = np.inf                           # inf times +-W
+    W[:, 9] = -0.0
+    W[:, 10] = W[:, 11]                        # exact ties
+    ref = oracle_route(x, W, kx)
+    for variant in ("rowwise", "tiled"):
+        note(f"special values {variant}")
+        got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
+        assert_route_equal(got, ref, what=f"special {variant}")
+
+
+def test_empty_batch_is_a_no_op(dr, router_w):
+    x = torch.empty((0, K), dtype=torch.float32, device="cuda")
+    ids, w, lg, mg = dr.route(x, dev(router_w), TOPK)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, TOPK)
+
+
+def test_rows_at_any_offset(dr, router_w, sweep):
+    """A row's result does not depend on where it sits in the batch: shift a
+    block of rows by 1..40 positions inside otherwise different batches."""
+    x, ref = sweep
+    Wd = dev(router_w)
+    block = x[1000:1050]
+    rng = np.random.default_rng(5)
+    for shift in (1, 7, 16, 31, 40):
+        filler = rng.standard_normal((shift, K)).astype(np.float32)
+        xb = np.concatenate([filler, block, filler[: shift // 2]], axis=0)
+        note(f"offset shift={shift} M={xb.shape[0]}")
+        got = gpu_route_np(dr, dev(xb), Wd, TOPK)
+        rows = slice(shift, shift + 50)
+        assert_route_equal(tuple(g[rows] for g in got), tuple(r[1000:1050] for r in ref), what=f"shift={shift}")
