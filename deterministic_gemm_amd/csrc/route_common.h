@@ -77,43 +77,88 @@ __device__ __forceinline__ uint32_t rank_key(float v) {
 
 // Fold the partial of block b (0-based, blocks finished in ascending order)
 // into the counter stack.  stk[l] holds the sum of a complete subtree of 2^l
-// leaves whenever bit l of the number of finished blocks is set.
+// leaves whenever bit l of the number of finished blocks is set.  The level is
+// a template parameter so that every stack access has a constant index and
+// the stack stays in registers.
+template <int L, int MAXL, int N>
+__device__ __forceinline__ void tree_push_level(float (&stk)[MAXL][N], float (&p)[N], int b) {
+  if constexpr (L < MAXL) {
+    if (((b >> L) & 1) == 0) {
+#pragma unroll
+      for (int o = 0; o < N; ++o) stk[L][o] = p[o];
+    } else {
+#pragma unroll
+      for (int o = 0; o < N; ++o) p[o] = stk[L][o] + p[o];
+      tree_push_level<L + 1, MAXL, N>(stk, p, b);
+    }
+  }
+}
+
 template <int MAXL, int N>
 __device__ __forceinline__ void tree_push(float (&stk)[MAXL][N], float (&p)[N], int b) {
-#pragma unroll
-  for (int l = 0; l < MAXL; ++l) {
-    if (((b >> l) & 1) == 0) {
-#pragma unroll
-      for (int o = 0; o < N; ++o) stk[l][o] = p[o];
-      return;
-    }
-#pragma unroll
-    for (int o = 0; o < N; ++o) p[o] = stk[l][o] + p[o];
-  }
+  tree_push_level<0, MAXL, N>(stk, p, b);
 }
 
 // After nb blocks: the stored subtrees sit at the set bits of nb; combine them
 // from the smallest (rightmost leaves) upward, which is the padded balanced tree.
+template <int L, int MAXL, int N>
+__device__ __forceinline__ void tree_final_level(float (&stk)[MAXL][N], int nb, float (&out)[N], bool have) {
+  if constexpr (L < MAXL) {
+    if ((nb >> L) & 1) {
+#pragma unroll
+      for (int o = 0; o < N; ++o) out[o] = have ? stk[L][o] + out[o] : stk[L][o];
+      have = true;
+    }
+    tree_final_level<L + 1, MAXL, N>(stk, nb, out, have);
+  }
+}
+
 template <int MAXL, int N>
 __device__ __forceinline__ void tree_final(float (&stk)[MAXL][N], int nb, float (&out)[N]) {
-  bool have = false;
-#pragma unroll
-  for (int l = 0; l < MAXL; ++l) {
-    if ((nb >> l) & 1) {
-#pragma unroll
-      for (int o = 0; o < N; ++o) out[o] = have ? stk[l][o] + out[o] : stk[l][o];
-      have = true;
+  tree_final_level<0, MAXL, N>(stk, nb, out, false);
+}
+
+// The same counter tree over whole vectors of 16 partials (one element per
+// output; the additions are elementwise fp32 adds).  Kernels keep their group
+// stack as vectors so it stays in registers.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int L, int MAXL>
+__device__ __forceinline__ void tree_push_vec_level(f32x16 (&stk)[MAXL], f32x16 &p, int b) {
+  if constexpr (L < MAXL) {
+    if (((b >> L) & 1) == 0) {
+      stk[L] = p;
+    } else {
+      p = stk[L] + p;
+      tree_push_vec_level<L + 1, MAXL>(stk, p, b);
     }
   }
 }
 
-// ---------------------------------------------------------------- epilogue
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int d) {
-  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), d, 64);
-  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), d, 64);
-  return (static_cast<uint64_t>(hi) << 32) | lo;
+template <int MAXL>
+__device__ __forceinline__ void tree_push_vec(f32x16 (&stk)[MAXL], f32x16 p, int b) {
+  tree_push_vec_level<0, MAXL>(stk, p, b);
 }
+
+template <int L, int MAXL>
+__device__ __forceinline__ void tree_final_vec_level(f32x16 (&stk)[MAXL], int nb, f32x16 &out, bool have) {
+  if constexpr (L < MAXL) {
+    if ((nb >> L) & 1) {
+      out = have ? stk[L] + out : stk[L];
+      have = true;
+    }
+    tree_final_vec_level<L + 1, MAXL>(stk, nb, out, have);
+  }
+}
+
+template <int MAXL>
+__device__ __forceinline__ f32x16 tree_final_vec(f32x16 (&stk)[MAXL], int nb) {
+  f32x16 out = {};
+  tree_final_vec_level<0, MAXL>(stk, nb, out, false);
+  return out;
+}
+
+// ---------------------------------------------------------------- epilogue
 
 struct EpilogueArgs {
   int k;
@@ -125,8 +170,67 @@ struct EpilogueArgs {
   dr_margin *margins;
 };
 
+// DPP controls (gfx9 encoding): quad_perm, row rotate right.
+constexpr int DPP_QUAD_XOR1 = 0xB1;  // quad_perm:[1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;  // quad_perm:[2,3,0,1]
+constexpr int DPP_ROW_ROR1 = 0x121;
+constexpr int DPP_ROW_ROR2 = 0x122;
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum of a u32 over the wavefront, returned uniform: rotations inside each
+// row of 16 lanes, then the four row results combined.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<DPP_ROW_ROR8>(x));
+  x = max(x, dpp_u32<DPP_ROW_ROR4>(x));
+  x = max(x, dpp_u32<DPP_ROW_ROR2>(x));
+  x = max(x, dpp_u32<DPP_ROW_ROR1>(x));
+  const uint32_t a = __builtin_amdgcn_readlane(x, 0), b = __builtin_amdgcn_readlane(x, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(x, 32), d = __builtin_amdgcn_readlane(x, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Pairwise tree sum of one value per lane in lane order (lane 2i with 2i+1,
+// then pairs of pairs, ...), returned uniform.  Levels 1-2 pair lanes inside
+// quads (every lane of a quad then holds the quad's sum).  Levels 3-4 use
+// row rotations, where lane i reads lane i-4 (then i-8) of its row: lanes
+// 4-7 combine quads 0 and 1, lanes 12-15 quads 2 and 3, and lanes 12-15 then
+// combine those two halves, so lane 16r+15 holds row r's tree sum.  Levels 5-6
+// combine the four rows.  Other lanes hold sums of other groupings, never read.
+__device__ __forceinline__ float wave_tree_sum(float s) {
+  s = s + dpp_f32<DPP_QUAD_XOR1>(s);
+  s = s + dpp_f32<DPP_QUAD_XOR2>(s);
+  s = dpp_f32<DPP_ROW_ROR4>(s) + s;
+  s = dpp_f32<DPP_ROW_ROR8>(s) + s;
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), 63));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Inverse of rank_key(v) + 1 for selection keys (0 = taken, 1 = NaN); +0 and
+// -0 share a key and come back as +0, which no caller distinguishes.
+__device__ __forceinline__ float key_value(uint32_t kp1) {
+  const uint32_t kk = kp1 - 1u;
+  if (kk == 0u) return u2f(0x7FC00000u);
+  return u2f((kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk);
+}
+
 // One wavefront routes one token.  `row` holds the token's E canonical fp32
-// logits (in LDS).  Lane l owns experts l*V .. l*V+V-1 (V = E/64).
+// logits (in LDS, 16-byte aligned).  Lane l owns experts l*V .. l*V+V-1.
+// Each rank round takes the wavefront maximum of the selection keys, then the
+// lowest expert index holding it (ballots per slot, first set lane), and
+// retires that entry: larger value first, equal values by ascending index.
 template <int E>
 __device__ void route_token(const float *__restrict__ row, int64_t m, const EpilogueArgs &a) {
   constexpr int V = E / 64;
@@ -140,7 +244,7 @@ __device__ void route_token(const float *__restrict__ row, int64_t m, const Epil
     float t = row[lane * V + j];
     if (a.logit_bf16) t = bf16_to_f32(f32_to_bf16(t));
     v[j] = t;
-    key[j] = rank_key(t);
+    key[j] = rank_key(t) + 1u;
   }
 
   if (a.logits) {
@@ -155,48 +259,36 @@ __device__ void route_token(const float *__restrict__ row, int64_t m, const Epil
     }
   }
 
-  // Rank rounds: k winners, plus the first rejected value when k < E.
   const int rounds = (k < E) ? k + 1 : k;
-  uint32_t avail = (V >= 32) ? 0xFFFFFFFFu : ((1u << V) - 1u);
-  float my_val = 0.0f;  // lane r keeps rank r
+  uint32_t my_key = 0, mx_key = 0;
   int32_t my_id = 0;
-  float mx = 0.0f, sel = 0.0f, rej = -__builtin_inff();
+  int sel_at = 0, rej_at = -1;  // winning expert index of rank k-1 and rank k
   for (int r = 0; r < rounds; ++r) {
-    uint32_t bk = 0;
-    int bj = -1;
+    uint32_t lm = key[0];
+#pragma unroll
+    for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
+    const uint32_t wmax = wave_max_u32(lm);
+    int best = 0x7FFFFFFF;
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      if (((avail >> j) & 1u) && (bj < 0 || key[j] > bk)) {
-        bk = key[j];
-        bj = j;
-      }
+      const uint64_t msk = __builtin_amdgcn_ballot_w64(key[j] == wmax);
+      if (msk) best = min(best, static_cast<int>(__builtin_ctzll(msk)) * V + j);
     }
-    // larger key first; on equal keys the larger ~index, i.e. the lower index
-    uint64_t comp = (bj < 0) ? 0ull
-                             : ((static_cast<uint64_t>(bk) << 32) |
-                                static_cast<uint32_t>(~static_cast<uint32_t>(lane * V + bj)));
+    const int wl = best / V, wj = best % V;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint64_t o = shfl_xor_u64(comp, d);
-      comp = (o > comp) ? o : comp;
+    for (int j = 0; j < V; ++j)
+      if (j == wj && lane == wl) key[j] = 0u;
+    if (lane == r) {
+      my_key = wmax;
+      my_id = best;
     }
-    const int win = static_cast<int>(~static_cast<uint32_t>(comp));
-    const int owner = win / V, wj = win % V;
-    float cand = v[0];
-#pragma unroll
-    for (int j = 1; j < V; ++j) cand = (j == wj) ? v[j] : cand;
-    const float wv = __shfl(cand, owner, 64);
-    if (lane == owner) avail &= ~(1u << wj);
-    if (r < k && lane == r) {
-      my_val = wv;
-      my_id = win;
-    }
-    if (r == 0) mx = wv;
-    if (r == k - 1) sel = wv;
-    if (r == k) rej = wv;
+    if (r == 0) mx_key = wmax;
+    if (r == k - 1) sel_at = best;
+    if (r == k) rej_at = best;
   }
 
   if (a.weights) {
+    const float mx = key_value(mx_key);
     float u[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) u[j] = route_exp(v[j] - mx);
@@ -205,26 +297,37 @@ __device__ void route_token(const float *__restrict__ row, int64_t m, const Epil
 #pragma unroll
       for (int i = 0; i < w / 2; ++i) u[i] = u[2 * i] + u[2 * i + 1];
     }
-    float s = u[0];
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) s = s + __shfl_xor(s, d, 64);
-    float w = route_exp(my_val - mx) / s;
+    const float s = wave_tree_sum(u[0]);
+    float w = route_exp(key_value(my_key) - mx) / s;
     if (a.flags & DR_ROUTE_RENORMALIZE) {
-      float rs = __shfl(w, 0, 64);
-      for (int j = 1; j < k; ++j) rs = rs + __shfl(w, j, 64);
+      float rs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), 0));
+      for (int j = 1; j < k; ++j)
+        rs = rs + __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
       w = w / rs;
     }
     if (lane < k) a.weights[m * k + lane] = w;
   }
   if (lane < k) a.ids[m * k + lane] = my_id;
-  if (a.margins && lane == 0) {
-    dr_margin g;
-    g.sel_min = sel;
-    g.rej_max = rej;
-    g.sel_min_bf16 = f32_to_bf16(sel);
-    g.rej_max_bf16 = f32_to_bf16(rej);
-    g.ulps = (k < E) ? (bf16_ord(g.sel_min_bf16) - bf16_ord(g.rej_max_bf16)) : 0x7FFFFFFF;
-    a.margins[m] = g;
+  if (a.margins) {
+    // exact values (sign of zero included) of ranks k-1 and k, read back
+    float cs = v[0], cr = v[0];
+#pragma unroll
+    for (int j = 1; j < V; ++j) {
+      cs = (j == sel_at % V) ? v[j] : cs;
+      cr = (rej_at >= 0 && j == rej_at % V) ? v[j] : cr;
+    }
+    const float sel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cs), sel_at / V));
+    float rej = -__builtin_inff();
+    if (rej_at >= 0) rej = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cr), rej_at / V));
+    if (lane == 0) {
+      dr_margin g;
+      g.sel_min = sel;
+      g.rej_max = rej;
+      g.sel_min_bf16 = f32_to_bf16(sel);
+      g.rej_max_bf16 = f32_to_bf16(rej);
+      g.ulps = (k < E) ? (bf16_ord(g.sel_min_bf16) - bf16_ord(g.rej_max_bf16)) : 0x7FFFFFFF;
+      a.margins[m] = g;
+    }
   }
 }
 

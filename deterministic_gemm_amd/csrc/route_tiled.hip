@@ -25,12 +25,13 @@
 // 16x16.  K is walked in chunks of KC steps of all four slots: a chunk of x
 // (4 slots x 32 tokens x KC) and of W (4 slots x KC rows x E) is prefetched
 // into registers while the previous chunk is consumed from LDS.
+#include <type_traits>
+
 #include "route_common.h"
 #include "launch.h"
 
 namespace drk {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 template <int E_, int AT_, int BT_, int KC_>
 struct TiledCfg {
@@ -203,6 +204,276 @@ __global__ __launch_bounds__(C::NT) void route_tiled_kernel(const float *__restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Pipelined variant for fp32 x with K % 4 == 0: x and W chunks go from global
+// memory straight into LDS (global_load_lds_dwordx4: each lane moves 16 bytes,
+// written at the instruction's LDS base + 16 * lane) through a ring of S
+// stages, so S-1 chunks are in flight while one is consumed and no register
+// staging is needed.  Every wavefront issues the same number of transfers per
+// chunk (padding transfers read a 16-byte vector of -0.0 or +0.0), so waiting
+// for "all but the last (S-2) chunks' transfers" is one fixed vmcnt; a barrier
+// after that wait publishes the chunk to all wavefronts and also guarantees
+// the stage about to be refilled has been consumed.  The arithmetic per
+// output is the same as in route_tiled_kernel above.
+//
+// LDS stage layout (floats): W rows of slot s at s*SW + c*E (SW = KC*E + 16,
+// the 16-float skew spreads the four slot groups over the LDS banks), then x
+// as 16-byte units (slot, token, h) with h, the 4-wide piece of the chunk,
+// XOR-swizzled by token so that 16 lanes reading one piece of 16 tokens hit
+// distinct banks.
+
+struct Pad16 {
+  float v[4];
+};
+__device__ const Pad16 g_pad_pos = {{0.0f, 0.0f, 0.0f, 0.0f}};
+__device__ const Pad16 g_pad_neg = {{-0.0f, -0.0f, -0.0f, -0.0f}};
+
+template <int E_, int AT_, int BT_, int KC_, int S_>
+struct DmaCfg {
+  static constexpr int E = E_, AT = AT_, BT = BT_, KC = KC_, S = S_;
+  static constexpr int EW = 16 * BT, NW = E / EW, NT = NW * 64, TT = 16 * AT;
+  static constexpr int HU = KC / 4;                   // 16-byte units per (slot, token) row
+  static constexpr int SW = KC * E + 16;              // W slot stride (floats)
+  static constexpr int WST = 4 * SW;                  // W floats per stage
+  static constexpr int XST = 4 * TT * KC;             // x floats per stage
+  static constexpr int STG = WST + XST;               // floats per stage
+  static constexpr int LGP = E + 4;
+  static constexpr int WI = 4 * KC * E / 256;         // W transfers (64 lanes x 16 B) per chunk
+  static constexpr int WIW = WI / NW;                 // ... per wavefront
+  static constexpr int XU = TT * KC;                  // x 16-byte units per chunk
+  static constexpr int XUW = XU / NW;                 // ... per wavefront
+  static constexpr int XIW = (XUW + 63) / 64;         // x transfers per wavefront
+  static constexpr int PER_CHUNK = WIW + XIW;         // transfers per wavefront per chunk
+  static constexpr int CPG = 256 / KC;
+  static_assert(WIW * NW == WI && WIW >= 1, "W transfers split evenly");
+  static_assert(XUW * NW == XU && XUW >= 1, "x units split evenly");
+  static_assert((KC * E / 4) % 64 == 0, "a W transfer stays inside one slot");
+  static_assert(PER_CHUNK * (S - 2) <= 63, "vmcnt range");
+  static_assert(KC % 4 == 0 && 256 % KC == 0 && S >= 2, "chunking");
+  __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
+};
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// One global -> LDS transfer: every active lane moves the 16 bytes at `src`
+// to LDS address lds_base + 16 * lane.  Written as inline assembly so that
+// the compiler's wait-count pass does not treat it as an LDS write to be
+// drained before every LDS read; the kernel orders these transfers itself
+// (wait_vmcnt + barrier).  m0 is used only here.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const float *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Issue the transfers of chunk ci into `stage` (chunks past the end load
+// padding, keeping the per-wavefront transfer count fixed).
+template <class C>
+__device__ __forceinline__ void dma_issue(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+                                          int K, int64_t m0, int nb, int nchunks, int wave, int lane, int ci,
+                                          float *stage) {
+  constexpr int E = C::E, KC = C::KC, TT = C::TT, HU = C::HU;
+  const int g = ci / C::CPG;
+  const int kk0 = (ci % C::CPG) * KC;
+  const bool live = ci < nchunks;
+#pragma unroll
+  for (int i = 0; i < C::WIW; ++i) {
+    const int j = wave * C::WIW + i;           // transfer index within the chunk
+    const int s = j / (KC * E / 256);          // slot
+    const int uo = (j % (KC * E / 256)) * 64;  // first 16-byte unit within the slot
+    const int u = uo + lane;
+    const int c = u / (E / 4), e4 = u % (E / 4);
+    const int blk = 4 * g + s;
+    const int kg = blk * 256 + kk0 + c;
+    const void *src = &g_pad_neg;
+    if (live && blk < nb && kg < K) src = W + static_cast<int64_t>(kg) * E + 4 * e4;
+    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(stage + s * C::SW + uo * 4)));
+  }
+#pragma unroll
+  for (int i = 0; i < C::XIW; ++i) {
+    const int ul = i * 64 + lane;  // unit within this wavefront's share
+    const int u = wave * C::XUW + ul;
+    const int s = u / (TT * HU);
+    const int rem = u % (TT * HU);
+    const int tok = rem / HU, hp = rem % HU;
+    const int h = hp ^ C::swz(tok);
+    const int blk = 4 * g + s;
+    const int kg = blk * 256 + kk0 + 4 * h;
+    const int64_t m = m0 + tok;
+    const void *src = &g_pad_pos;
+    if (live && blk < nb && kg < K && m < M) src = xf + m * K + kg;
+    if (ul < C::XUW) dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(stage + C::WST + (wave * C::XUW + i * 64) * 4)));
+  }
+}
+
+// One chunk: retire its transfers, publish them (barrier), refill the stage
+// freed by the previous chunk, then 4 slots x KC chain steps on the matrix
+// cores; at the end of a group of four K-blocks, fold the group's partials.
+template <class C, int MAXL>
+__device__ __forceinline__ void dma_step(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+                                         int K, int64_t m0, int nb, int nchunks, int wave, int lane, int ci,
+                                         const float *cur, float *refill, f32x16 (&acc)[C::AT][C::BT],
+                                         f32x16 (&stk)[MAXL]) {
+  constexpr int E = C::E, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, S = C::S, HU = C::HU;
+  const int s_l = lane >> 4, r_l = lane & 15;
+  const int eb = wave * C::EW;
+  const int g = ci / C::CPG;
+  const int cg = ci % C::CPG;
+  if (cg == 0) {
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float init = (4 * g + s < nb) ? 0.0f : -0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[a][b][4 * s + q] = init;
+        }
+  }
+  compiler_fence();
+  wait_vmcnt<C::PER_CHUNK * (S - 2)>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  dma_issue<C>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + S - 1, refill);
+
+  const float *xs = cur + C::WST;
+#pragma unroll
+  for (int c4 = 0; c4 < KC / 4; ++c4) {
+    float4 av[AT];
+#pragma unroll
+    for (int a = 0; a < AT; ++a) {
+      const int tok = a * 16 + r_l;
+      av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+    }
+    float bw[BT][4];
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bw[b][q] = cur[s_l * C::SW + (4 * c4 + q) * E + eb + b * 16 + r_l];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          const float aval = (q == 0) ? av[a].x : (q == 1) ? av[a].y : (q == 2) ? av[a].z : av[a].w;
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[b][q], acc[a][b], 0, 0, 0);
+        }
+  }
+
+  if (cg == C::CPG - 1) {
+    // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
+    static_assert(AT * BT * 4 == 16, "one vector of 16 group partials per lane");
+    f32x16 qv;
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          qv[(a * BT + b) * 4 + q] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
+    tree_push_vec<MAXL>(stk, qv, g);
+  }
+}
+
+// The S stages are separate __shared__ objects and the chunk loop is unrolled
+// by S, so every stage address is a compile-time constant.
+template <class C, int MAXL>
+__global__ __launch_bounds__(C::NT) void route_tiled_dma_kernel(const float *__restrict__ xf,
+                                                                const float *__restrict__ W, int64_t M,
+                                                                int K, EpilogueArgs ea) {
+  constexpr int E = C::E, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S;
+  static_assert(S == 2 || S == 4, "two or four stages");
+  __shared__ __attribute__((aligned(16))) float stg0[C::STG];
+  __shared__ __attribute__((aligned(16))) float stg1[C::STG];
+  __shared__ __attribute__((aligned(16))) float stg2[S == 4 ? C::STG : 4];
+  __shared__ __attribute__((aligned(16))) float stg3[S == 4 ? C::STG : 4];
+  static_assert(TT * C::LGP <= C::STG, "the epilogue's logits fit in stage 0");
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int s_l = lane >> 4, r_l = lane & 15;
+  const int eb = wave * C::EW;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.x) * TT;
+  const int nb = (K + 255) / 256;
+  const int G = (nb + 3) / 4;
+  const int nchunks = G * C::CPG;  // a multiple of S
+
+  f32x16 acc[AT][BT];
+  f32x16 stk[MAXL];
+
+  if constexpr (S == 4) {
+    dma_issue<C>(xf, W, M, K, m0, nb, nchunks, wave, lane, 0, stg0);
+    dma_issue<C>(xf, W, M, K, m0, nb, nchunks, wave, lane, 1, stg1);
+    dma_issue<C>(xf, W, M, K, m0, nb, nchunks, wave, lane, 2, stg2);
+    for (int ci = 0; ci < nchunks; ci += 4) {
+      dma_step<C, MAXL>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + 0, stg0, stg3, acc, stk);
+      dma_step<C, MAXL>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + 1, stg1, stg0, acc, stk);
+      dma_step<C, MAXL>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + 2, stg2, stg1, acc, stk);
+      dma_step<C, MAXL>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + 3, stg3, stg2, acc, stk);
+    }
+  } else {
+    dma_issue<C>(xf, W, M, K, m0, nb, nchunks, wave, lane, 0, stg0);
+    for (int ci = 0; ci < nchunks; ci += 2) {
+      dma_step<C, MAXL>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + 0, stg0, stg1, acc, stk);
+      dma_step<C, MAXL>(xf, W, M, K, m0, nb, nchunks, wave, lane, ci + 1, stg1, stg0, acc, stk);
+    }
+  }
+
+  const f32x16 out = tree_final_vec<MAXL>(stk, G);
+
+  // drain the trailing padding transfers before stage 0 is reused for the logits
+  compiler_fence();
+  wait_vmcnt<0>();
+  __syncthreads();
+  float *lg = stg0;
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tok = a * 16 + 4 * s_l + q;
+        const int e = eb + b * 16 + r_l;
+        lg[tok * C::LGP + e] = out[(a * BT + b) * 4 + q];
+      }
+  __syncthreads();
+  for (int i = wave; i < TT; i += C::NW) {
+    const int64_t mm = m0 + i;
+    if (mm < M) route_token<E>(lg + i * C::LGP, mm, ea);
+  }
+}
+
+template <class C, int MAXL>
+static hipError_t launch_dma_cm(const RouteLaunch &L) {
+  const int64_t nblk = (L.M + C::TT - 1) / C::TT;
+  EpilogueArgs ea{L.k, L.logit_bf16, L.flags, L.ids, L.weights, L.logits, L.margins};
+  hipLaunchKernelGGL((route_tiled_dma_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0,
+                     L.stream, L.xf, L.W, L.M, static_cast<int>(L.K), ea);
+  return hipGetLastError();
+}
+
+template <class C>
+static hipError_t launch_dma_c(const RouteLaunch &L) {
+  const int64_t nb = (L.K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  if (G <= 1) return launch_dma_cm<C, 1>(L);
+  if (G <= 2) return launch_dma_cm<C, 2>(L);
+  if (G <= 4) return launch_dma_cm<C, 3>(L);
+  if (G <= 8) return launch_dma_cm<C, 4>(L);
+  return launch_dma_cm<C, 5>(L);
+}
+
 template <class C, int MAXL>
 static hipError_t launch_tiled_cm(const RouteLaunch &L) {
   const int64_t nblk = (L.M + C::TT - 1) / C::TT;
@@ -229,11 +500,14 @@ bool tiled_supports(int64_t E, int64_t K) {
 }
 
 hipError_t launch_route_tiled(const RouteLaunch &L) {
+  // fp32 x in whole 16-byte pieces: the pipelined kernel; otherwise (bf16 x,
+  // K % 4 != 0) the register-staged one.  Both compute identical bits.
+  const bool dma = L.xf != nullptr && (L.K % 4) == 0;
   switch (L.E) {
-    case 64: return launch_tiled_c<TiledCfg<64, 2, 2, 16>>(L);
-    case 128: return launch_tiled_c<TiledCfg<128, 2, 2, 16>>(L);
-    case 256: return launch_tiled_c<TiledCfg<256, 2, 2, 16>>(L);
-    case 512: return launch_tiled_c<TiledCfg<512, 1, 4, 8>>(L);
+    case 64: return dma ? launch_dma_c<DmaCfg<64, 2, 2, 8, 4>>(L) : launch_tiled_c<TiledCfg<64, 2, 2, 16>>(L);
+    case 128: return dma ? launch_dma_c<DmaCfg<128, 2, 2, 8, 4>>(L) : launch_tiled_c<TiledCfg<128, 2, 2, 16>>(L);
+    case 256: return dma ? launch_dma_c<DmaCfg<256, 2, 2, 8, 4>>(L) : launch_tiled_c<TiledCfg<256, 2, 2, 16>>(L);
+    case 512: return dma ? launch_dma_c<DmaCfg<512, 1, 4, 4, 4>>(L) : launch_tiled_c<TiledCfg<512, 1, 4, 8>>(L);
     default: return hipErrorInvalidValue;
   }
 }
