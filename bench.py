@@ -58,6 +58,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run one 256 MiB device-to-device copy, the known-size reference for "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (rows are independent, "
@@ -86,6 +89,12 @@ def main():
            torch.empty((M, E), dtype=torch.float32, device=dev),
            torch.empty((M, 4), dtype=torch.int32, device=dev))
     stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         dr.route(xd, Wd, TOPK, out=out)
