@@ -350,7 +350,7 @@ template <class C, int MAXL>
 __device__ __forceinline__ void dma_step(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
                                          int K, int64_t m0, int nb, int nchunks, int wave, int lane, int ci,
                                          const float *cur, float *refill, f32x16 (&acc)[C::AT][C::BT],
-                                         f32x16 (&stk)[MAXL]) {
+                                         f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
   constexpr int E = C::E, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, S = C::S, HU = C::HU;
   const int s_l = lane >> 4, r_l = lane & 15;
   const int eb = wave * C::EW;
@@ -404,16 +404,20 @@ __device__ __forceinline__ void dma_step(const float *__restrict__ xf, const flo
 
   if (cg == C::CPG - 1) {
     // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
-    static_assert(AT * BT * 4 == 16, "one vector of 16 group partials per lane");
-    f32x16 qv;
+    constexpr int NV = AT * BT * 4 / 16;
+    static_assert(NV * 16 == AT * BT * 4, "group partials fill whole vectors of 16");
+    f32x16 qv[NV];
 #pragma unroll
     for (int a = 0; a < AT; ++a)
 #pragma unroll
       for (int b = 0; b < BT; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          qv[(a * BT + b) * 4 + q] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
-    tree_push_vec<MAXL>(stk, qv, g);
+        for (int q = 0; q < 4; ++q) {
+          const int o = (a * BT + b) * 4 + q;
+          qv[o / 16][o % 16] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
+        }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) tree_push_vec<MAXL>(stk[v], qv[v], g);
   }
 }
 
@@ -441,7 +445,7 @@ __global__ __launch_bounds__(C::NT) void route_tiled_dma_kernel(const float *__r
   const int nchunks = G * C::CPG;  // a multiple of S
 
   f32x16 acc[AT][BT];
-  f32x16 stk[MAXL];
+  f32x16 stk[AT * BT * 4 / 16][MAXL];
 
   if constexpr (S == 4) {
     dma_issue<C>(xf, W, M, K, m0, nb, nchunks, wave, lane, 0, stg0);
@@ -461,7 +465,9 @@ __global__ __launch_bounds__(C::NT) void route_tiled_dma_kernel(const float *__r
     }
   }
 
-  const f32x16 out = tree_final_vec<MAXL>(stk, G);
+  f32x16 outv[AT * BT * 4 / 16];
+#pragma unroll
+  for (int v = 0; v < AT * BT * 4 / 16; ++v) outv[v] = tree_final_vec<MAXL>(stk[v], G);
 
   // drain the trailing padding transfers before stage 0 is reused for the logits
   compiler_fence();
@@ -476,7 +482,7 @@ __global__ __launch_bounds__(C::NT) void route_tiled_dma_kernel(const float *__r
       for (int q = 0; q < 4; ++q) {
         const int tok = a * 16 + 4 * s_l + q;
         const int e = eb + b * 16 + r_l;
-        lg[tok * C::LGP + e] = out[(a * BT + b) * 4 + q];
+        lg[tok * C::LGP + e] = outv[((a * BT + b) * 4 + q) / 16][((a * BT + b) * 4 + q) % 16];
       }
   __syncthreads();
   for (int i = wave; i < TT; i += C::NW) {
