@@ -31,37 +31,42 @@ MARGIN_DTYPE = np.dtype(
 assert MARGIN_DTYPE.itemsize == 16
 
 
+def bind(path: str) -> ctypes.CDLL:
+    """ctypes handle with the oracle's signatures for the library at `path`."""
+    L = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i64, i32, u32, c_int = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int
+    L.dro_bf16_rne.argtypes = [ctypes.c_float]
+    L.dro_bf16_rne.restype = ctypes.c_uint16
+    L.dro_bf16_ord.argtypes = [ctypes.c_uint16]
+    L.dro_bf16_ord.restype = i32
+    L.dro_ulps.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
+    L.dro_ulps.restype = i32
+    L.dro_expf.argtypes = [ctypes.c_float]
+    L.dro_expf.restype = ctypes.c_float
+    L.dro_expf_array.argtypes = [P, P, i64]
+    L.dro_expf_array.restype = None
+    L.dro_logits.argtypes = [P, c_int, P, i64, i64, i64, i64, P, c_int]
+    L.dro_logits.restype = None
+    L.dro_route.argtypes = [P, c_int, P, i64, i64, i64, i32, i64, c_int, u32, P, P, P, P, c_int]
+    L.dro_route.restype = c_int
+    L.dro_route_split_by_m.argtypes = [P, c_int, P, i64, i64, i64, i32, c_int, u32, P, P, P, P, c_int]
+    L.dro_route_split_by_m.restype = c_int
+    L.dro_gate_dot.argtypes = [P, c_int, P, c_int, i64, i64, i64, P, P, c_int]
+    L.dro_gate_dot.restype = None
+    L.dro_gemm_bf16_ref.argtypes = [P, P, P, i64, i64, i64, c_int]
+    L.dro_gemm_bf16_ref.restype = None
+    L.dro_default_threads.argtypes = []
+    L.dro_default_threads.restype = c_int
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_build.LIB):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
-        P = ctypes.c_void_p
-        i64, i32, u32, c_int = ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int
-        L.dro_bf16_rne.argtypes = [ctypes.c_float]
-        L.dro_bf16_rne.restype = ctypes.c_uint16
-        L.dro_bf16_ord.argtypes = [ctypes.c_uint16]
-        L.dro_bf16_ord.restype = i32
-        L.dro_ulps.argtypes = [ctypes.c_uint16, ctypes.c_uint16]
-        L.dro_ulps.restype = i32
-        L.dro_expf.argtypes = [ctypes.c_float]
-        L.dro_expf.restype = ctypes.c_float
-        L.dro_expf_array.argtypes = [P, P, i64]
-        L.dro_expf_array.restype = None
-        L.dro_logits.argtypes = [P, c_int, P, i64, i64, i64, i64, P, c_int]
-        L.dro_logits.restype = None
-        L.dro_route.argtypes = [P, c_int, P, i64, i64, i64, i32, i64, c_int, u32, P, P, P, P, c_int]
-        L.dro_route.restype = c_int
-        L.dro_route_split_by_m.argtypes = [P, c_int, P, i64, i64, i64, i32, c_int, u32, P, P, P, P, c_int]
-        L.dro_route_split_by_m.restype = c_int
-        L.dro_gate_dot.argtypes = [P, c_int, P, c_int, i64, i64, i64, P, P, c_int]
-        L.dro_gate_dot.restype = None
-        L.dro_gemm_bf16_ref.argtypes = [P, P, P, i64, i64, i64, c_int]
-        L.dro_gemm_bf16_ref.restype = None
-        L.dro_default_threads.argtypes = []
-        L.dro_default_threads.restype = c_int
-        _lib = L
+        _lib = bind(_build.LIB)
     return _lib
 
 

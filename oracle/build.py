@@ -11,12 +11,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libdro.so")
 
 
+FLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",
+         "-fPIC", "-shared", "-Wall", "-Wextra", "-pthread"]
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one oracle source file (with dro.h beside it) into `out`."""
+    subprocess.run(["gcc"] + FLAGS + [src, "-o", out, "-lm"], check=True)
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    cmd = [
-        "gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fno-finite-math-only",
-        "-fPIC", "-shared", "-Wall", "-Wextra", "-pthread",
-        os.path.join(HERE, "dro.c"), "-o", LIB + ".tmp", "-lm",
-    ]
+    cmd = ["gcc"] + FLAGS + [os.path.join(HERE, "dro.c"), "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)

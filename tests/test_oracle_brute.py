@@ -158,3 +158,31 @@ def test_weights_against_float64_softmax():
         # renormalising adds a k-term sum and a second division
         bound = (10 if renorm else 8) * 2.0 ** -24
         assert rel.max() < bound, rel.max()
+
+
+def test_weights_exact_tree_denominator():
+    """Weights bit for bit from exact rationals: u_e = expf(l_e - max) with
+    the oracle's exp (pinned on its own), the denominator the pairwise tree of
+    the u_e in index order with each add rounded to nearest-even, one rounded
+    division per weight; renormalisation by the left-to-right sum of the k
+    weights.  A sequential denominator or another grouping changes bits."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21)
+    E, k = 48, 6
+    x = rng.standard_normal((12, 40)).astype(np.float32)
+    W = (rng.standard_normal((40, E)) * 0.7).astype(np.float32)
+    for renorm in (False, True):
+        ids, w, lg, _ = oracle.route(x, W, k, renormalize=renorm)
+        for m in range(x.shape[0]):
+            l = lg[m]
+            mx = np.float32(l[ids[m, 0]])
+            u = oracle.expf((l - mx).astype(np.float32))
+            s = brute.tree([float(v) for v in u])
+            want = [brute.rne_f32(Fraction(float(u[i])) / Fraction(s)) for i in ids[m]]
+            if renorm:
+                r = want[0]
+                for v in want[1:]:
+                    r = brute.add(r, v)
+                want = [brute.rne_f32(Fraction(v) / Fraction(r)) for v in want]
+            got = [float(v) for v in w[m]]
+            assert [brute.f32_bits(v) for v in got] == [brute.f32_bits(v) for v in want], (renorm, m)

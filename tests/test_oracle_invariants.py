@@ -128,6 +128,24 @@ def test_integer_inputs_give_exact_integer_matmul():
     assert np.array_equal(got, want.astype(np.float32))
 
 
+def test_zero_rows_give_positive_zero():
+    """Every chain starts at +0 and fma(+-0, w, +0) = +0 for finite w, so a
+    row of zeros (either sign) gives +0.0 logits bit for bit, whatever the
+    signs of W."""
+    rng = np.random.default_rng(14)
+    K, E = 600, 12
+    W = rng.standard_normal((K, E)).astype(np.float32)
+    # columns of one sign make every product of a -0 or +0 row the same
+    # signed zero, so a chain started at -0 would end at -0
+    W[:, 0] = np.abs(W[:, 0])
+    W[:, 1] = -np.abs(W[:, 1])
+    x = np.zeros((3, K), np.float32)
+    x[1] = -0.0
+    x[2, ::2] = -0.0
+    got = oracle.logits(x, W)
+    assert np.all(got.view(np.uint32) == 0)
+
+
 def test_one_hot_row_returns_w_row():
     rng = np.random.default_rng(8)
     K, E = 1000, 48
