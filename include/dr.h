@@ -145,8 +145,11 @@ dr_status dr_gate_dot(const void *x, dr_dtype x_dtype, const void *w, dr_dtype w
  * whatever M is, so rows are bit-identical across M; the order inside one MFMA
  * is the hardware's, so the result is within a tolerance of the exact product,
  * not bit-equal to a CPU fmaf chain.
- *   x [M,K] bf16 bits, W [K,N] bf16 bits, out [M,N] fp32.
- *   K % 64 == 0 and N % 64 == 0, else DR_ERR_UNSUPPORTED.
+ *   x [M,K] bf16 bits, W [K,N] bf16 bits, out [M,N] fp32, all row-major,
+ *   device memory owned by the caller, 16-byte aligned (else DR_ERR_INVALID).
+ *   K % 32 == 0 and N % 128 == 0; K, N <= 2^30 and M <= 65535*128, else
+ *   DR_ERR_UNSUPPORTED.  M == 0 returns DR_OK without a launch.  Errors are
+ *   reported before anything is launched.
  */
 dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K,
                        int64_t N, void *stream);
