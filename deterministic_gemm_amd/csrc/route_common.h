@@ -331,4 +331,159 @@ __device__ void route_token(const float *__restrict__ row, int64_t m, const Epil
   }
 }
 
+// Maximum of a u32 over each row of 16 lanes, returned in every lane of the row.
+__device__ __forceinline__ uint32_t row_max16(uint32_t x) {
+  x = max(x, dpp_u32<DPP_ROW_ROR8>(x));
+  x = max(x, dpp_u32<DPP_ROW_ROR4>(x));
+  x = max(x, dpp_u32<DPP_ROW_ROR2>(x));
+  x = max(x, dpp_u32<DPP_ROW_ROR1>(x));
+  return x;
+}
+
+// Pairwise tree sum over the 16 lanes of each row in lane order, returned in
+// every lane of the row: the same four levels as wave_tree_sum's first four
+// (lane 16r+15 ends up with row r's sum), then a broadcast from that lane.
+__device__ __forceinline__ float row_tree_sum16(float s) {
+  s = s + dpp_f32<DPP_QUAD_XOR1>(s);
+  s = s + dpp_f32<DPP_QUAD_XOR2>(s);
+  s = dpp_f32<DPP_ROW_ROR4>(s) + s;
+  s = dpp_f32<DPP_ROW_ROR8>(s) + s;
+  const int lane = threadIdx.x & 63;
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane | 15) << 2, __builtin_bit_cast(int, s)));
+}
+
+// Four tokens per wavefront, one per row of 16 lanes: the same results as
+// route_token, with the token's rank rounds run by 16 lanes instead of 64 so
+// that the four tokens' rounds proceed together.  Row r routes token m0 + r
+// (skipped past M), whose E logits are at lg + r * pitch in LDS (16-byte
+// aligned); lane q of the row owns experts q*V .. q*V+V-1.  After its values
+// are read, the token's LDS row is reused as the row's scratch: [0, 33) the
+// winning ids by rank, [33, 66) their keys (then their weights), 66 and 67
+// the exact values at ranks k-1 and k.  Needs pitch >= 68 and k <= 32.
+template <int E>
+__device__ void route_tokens_row16(float *lg, int pitch, int64_t m0, int64_t M, const EpilogueArgs &a) {
+  constexpr int V = E / 16;
+  static_assert(V % 4 == 0, "whole float4s per lane");
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 15, row = lane >> 4;
+  const int k = a.k;
+  const int64_t m = m0 + row;
+  const bool live = m < M;
+  float *rp = lg + row * pitch;
+
+  float v[V];
+  uint32_t key[V];
+#pragma unroll
+  for (int j4 = 0; j4 < V / 4; ++j4) {
+    const float4 t = *reinterpret_cast<const float4 *>(rp + q * V + 4 * j4);
+    v[4 * j4 + 0] = t.x;
+    v[4 * j4 + 1] = t.y;
+    v[4 * j4 + 2] = t.z;
+    v[4 * j4 + 3] = t.w;
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    if (a.logit_bf16) v[j] = bf16_to_f32(f32_to_bf16(v[j]));
+    key[j] = rank_key(v[j]) + 1u;
+  }
+
+  if (a.logits && live) {
+    if (a.logit_bf16) {
+      uint32_t pk[V / 2];
+#pragma unroll
+      for (int j = 0; j < V / 2; ++j)
+        pk[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1])) << 16);
+      uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.logits) + m * E + q * V);
+      if constexpr (V % 8 == 0) {
+#pragma unroll
+        for (int j = 0; j < V / 8; ++j)
+          reinterpret_cast<uint4 *>(o)[j] = make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) reinterpret_cast<uint2 *>(o)[j] = make_uint2(pk[2 * j], pk[2 * j + 1]);
+      }
+    } else {
+      float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(a.logits) + m * E + q * V);
+#pragma unroll
+      for (int j4 = 0; j4 < V / 4; ++j4) o[j4] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
+    }
+  }
+
+  uint32_t lm = key[0];
+#pragma unroll
+  for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
+  const uint32_t top = row_max16(lm);
+  const float mx = key_value(top);
+
+  // softmax denominator: the canonical tree over the E terms in index order
+  // is the tree over each lane's V consecutive terms, then over the 16 lanes
+  float s = 0.0f;
+  if (a.weights) {
+    float u[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) u[j] = route_exp(v[j] - mx);
+#pragma unroll
+    for (int w = V; w > 1; w >>= 1) {
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) u[i] = u[2 * i] + u[2 * i + 1];
+    }
+    s = row_tree_sum16(u[0]);
+  }
+
+  const int rounds = (k < E) ? k + 1 : k;
+  uint32_t rm = top;
+  for (int r = 0; r < rounds; ++r) {
+    if (r > 0) {
+      lm = key[0];
+#pragma unroll
+      for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
+      rm = row_max16(lm);
+    }
+    // the row's lowest lane holding the maximum, then its lowest slot
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(lm == rm);
+    const uint32_t bits = static_cast<uint32_t>(bal >> (lane & 48)) & 0xFFFFu;
+    const bool win = q == static_cast<int>(__builtin_ctz(bits));
+    int li = 0;
+#pragma unroll
+    for (int j = V - 1; j >= 0; --j) li = (key[j] == rm) ? j : li;
+    float exact = v[0];
+#pragma unroll
+    for (int j = 1; j < V; ++j) exact = (j == li) ? v[j] : exact;
+#pragma unroll
+    for (int j = 0; j < V; ++j) key[j] = (win && j == li) ? 0u : key[j];
+    if (win) {
+      rp[r] = __builtin_bit_cast(float, q * V + li);
+      rp[33 + r] = __builtin_bit_cast(float, rm);
+      if (r == k - 1) rp[66] = exact;
+      if (r == k) rp[67] = exact;
+    }
+  }
+
+  if (!live) return;
+  // ranks j = q, q + 16, ... of the row's token
+  for (int j = q; j < k; j += 16) a.ids[m * k + j] = __builtin_bit_cast(int32_t, rp[j]);
+  if (a.weights) {
+    for (int j = q; j < k; j += 16)
+      rp[33 + j] = route_exp(key_value(__builtin_bit_cast(uint32_t, rp[33 + j])) - mx) / s;
+    if (a.flags & DR_ROUTE_RENORMALIZE) {
+      float rs = rp[33];
+      for (int j = 1; j < k; ++j) rs = rs + rp[33 + j];
+      for (int j = q; j < k; j += 16) a.weights[m * k + j] = rp[33 + j] / rs;
+    } else {
+      for (int j = q; j < k; j += 16) a.weights[m * k + j] = rp[33 + j];
+    }
+  }
+  if (a.margins && q == 0) {
+    const float sel = rp[66];
+    const float rej = (k < E) ? rp[67] : -__builtin_inff();
+    dr_margin g;
+    g.sel_min = sel;
+    g.rej_max = rej;
+    g.sel_min_bf16 = f32_to_bf16(sel);
+    g.rej_max_bf16 = f32_to_bf16(rej);
+    g.ulps = (k < E) ? (bf16_ord(g.sel_min_bf16) - bf16_ord(g.rej_max_bf16)) : 0x7FFFFFFF;
+    a.margins[m] = g;
+  }
+}
+
 }  // namespace drk

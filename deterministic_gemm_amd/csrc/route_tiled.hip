@@ -198,10 +198,7 @@ __global__ __launch_bounds__(C::NT) void route_tiled_kernel(const float *__restr
         lg[tok * C::LGP + e] = out[(a * BT + b) * 4 + q];
       }
   __syncthreads();
-  for (int i = wave; i < TT; i += C::NW) {
-    const int64_t mm = m0 + i;
-    if (mm < M) route_token<E>(lg + i * C::LGP, mm, ea);
-  }
+  for (int i = 4 * wave; i < TT; i += 4 * C::NW) route_tokens_row16<E>(lg + i * C::LGP, C::LGP, m0 + i, M, ea);
 }
 
 // ---------------------------------------------------------------------------
@@ -485,10 +482,7 @@ __global__ __launch_bounds__(C::NT) void route_tiled_dma_kernel(const float *__r
         lg[tok * C::LGP + e] = outv[((a * BT + b) * 4 + q) / 16][((a * BT + b) * 4 + q) % 16];
       }
   __syncthreads();
-  for (int i = wave; i < TT; i += C::NW) {
-    const int64_t mm = m0 + i;
-    if (mm < M) route_token<E>(lg + i * C::LGP, mm, ea);
-  }
+  for (int i = 4 * wave; i < TT; i += 4 * C::NW) route_tokens_row16<E>(lg + i * C::LGP, C::LGP, m0 + i, M, ea);
 }
 
 template <class C, int MAXL>
