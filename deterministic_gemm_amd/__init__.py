@@ -10,7 +10,8 @@ the GPU, the call raises.
 
 x is [M,K] float32 or bfloat16 on the GPU, W is [K,E] float32.  The functions
 mirror the C entry points: route -> dr_route, route_variant ->
-dr_route_variant, gate_dot -> dr_gate_dot, gemm_bf16 -> dr_gemm_bf16,
+dr_route_variant, route_logits -> dr_route_logits, route_select ->
+dr_route_select, gate_dot -> dr_gate_dot, gemm_bf16 -> dr_gemm_bf16,
 contract -> dr_contract.
 """
 from __future__ import annotations
@@ -26,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdr.so")
 
 DR_OK, DR_ERR_INVALID, DR_ERR_UNSUPPORTED, DR_ERR_DEVICE = 0, 1, 2, 3
 DR_F32, DR_BF16 = 0, 1
-VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2}
+VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 DR_ROUTE_RENORMALIZE = 1
 
@@ -36,8 +37,8 @@ MARGIN_DTYPE = np.dtype(
 )
 
 EXPORTED = (
-    "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_gate_dot", "dr_gemm_bf16",
-    "dr_contract", "dr_status_string", "dr_last_error",
+    "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
+    "dr_gate_dot", "dr_gemm_bf16", "dr_contract", "dr_status_string", "dr_last_error",
 )
 
 
@@ -69,8 +70,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dr_route_variant.argtypes = [P, ctypes.c_int, P, i64, i64, i64, i32, ctypes.c_int, P, P, P, P, u32,
                                    ctypes.c_int, P]
     L.dr_route_variant.restype = ctypes.c_int
-    L.dr_route_auto_variant.argtypes = [i64, i64, i64]
+    L.dr_route_auto_variant.argtypes = [i64, i64, i64, ctypes.c_int, ctypes.c_int]
     L.dr_route_auto_variant.restype = ctypes.c_int
+    L.dr_route_logits.argtypes = [P, P, i64, i64, i64, ctypes.c_int, P, P]
+    L.dr_route_logits.restype = ctypes.c_int
+    L.dr_route_select.argtypes = [P, ctypes.c_int, i64, i64, i32, P, P, P, u32, P]
+    L.dr_route_select.restype = ctypes.c_int
     L.dr_gate_dot.argtypes = [P, ctypes.c_int, P, ctypes.c_int, P, P, i64, i64, P]
     L.dr_gate_dot.restype = ctypes.c_int
     L.dr_gemm_bf16.argtypes = [P, P, P, i64, i64, i64, P]
@@ -116,8 +121,10 @@ def contract() -> dict:
     return {n: getattr(c, n) for n, _ in _Contract._fields_}
 
 
-def auto_variant(M: int, K: int, E: int) -> str:
-    return VARIANT_NAMES[load_library().dr_route_auto_variant(M, K, E)]
+def auto_variant(M: int, K: int, E: int, x_dtype: str = "f32", logits: bool = True) -> str:
+    """dr_route_auto_variant: the kernel family dr_route runs for this call shape."""
+    xd = {"f32": DR_F32, "bf16": DR_BF16}[x_dtype]
+    return VARIANT_NAMES[load_library().dr_route_auto_variant(M, K, E, xd, int(bool(logits)))]
 
 
 def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, logits: bool = True,
@@ -160,6 +167,48 @@ def route_variant(x, W, k: int, variant: str, **kw):
     return route(x, W, k, variant=variant, **kw)
 
 
+def route_logits(x, W, *, logit_dtype: str = "f32", out=None):
+    """dr_route_logits: x [M,K] float32, W [K,E] float32 -> logits [M,E]
+    float32 (or bfloat16 with logit_dtype="bf16")."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.float32,))
+    _dev_tensor(W, "W", (torch.float32,))
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[0]:
+        raise ValueError("x must be [M,K] and W [K,E]")
+    M, K = x.shape
+    E = W.shape[1]
+    ldt = {"f32": DR_F32, "bf16": DR_BF16}[logit_dtype]
+    if out is None:
+        out = torch.empty((M, E), dtype=torch.float32 if ldt == DR_F32 else torch.bfloat16, device=x.device)
+    st = L.dr_route_logits(_ptr(x), _ptr(W), M, K, E, ldt, _ptr(out), _stream(x.device))
+    _check(st, "dr_route_logits")
+    return out
+
+
+def route_select(logits, k: int, *, renormalize: bool = False, weights: bool = True, margins: bool = True,
+                 out=None):
+    """dr_route_select: logits [M,E] float32 or bfloat16 -> (ids [M,k] int32,
+    weights [M,k] float32 or None, margins [M,4] int32 raw dr_margin records
+    or None)."""
+    L = load_library()
+    _dev_tensor(logits, "logits", (torch.float32, torch.bfloat16))
+    if logits.dim() != 2:
+        raise ValueError("logits must be [M,E]")
+    M, E = logits.shape
+    dev = logits.device
+    if out is not None:
+        ids_t, w_t, mg_t = out
+    else:
+        ids_t = torch.empty((M, k), dtype=torch.int32, device=dev)
+        w_t = torch.empty((M, k), dtype=torch.float32, device=dev) if weights else None
+        mg_t = torch.empty((M, 4), dtype=torch.int32, device=dev) if margins else None
+    ldt = DR_F32 if logits.dtype == torch.float32 else DR_BF16
+    st = L.dr_route_select(_ptr(logits), ldt, M, E, k, _ptr(ids_t), _ptr(w_t), _ptr(mg_t),
+                           DR_ROUTE_RENORMALIZE if renormalize else 0, _stream(dev))
+    _check(st, "dr_route_select")
+    return ids_t, w_t, mg_t
+
+
 def gate_dot(x, w, *, dot: bool = True, gate: bool = True):
     """dr_gate_dot: returns (dot [M] float32 or None, gate [M] float32 or None)."""
     L = load_library()
@@ -199,6 +248,8 @@ def margins_to_numpy(mg: torch.Tensor) -> np.ndarray:
 
 dr_route = route
 dr_route_variant = route_variant
+dr_route_logits = route_logits
+dr_route_select = route_select
 dr_gate_dot = gate_dot
 dr_gemm_bf16 = gemm_bf16
 dr_contract = contract

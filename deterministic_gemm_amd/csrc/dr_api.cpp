@@ -38,6 +38,9 @@ constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
 // inside the 19..80 token m-scan on purpose, so that scan crosses a dispatch
 // change and shows it cannot move a bit.
 constexpr int64_t kTiledMinM = 48;
+// Batches at or above this size that ask for the logits run as two kernels
+// (a squarer logits tile, then the selection); below it the fused kernel.
+constexpr int64_t kSplitMinM = 2048;
 
 dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
                      int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
@@ -51,7 +54,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   if (x_dtype != DR_F32 && x_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad x_dtype");
   if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
   if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
-  if (variant != DR_VARIANT_AUTO && variant != DR_VARIANT_ROWWISE && variant != DR_VARIANT_TILED)
+  if (variant != DR_VARIANT_AUTO && variant != DR_VARIANT_ROWWISE && variant != DR_VARIANT_TILED &&
+      variant != DR_VARIANT_SPLIT)
     return fail(DR_ERR_INVALID, "bad variant");
   if (M > 0 && (!x || !W || !ids)) return fail(DR_ERR_INVALID, "x, W and ids are required");
   if (!aligned16(x) || !aligned16(W) || !aligned16(ids) || !aligned16(weights) || !aligned16(logits) ||
@@ -61,9 +65,12 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
     return fail(DR_ERR_UNSUPPORTED, "E=%lld: supported E are 64, 128, 256, 512, 1024", (long long)E);
   if (K > kMaxK) return fail(DR_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K, (long long)kMaxK);
   if (k > kMaxTopK) return fail(DR_ERR_UNSUPPORTED, "k=%d above %d", k, kMaxTopK);
-  if (variant == DR_VARIANT_AUTO) variant = dr_route_auto_variant(M, K, E);
+  if (variant == DR_VARIANT_AUTO) variant = dr_route_auto_variant(M, K, E, x_dtype, logits != nullptr);
   if (variant == DR_VARIANT_TILED && !drk::tiled_supports(E, K))
     return fail(DR_ERR_UNSUPPORTED, "tiled variant does not support E=%lld", (long long)E);
+  if (variant == DR_VARIANT_SPLIT && !drk::split_supports(E, K, x_dtype == DR_F32, logits != nullptr))
+    return fail(DR_ERR_UNSUPPORTED,
+                "split variant needs fp32 x, K %% 4 == 0, E in {256, 512} and the logits output");
   if (M == 0) return DR_OK;
 
   drk::RouteLaunch L;
@@ -81,8 +88,9 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   L.logits = logits;
   L.margins = margins;
   L.stream = static_cast<hipStream_t>(stream);
-  const hipError_t e =
-      variant == DR_VARIANT_TILED ? drk::launch_route_tiled(L) : drk::launch_route_rowwise(L);
+  const hipError_t e = variant == DR_VARIANT_SPLIT   ? drk::launch_route_split(L)
+                       : variant == DR_VARIANT_TILED ? drk::launch_route_tiled(L)
+                                                     : drk::launch_route_rowwise(L);
   return device_status(e, "route launch");
 }
 
@@ -90,7 +98,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
 
 extern "C" {
 
-dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E) {
+dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits) {
+  if (M >= kSplitMinM && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
   if (M >= kTiledMinM && drk::tiled_supports(E, K)) return DR_VARIANT_TILED;
   return DR_VARIANT_ROWWISE;
 }
@@ -108,6 +117,62 @@ dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int6
                            dr_variant variant, void *stream) {
   return route_impl(x, x_dtype, W, M, K, E, k, logit_dtype, ids, weights, logits, margins, flags,
                     variant, stream);
+}
+
+dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, int64_t E,
+                          dr_dtype logit_dtype, void *logits, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || M > kMaxM) return fail(DR_ERR_INVALID, "M=%lld out of range", (long long)M);
+  if (K < 1) return fail(DR_ERR_INVALID, "K=%lld must be >= 1", (long long)K);
+  if (E < 1) return fail(DR_ERR_INVALID, "E=%lld must be >= 1", (long long)E);
+  if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
+  if (M > 0 && (!x || !W || !logits)) return fail(DR_ERR_INVALID, "x, W and logits are required");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(logits))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (!drk::split_supports(E, K, true, true))
+    return fail(DR_ERR_UNSUPPORTED, "dr_route_logits needs K %% 4 == 0, K <= %lld and E in {256, 512}",
+                (long long)kMaxK);
+  if (M == 0) return DR_OK;
+  drk::RouteLaunch L{};
+  L.xf = x;
+  L.W = W;
+  L.M = M;
+  L.K = K;
+  L.E = E;
+  L.logit_bf16 = logit_dtype == DR_BF16;
+  L.logits = logits;
+  L.stream = static_cast<hipStream_t>(stream);
+  return device_status(drk::launch_route_logits(L), "logits launch");
+}
+
+dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, int64_t E, int32_t k,
+                          int32_t *ids, float *weights, dr_margin *margins, uint32_t flags,
+                          void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || M > kMaxM) return fail(DR_ERR_INVALID, "M=%lld out of range", (long long)M);
+  if (E < 1) return fail(DR_ERR_INVALID, "E=%lld must be >= 1", (long long)E);
+  if (k < 1 || k > E) return fail(DR_ERR_INVALID, "k=%d must be in [1, E=%lld]", k, (long long)E);
+  if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
+  if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (M > 0 && (!logits || !ids)) return fail(DR_ERR_INVALID, "logits and ids are required");
+  if (!aligned16(logits) || !aligned16(ids) || !aligned16(weights) || !aligned16(margins))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (!drk::select_supports(E))
+    return fail(DR_ERR_UNSUPPORTED, "E=%lld: dr_route_select supports E in {64, 128, 256, 512}", (long long)E);
+  if (k > kMaxTopK) return fail(DR_ERR_UNSUPPORTED, "k=%d above %d", k, kMaxTopK);
+  if (M == 0) return DR_OK;
+  drk::RouteLaunch L{};
+  L.M = M;
+  L.E = E;
+  L.k = k;
+  L.logit_bf16 = logit_dtype == DR_BF16;
+  L.flags = flags;
+  L.ids = ids;
+  L.weights = weights;
+  L.logits = const_cast<void *>(logits);
+  L.margins = margins;
+  L.stream = static_cast<hipStream_t>(stream);
+  return device_status(drk::launch_route_select(L), "select launch");
 }
 
 dr_status dr_gate_dot(const void *x, dr_dtype x_dtype, const void *w, dr_dtype w_dtype,

@@ -27,6 +27,12 @@ struct RouteLaunch {
 hipError_t launch_route_rowwise(const RouteLaunch &L);
 hipError_t launch_route_tiled(const RouteLaunch &L);
 bool tiled_supports(int64_t E, int64_t K);
+hipError_t launch_route_split(const RouteLaunch &L);
+bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
+// The two halves of the split family on their own.
+hipError_t launch_route_logits(const RouteLaunch &L);
+hipError_t launch_route_select(const RouteLaunch &L);
+bool select_supports(int64_t E);
 
 hipError_t launch_gate_dot(const void *x, int x_bf16, const void *w, int w_bf16, float *dot,
                            float *gate, int64_t M, int64_t K, hipStream_t stream);

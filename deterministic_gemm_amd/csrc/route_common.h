@@ -46,11 +46,14 @@ __device__ __forceinline__ int32_t bf16_ord(uint16_t b) {
 // fused steps (ln2 split high + low), p = degree-7 Taylor polynomial in Horner
 // form with fused steps and fp32 coefficients 1/i!, result p * 2^n with 2^n
 // built exactly (n >= -126).  t < -87 gives +0; t > 0 or NaN gives NaN.
+//
+// Written without branches: the steps run on t clamped to [-87.5, 0] (equal
+// to t wherever their result is used; NaN becomes -87.5) and the out-of-range
+// cases are selected at the end, so a wavefront never diverges here.
 __device__ __forceinline__ float route_exp(float t) {
-  if (!(t <= 0.0f)) return u2f(0x7FC00000u);
-  if (t < -87.0f) return 0.0f;
-  const float n = __builtin_rintf(t * 0x1.715476p+0f);
-  float r = __builtin_fmaf(-n, 0x1.62e43p-1f, t);
+  const float tc = __builtin_fminf(__builtin_fmaxf(t, -87.5f), 0.0f);
+  const float n = __builtin_rintf(tc * 0x1.715476p+0f);
+  float r = __builtin_fmaf(-n, 0x1.62e43p-1f, tc);
   r = __builtin_fmaf(-n, -0x1.05c61p-29f, r);
   float p = 0x1.a01a02p-13f;                 // 1/7!
   p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f); // 1/6!
@@ -61,7 +64,8 @@ __device__ __forceinline__ float route_exp(float t) {
   p = __builtin_fmaf(p, r, 1.0f);            // 1/1!
   p = __builtin_fmaf(p, r, 1.0f);            // 1/0!
   const int ni = static_cast<int>(n);
-  return p * u2f(static_cast<uint32_t>(ni + 127) << 23);
+  const float e = p * u2f(static_cast<uint32_t>(ni + 127) << 23);
+  return (t <= 0.0f) ? ((t < -87.0f) ? 0.0f : e) : u2f(0x7FC00000u);
 }
 
 // Unsigned key whose order is the ranking order of values: NaN lowest (0),
@@ -352,66 +356,53 @@ __device__ __forceinline__ float row_tree_sum16(float s) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((lane | 15) << 2, __builtin_bit_cast(int, s)));
 }
 
-// Four tokens per wavefront, one per row of 16 lanes: the same results as
-// route_token, with the token's rank rounds run by 16 lanes instead of 64 so
-// that the four tokens' rounds proceed together.  Row r routes token m0 + r
-// (skipped past M), whose E logits are at lg + r * pitch in LDS (16-byte
-// aligned); lane q of the row owns experts q*V .. q*V+V-1.  After its values
-// are read, the token's LDS row is reused as the row's scratch: [0, 33) the
-// winning ids by rank, [33, 66) their keys (then their weights), 66 and 67
-// the exact values at ranks k-1 and k.  Needs pitch >= 68 and k <= 32.
-template <int E>
-__device__ void route_tokens_row16(float *lg, int pitch, int64_t m0, int64_t M, const EpilogueArgs &a) {
-  constexpr int V = E / 16;
-  static_assert(V % 4 == 0, "whole float4s per lane");
-  const int lane = threadIdx.x & 63;
-  const int q = lane & 15, row = lane >> 4;
-  const int k = a.k;
-  const int64_t m = m0 + row;
-  const bool live = m < M;
-  float *rp = lg + row * pitch;
+// Maximum / bitwise or of a lane's N values as a balanced tree (short
+// dependency chains).
+template <int N>
+__device__ __forceinline__ uint32_t lane_max(const uint32_t (&a)[N]) {
+  uint32_t t[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) t[j] = a[j];
+#pragma unroll
+  for (int w = N; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) t[i] = max(t[i], t[i + w / 2]);
+  return t[0];
+}
 
-  float v[V];
+template <int N>
+__device__ __forceinline__ uint32_t lane_or(const uint32_t (&a)[N]) {
+  uint32_t t[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) t[j] = a[j];
+#pragma unroll
+  for (int w = N; w > 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w / 2; ++i) t[i] = t[i] | t[i + w / 2];
+  return t[0];
+}
+
+// Selection, weights and margin for four tokens per wavefront, one per row of
+// 16 lanes: the same results as route_token, with a token's rank rounds run by
+// 16 lanes instead of 64 so that four tokens' rounds proceed together.  Lane q
+// of row r holds in v the selection values of experts q*V .. q*V+V-1 of token
+// m (bf16-rounded already in bf16-logit mode); rp is the row's LDS scratch of
+// at least 68 floats: [0, 33) the winning ids by rank, [33, 66) their keys
+// (then their weights), 66 and 67 the exact values at ranks k-1 and k.  Rows
+// with live == false compute but store nothing.  Needs k <= 32.
+template <int E>
+__device__ void route_select_row16(const float (&v)[E / 16], float *rp, int64_t m, bool live,
+                                   const EpilogueArgs &a) {
+  constexpr int V = E / 16;
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 15;
+  const int k = a.k;
+
   uint32_t key[V];
 #pragma unroll
-  for (int j4 = 0; j4 < V / 4; ++j4) {
-    const float4 t = *reinterpret_cast<const float4 *>(rp + q * V + 4 * j4);
-    v[4 * j4 + 0] = t.x;
-    v[4 * j4 + 1] = t.y;
-    v[4 * j4 + 2] = t.z;
-    v[4 * j4 + 3] = t.w;
-  }
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    if (a.logit_bf16) v[j] = bf16_to_f32(f32_to_bf16(v[j]));
-    key[j] = rank_key(v[j]) + 1u;
-  }
+  for (int j = 0; j < V; ++j) key[j] = rank_key(v[j]) + 1u;
 
-  if (a.logits && live) {
-    if (a.logit_bf16) {
-      uint32_t pk[V / 2];
-#pragma unroll
-      for (int j = 0; j < V / 2; ++j)
-        pk[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1])) << 16);
-      uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.logits) + m * E + q * V);
-      if constexpr (V % 8 == 0) {
-#pragma unroll
-        for (int j = 0; j < V / 8; ++j)
-          reinterpret_cast<uint4 *>(o)[j] = make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < V / 4; ++j) reinterpret_cast<uint2 *>(o)[j] = make_uint2(pk[2 * j], pk[2 * j + 1]);
-      }
-    } else {
-      float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(a.logits) + m * E + q * V);
-#pragma unroll
-      for (int j4 = 0; j4 < V / 4; ++j4) o[j4] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
-    }
-  }
-
-  uint32_t lm = key[0];
-#pragma unroll
-  for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
+  uint32_t lm = lane_max<V>(key);
   const uint32_t top = row_max16(lm);
   const float mx = key_value(top);
 
@@ -434,28 +425,29 @@ __device__ void route_tokens_row16(float *lg, int pitch, int64_t m0, int64_t M, 
   uint32_t rm = top;
   for (int r = 0; r < rounds; ++r) {
     if (r > 0) {
-      lm = key[0];
-#pragma unroll
-      for (int j = 1; j < V; ++j) lm = max(lm, key[j]);
+      lm = lane_max<V>(key);
       rm = row_max16(lm);
     }
-    // the row's lowest lane holding the maximum, then its lowest slot
+    // the row's lowest lane holding the maximum, then its lowest slot: the
+    // slots equal to the maximum as a bit mask, its lowest set bit
     const uint64_t bal = __builtin_amdgcn_ballot_w64(lm == rm);
     const uint32_t bits = static_cast<uint32_t>(bal >> (lane & 48)) & 0xFFFFu;
     const bool win = q == static_cast<int>(__builtin_ctz(bits));
-    int li = 0;
+    uint32_t hit[V];
 #pragma unroll
-    for (int j = V - 1; j >= 0; --j) li = (key[j] == rm) ? j : li;
-    float exact = v[0];
-#pragma unroll
-    for (int j = 1; j < V; ++j) exact = (j == li) ? v[j] : exact;
+    for (int j = 0; j < V; ++j) hit[j] = (key[j] == rm) ? (1u << j) : 0u;
+    const int li = static_cast<int>(__builtin_ctz(lane_or<V>(hit) | (1u << (V - 1))));
 #pragma unroll
     for (int j = 0; j < V; ++j) key[j] = (win && j == li) ? 0u : key[j];
     if (win) {
       rp[r] = __builtin_bit_cast(float, q * V + li);
       rp[33 + r] = __builtin_bit_cast(float, rm);
-      if (r == k - 1) rp[66] = exact;
-      if (r == k) rp[67] = exact;
+      if (r >= k - 1) {
+        float exact = v[0];
+#pragma unroll
+        for (int j = 1; j < V; ++j) exact = (j == li) ? v[j] : exact;
+        rp[66 + (r - (k - 1))] = exact;
+      }
     }
   }
 
@@ -484,6 +476,58 @@ __device__ void route_tokens_row16(float *lg, int pitch, int64_t m0, int64_t M, 
     g.ulps = (k < E) ? (bf16_ord(g.sel_min_bf16) - bf16_ord(g.rej_max_bf16)) : 0x7FFFFFFF;
     a.margins[m] = g;
   }
+}
+
+// The fused kernels' epilogue: row r of the wavefront takes token m0 + r
+// (skipped past M), whose E canonical fp32 logits are at lg + r * pitch in
+// LDS (16-byte aligned, pitch >= 68): it stores the token's logits in the
+// requested dtype, then selects; the token's LDS row becomes its scratch.
+template <int E>
+__device__ void route_tokens_row16(float *lg, int pitch, int64_t m0, int64_t M, const EpilogueArgs &a) {
+  constexpr int V = E / 16;
+  static_assert(V % 4 == 0, "whole float4s per lane");
+  const int lane = threadIdx.x & 63;
+  const int q = lane & 15, row = lane >> 4;
+  const int64_t m = m0 + row;
+  const bool live = m < M;
+  float *rp = lg + row * pitch;
+
+  float v[V];
+#pragma unroll
+  for (int j4 = 0; j4 < V / 4; ++j4) {
+    const float4 t = *reinterpret_cast<const float4 *>(rp + q * V + 4 * j4);
+    v[4 * j4 + 0] = t.x;
+    v[4 * j4 + 1] = t.y;
+    v[4 * j4 + 2] = t.z;
+    v[4 * j4 + 3] = t.w;
+  }
+  if (a.logit_bf16) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = bf16_to_f32(f32_to_bf16(v[j]));
+  }
+
+  if (a.logits && live) {
+    if (a.logit_bf16) {
+      uint32_t pk[V / 2];
+#pragma unroll
+      for (int j = 0; j < V / 2; ++j)
+        pk[j] = static_cast<uint32_t>(f32_to_bf16(v[2 * j])) | (static_cast<uint32_t>(f32_to_bf16(v[2 * j + 1])) << 16);
+      uint32_t *o = reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(a.logits) + m * E + q * V);
+      if constexpr (V % 8 == 0) {
+#pragma unroll
+        for (int j = 0; j < V / 8; ++j)
+          reinterpret_cast<uint4 *>(o)[j] = make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < V / 4; ++j) reinterpret_cast<uint2 *>(o)[j] = make_uint2(pk[2 * j], pk[2 * j + 1]);
+      }
+    } else {
+      float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(a.logits) + m * E + q * V);
+#pragma unroll
+      for (int j4 = 0; j4 < V / 4; ++j4) o[j4] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
+    }
+  }
+  route_select_row16<E>(v, rp, m, live, a);
 }
 
 }  // namespace drk

@@ -1,0 +1,401 @@
+// route_split.hip -- the router as two kernels, for large batches that also
+// ask for the logits.
+//
+//  1. route_split_logits_kernel: the canonical-order logits GEMM on fp32
+//     matrix cores over (token tile, expert tile) workgroups -- 64 tokens x
+//     128 experts instead of the fused kernel's 32 x E -- written to the
+//     caller's logits buffer in the requested dtype.  A squarer tile moves
+//     fewer bytes into LDS per multiply-add: per step of K, 64 + 128 operand
+//     values feed 8192 products, against 32 + 256 in the fused kernel.
+//  2. route_split_epilogue_kernel: top-k, softmax weights and margin per
+//     token, reading those logits back (four tokens per wavefront).
+//
+// Each output is produced by exactly the operations of the canonical order
+// (the same chains, K-block slots, lane-local tree levels and group counter
+// tree as the fused kernel, see route_tiled.hip), and the epilogue is the
+// fused kernel's, so every result is bit-identical to the fused and row-wise
+// kernels for every M ("Batch changed the model's mind", section "The fix:
+// m-invariant twins": the tile shape is a performance seam, never a numeric
+// one).  In bf16-logit mode the logits are stored rounded and the epilogue
+// selects on those stored values, which are the values the fused kernel
+// selects on.
+#include "route_common.h"
+#include "lds_dma.h"
+#include "launch.h"
+
+namespace drk {
+
+// A wavefront owns 16*AT tokens x 16*BT experts as AT x BT tiles of 16x16.
+template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_>
+struct SplitCfg {
+  static constexpr int E = E_, ET = ET_, AT = AT_, BT = BT_, WT = WT_, KC = KC_, S = S_;
+  static constexpr int EW = 16 * BT;          // experts per wavefront
+  static constexpr int NWE = ET / EW;         // wavefronts across the expert tile
+  static constexpr int NW = NWE * WT;         // wavefronts per workgroup
+  static constexpr int NT = NW * 64;          // threads per workgroup
+  static constexpr int TW = 16 * AT;          // tokens per wavefront
+  static constexpr int TT = WT * TW;          // tokens per workgroup
+  static constexpr int NET = E / ET;          // expert tiles
+  static constexpr int HU = KC / 4;           // 16-byte x units per (slot, token) row
+  static constexpr int SW = KC * ET + 16;     // W slot stride (floats), +16 staggers banks
+  static constexpr int WST = 4 * SW;          // W floats per stage
+  static constexpr int XST = 4 * TT * KC;     // x floats per stage
+  static constexpr int STG = WST + XST;       // floats per stage
+  static constexpr int LGP = ET + 4;          // logit tile pitch (floats)
+  static constexpr int WI = 4 * KC * ET / 256;  // W transfers (64 lanes x 16 B) per chunk
+  static constexpr int WIW = WI / NW;           // ... per wavefront
+  static constexpr int XU = TT * KC;            // x 16-byte units per chunk
+  static constexpr int XI = XU / 64;            // x transfers per chunk
+  static constexpr int XIW = XI / NW;           // ... per wavefront
+  static constexpr int PER = WIW + XIW;         // transfers per chunk per wavefront
+  static constexpr int CPG = 256 / KC;          // chunks per group of four K-blocks
+  static_assert(NWE * EW == ET, "whole wavefront expert tiles");
+  static_assert(WIW * NW == WI && WIW >= 1, "W transfers split evenly");
+  static_assert(XI * 64 == XU && XIW * NW == XI && XIW >= 1, "x transfers split evenly");
+  static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
+  static_assert(PER * (S - 2) <= 63, "vmcnt range");
+  static_assert(KC % 4 == 0 && 256 % KC == 0 && S == 4, "chunking");
+  static_assert(TT * LGP <= S * STG, "the logit tile fits in the stages");
+  static_assert(E % ET == 0, "whole expert tiles");
+  __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
+};
+
+// Transfers of chunk ci into `stage`; the same scheme as the fused kernel's
+// dma_issue (route_tiled.hip), with W columns e0 .. e0+ET-1 only.
+template <class C>
+__device__ __forceinline__ void split_issue(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+                                            int K, int64_t m0, int e0, int nb, int nchunks, int wave, int lane,
+                                            int ci, float *stage) {
+  constexpr int E = C::E, ET = C::ET, KC = C::KC, TT = C::TT, HU = C::HU;
+  const int g = ci / C::CPG;
+  const int kk0 = (ci % C::CPG) * KC;
+  const bool live = ci < nchunks;
+  const bool full_k = live && (4 * g + 3 < nb) && ((4 * g + 3) * 256 + kk0 + KC <= K);
+  const bool full_m = m0 + TT <= M;
+  const float *Wt = W + e0;
+#pragma unroll
+  for (int i = 0; i < C::WIW; ++i) {
+    const int j = wave * C::WIW + i;            // transfer index within the chunk
+    const int s = j / (KC * ET / 256);          // slot
+    const int uo = (j % (KC * ET / 256)) * 64;  // first 16-byte unit within the slot
+    const int u = uo + lane;
+    const int c = u / (ET / 4), e4 = u % (ET / 4);
+    const int blk = 4 * g + s;
+    const int kg = blk * 256 + kk0 + c;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + s * C::SW + uo * 4));
+    if (full_k) {
+      dma16_s(Wt, static_cast<uint32_t>((kg * E + 4 * e4) * 4), lds);
+    } else {
+      const void *src = &g_pad_neg;
+      if (live && blk < nb && kg < K) src = Wt + static_cast<int64_t>(kg) * E + 4 * e4;
+      dma16(src, lds);
+    }
+  }
+  const float *xrow0 = xf + m0 * K;
+#pragma unroll
+  for (int i = 0; i < C::XIW; ++i) {
+    const int u = (wave * C::XIW + i) * 64 + lane;  // x unit within the chunk
+    const int s = u / (TT * HU);
+    const int rem = u % (TT * HU);
+    const int tok = rem / HU, hp = rem % HU;
+    const int h = hp ^ C::swz(tok);
+    const int blk = 4 * g + s;
+    const int kg = blk * 256 + kk0 + 4 * h;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + C::WST + (wave * C::XIW + i) * 64 * 4));
+    if (full_k && full_m) {
+      dma16_s(xrow0, static_cast<uint32_t>((tok * K + kg) * 4), lds);
+    } else {
+      const int64_t m = m0 + tok;
+      const void *src = &g_pad_pos;
+      if (live && blk < nb && kg < K && m < M) src = xf + m * K + kg;
+      dma16(src, lds);
+    }
+  }
+}
+
+// One chunk: retire its transfers, publish them, refill the stage freed by
+// the previous chunk, then 4 slots x KC chain steps on the matrix cores; at
+// the end of a group of four K-blocks, fold the group's partials.
+template <class C, int MAXL>
+__device__ __forceinline__ void split_step(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+                                           int K, int64_t m0, int e0, int nb, int nchunks, int wave, int lane,
+                                           int ci, const float *cur, float *refill, f32x16 (&acc)[C::AT][C::BT],
+                                           f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
+  constexpr int ET = C::ET, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, S = C::S, HU = C::HU;
+  const int s_l = lane >> 4, r_l = lane & 15;
+  const int tb = (wave / C::NWE) * C::TW;
+  const int eb = (wave % C::NWE) * C::EW;
+  const int g = ci / C::CPG;
+  const int cg = ci % C::CPG;
+  if (cg == 0) {
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const float init = (4 * g + s < nb) ? 0.0f : -0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[a][b][4 * s + q] = init;
+        }
+  }
+  compiler_fence();
+  wait_vmcnt<C::PER * (S - 2)>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + S - 1, refill);
+
+  const float *xs = cur + C::WST;
+#pragma unroll
+  for (int c4 = 0; c4 < KC / 4; ++c4) {
+    float4 av[AT];
+#pragma unroll
+    for (int a = 0; a < AT; ++a) {
+      const int tok = tb + a * 16 + r_l;
+      av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+    }
+    float bw[BT][4];
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bw[b][q] = cur[s_l * C::SW + (4 * c4 + q) * ET + eb + b * 16 + r_l];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BT; ++b) {
+          const float aval = (q == 0) ? av[a].x : (q == 1) ? av[a].y : (q == 2) ? av[a].z : av[a].w;
+          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[b][q], acc[a][b], 0, 0, 0);
+        }
+  }
+
+  if (cg == C::CPG - 1) {
+    // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
+    constexpr int NV = AT * BT * 4 / 16;
+    f32x16 qv[NV];
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int o = (a * BT + b) * 4 + q;
+          qv[o / 16][o % 16] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
+        }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) tree_push_vec<MAXL>(stk[v], qv[v], g);
+  }
+}
+
+// Workgroup -> (token tile, expert tile).  Workgroups are placed on the eight
+// XCDs in turn, so the NET expert tiles of one token tile are given block
+// indices eight apart: they land on the same XCD and share its L2, and x is
+// fetched from HBM once.  Blocks past the last token tile exit at once.
+template <class C, int MAXL>
+__global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const float *__restrict__ xf,
+                                                                   const float *__restrict__ W, int64_t M, int K,
+                                                                   void *logits, int logit_bf16) {
+  constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, STG = C::STG;
+  __shared__ __attribute__((aligned(16))) float smem[S * STG];
+  float *const stg0 = smem;
+  float *const stg1 = smem + STG;
+  float *const stg2 = smem + 2 * STG;
+  float *const stg3 = smem + 3 * STG;
+
+  const int64_t bid = blockIdx.x;
+  const int64_t hi = bid / 8;
+  const int et = static_cast<int>(hi % C::NET);
+  const int64_t tt = (hi / C::NET) * 8 + bid % 8;
+  const int64_t m0 = tt * TT;
+  if (m0 >= M) return;
+  const int e0 = et * ET;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int s_l = lane >> 4, r_l = lane & 15;
+  const int tb = (wave / C::NWE) * C::TW;
+  const int eb = (wave % C::NWE) * C::EW;
+  const int nb = (K + 255) / 256;
+  const int G = (nb + 3) / 4;
+  const int nchunks = G * C::CPG;  // a multiple of S
+
+  f32x16 acc[AT][BT];
+  f32x16 stk[AT * BT * 4 / 16][MAXL];
+
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, 0, stg0);
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, 1, stg1);
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, 2, stg2);
+  for (int ci = 0; ci < nchunks; ci += 4) {
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 0, stg0, stg3, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 1, stg1, stg0, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 2, stg2, stg1, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 3, stg3, stg2, acc, stk);
+  }
+
+  f32x16 outv[AT * BT * 4 / 16];
+#pragma unroll
+  for (int v = 0; v < AT * BT * 4 / 16; ++v) outv[v] = tree_final_vec<MAXL>(stk[v], G);
+
+  // drain the trailing padding transfers, then stage the tile for row stores
+  compiler_fence();
+  wait_vmcnt<0>();
+  __syncthreads();
+  // lane (s_l, r_l) holds token tb + 16a + 4s_l + q at expert eb + 16b + r_l
+  float *lg = smem;
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int tok = tb + a * 16 + 4 * s_l + q;
+        const int o = (a * BT + b) * 4 + q;
+        lg[tok * C::LGP + eb + b * 16 + r_l] = outv[o / 16][o % 16];
+      }
+  __syncthreads();
+  if (!logit_bf16) {
+    float *out = static_cast<float *>(logits);
+    for (int u = t; u < TT * ET / 4; u += C::NT) {
+      const int tok = u / (ET / 4), c4 = u % (ET / 4);
+      const int64_t m = m0 + tok;
+      if (m < M)
+        *reinterpret_cast<float4 *>(out + m * C::E + e0 + 4 * c4) =
+            *reinterpret_cast<const float4 *>(lg + tok * C::LGP + 4 * c4);
+    }
+  } else {
+    uint16_t *out = static_cast<uint16_t *>(logits);
+    for (int u = t; u < TT * ET / 8; u += C::NT) {
+      const int tok = u / (ET / 8), c8 = u % (ET / 8);
+      const int64_t m = m0 + tok;
+      if (m < M) {
+        const float *src = lg + tok * C::LGP + 8 * c8;
+        uint32_t pk[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pk[j] = static_cast<uint32_t>(f32_to_bf16(src[2 * j])) |
+                  (static_cast<uint32_t>(f32_to_bf16(src[2 * j + 1])) << 16);
+        *reinterpret_cast<uint4 *>(out + m * C::E + e0 + 8 * c8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      }
+    }
+  }
+}
+
+// Four tokens per wavefront, 16 per workgroup: each row of 16 lanes reads
+// its token's logits (as stored: fp32, or bf16 widened exactly) and runs the
+// fused kernels' selection epilogue.
+template <int E>
+__global__ __launch_bounds__(256) void route_split_epilogue_kernel(int64_t M, EpilogueArgs ea) {
+  constexpr int V = E / 16;
+  __shared__ __attribute__((aligned(16))) float scr[16][68];
+  const int t = threadIdx.x;
+  const int lane = t & 63, q = lane & 15;
+  const int slot = t >> 4;  // wavefront * 4 + row
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * 16 + slot;
+  const bool live = m < M;
+  float v[V];
+  if (live) {
+    if (ea.logit_bf16) {
+      const uint16_t *src = static_cast<const uint16_t *>(ea.logits) + m * E + q * V;
+      uint32_t p[V / 2];
+      if constexpr (V % 8 == 0) {
+#pragma unroll
+        for (int j8 = 0; j8 < V / 8; ++j8) {
+          const uint4 w = reinterpret_cast<const uint4 *>(src)[j8];
+          p[4 * j8 + 0] = w.x;
+          p[4 * j8 + 1] = w.y;
+          p[4 * j8 + 2] = w.z;
+          p[4 * j8 + 3] = w.w;
+        }
+      } else {
+#pragma unroll
+        for (int j4 = 0; j4 < V / 4; ++j4) {
+          const uint2 w = reinterpret_cast<const uint2 *>(src)[j4];
+          p[2 * j4 + 0] = w.x;
+          p[2 * j4 + 1] = w.y;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < V / 2; ++j) {
+        v[2 * j] = u2f(p[j] << 16);
+        v[2 * j + 1] = u2f(p[j] & 0xFFFF0000u);
+      }
+    } else {
+      const float4 *src = reinterpret_cast<const float4 *>(static_cast<const float *>(ea.logits) + m * E + q * V);
+#pragma unroll
+      for (int j4 = 0; j4 < V / 4; ++j4) {
+        const float4 w = src[j4];
+        v[4 * j4 + 0] = w.x;
+        v[4 * j4 + 1] = w.y;
+        v[4 * j4 + 2] = w.z;
+        v[4 * j4 + 3] = w.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = 0.0f;
+  }
+  route_select_row16<E>(v, scr[slot], m, live, ea);
+}
+
+template <class C, int MAXL>
+static hipError_t launch_logits_cm(const RouteLaunch &L) {
+  const int64_t ntt = (L.M + C::TT - 1) / C::TT;
+  const int64_t nblk = (ntt + 7) / 8 * 8 * C::NET;
+  hipLaunchKernelGGL((route_split_logits_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0,
+                     L.stream, L.xf, L.W, L.M, static_cast<int>(L.K), L.logits, L.logit_bf16);
+  return hipGetLastError();
+}
+
+template <class C>
+static hipError_t launch_logits_c(const RouteLaunch &L) {
+  const int64_t nb = (L.K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  // stack depth = bit length of the number of groups
+  if (G <= 1) return launch_logits_cm<C, 1>(L);
+  if (G <= 2) return launch_logits_cm<C, 2>(L);
+  if (G <= 4) return launch_logits_cm<C, 3>(L);
+  if (G <= 8) return launch_logits_cm<C, 4>(L);
+  return launch_logits_cm<C, 5>(L);
+}
+
+template <int E>
+static hipError_t launch_select_e(const RouteLaunch &L) {
+  EpilogueArgs ea{L.k, L.logit_bf16, L.flags, L.ids, L.weights, L.logits, L.margins};
+  hipLaunchKernelGGL((route_split_epilogue_kernel<E>), dim3(static_cast<uint32_t>((L.M + 15) / 16)), dim3(256), 0,
+                     L.stream, L.M, ea);
+  return hipGetLastError();
+}
+
+bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
+  return (E == 256 || E == 512) && K >= 1 && K <= 16384 && (K % 4) == 0 && x_f32 && has_logits;
+}
+
+bool select_supports(int64_t E) { return E == 64 || E == 128 || E == 256 || E == 512; }
+
+hipError_t launch_route_logits(const RouteLaunch &L) {
+  switch (L.E) {
+    case 256: return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4>>(L);
+    case 512: return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4>>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Reads L.logits as stored (L.logit_bf16 says which dtype).
+hipError_t launch_route_select(const RouteLaunch &L) {
+  switch (L.E) {
+    case 64: return launch_select_e<64>(L);
+    case 128: return launch_select_e<128>(L);
+    case 256: return launch_select_e<256>(L);
+    case 512: return launch_select_e<512>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_route_split(const RouteLaunch &L) {
+  const hipError_t e = launch_route_logits(L);
+  if (e != hipSuccess) return e;
+  return launch_route_select(L);
+}
+
+}  // namespace drk

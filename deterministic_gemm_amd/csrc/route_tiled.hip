@@ -16,9 +16,10 @@
 // kernel is "a perf seam, not a numeric one").
 //
 // Steps of a chain past the end of K, and slots past the last K-block, are
-// fed x = -0.0 and W = +0.0: fma(-0, +0, c) == c exactly for every c, so the
-// padding changes no bit; an absent slot starts at -0.0, the identity of the
-// tree's additions.
+// fed one zero operand of each sign (x = -0.0 and W = +0.0 in the
+// register-staged kernel, the reverse in the pipelined one): the product is
+// -0.0 and fma(-0, +0, c) == fma(+0, -0, c) == c for every c, so the padding changes
+// no bit; an absent slot starts at -0.0, the identity of the tree's additions.
 //
 // Work decomposition (E=256): a workgroup of 8 wavefronts takes 32 tokens
 // and all E experts; wavefront w owns experts 32w..32w+31 as 2x2 tiles of
@@ -28,6 +29,7 @@
 #include <type_traits>
 
 #include "route_common.h"
+#include "lds_dma.h"
 #include "launch.h"
 
 namespace drk {
@@ -220,12 +222,6 @@ __global__ __launch_bounds__(C::NT) void route_tiled_kernel(const float *__restr
 // XOR-swizzled by token so that 16 lanes reading one piece of 16 tokens hit
 // distinct banks.
 
-struct Pad16 {
-  float v[4];
-};
-__device__ const Pad16 g_pad_pos = {{0.0f, 0.0f, 0.0f, 0.0f}};
-__device__ const Pad16 g_pad_neg = {{-0.0f, -0.0f, -0.0f, -0.0f}};
-
 template <int E_, int AT_, int BT_, int KC_, int S_>
 struct DmaCfg {
   static constexpr int E = E_, AT = AT_, BT = BT_, KC = KC_, S = S_;
@@ -252,35 +248,6 @@ struct DmaCfg {
   static_assert(KC % 4 == 0 && 256 % KC == 0 && S >= 2, "chunking");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
 };
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N <= 63, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// One global -> LDS transfer: every active lane moves the 16 bytes at `src`
-// to LDS address lds_base + 16 * lane.  Written as inline assembly so that
-// the compiler's wait-count pass does not treat it as an LDS write to be
-// drained before every LDS read; the kernel orders these transfers itself
-// (wait_vmcnt + barrier).  m0 is used only here.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
-}
-
-// The same transfer addressed as a 64-bit SGPR base plus a 32-bit per-lane
-// byte offset: half the per-lane address operand, which measurably reduces the
-// time each transfer takes from the matrix cores' issue.
-__device__ __forceinline__ void dma16_s(const float *base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_base) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const float *p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
 
 // Issue the transfers of chunk ci into `stage` (chunks past the end load
 // padding, keeping every wavefront's transfer count per chunk fixed).  A

@@ -57,7 +57,10 @@ typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
 typedef enum dr_variant {
   DR_VARIANT_AUTO = 0,
   DR_VARIANT_ROWWISE = 1, /* few tokens per workgroup, vector FMA (small M) */
-  DR_VARIANT_TILED = 2    /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
+  DR_VARIANT_TILED = 2,   /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
+  DR_VARIANT_SPLIT = 3    /* (token, expert) tiles on matrix cores writing the logits, then a
+                             selection kernel reading them back; needs fp32 x, K % 4 == 0,
+                             E in {256, 512} and the logits output */
 } dr_variant;
 
 /* Divide the k selected weights by their sum (left to right in rank order). */
@@ -121,8 +124,32 @@ dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int6
                            float *weights, void *logits, dr_margin *margins, uint32_t flags,
                            dr_variant variant, void *stream);
 
-/* The family AUTO picks for (M, E): a pure function of the shape. */
-dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E);
+/* The family AUTO picks: a pure function of the call's shape (M, K, E), the
+ * x dtype and whether the logits output is requested. */
+dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits);
+
+/*
+ * dr_route_logits -- the first half of dr_route on its own: the canonical
+ * logits [M,E] (fp32, or rounded to bf16 RNE when logit_dtype is DR_BF16),
+ * bit-identical to dr_route's logits output.  Runs the (token, expert) tile
+ * kernel of the split family: fp32 x, K % 4 == 0 and E in {256, 512}, else
+ * DR_ERR_UNSUPPORTED.  logits is required.
+ */
+dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, int64_t E,
+                          dr_dtype logit_dtype, void *logits, void *stream);
+
+/*
+ * dr_route_select -- the second half: top-k with the lowest-index tie-break,
+ * softmax weights and margins from given logits, exactly as dr_route selects
+ * on its own logits ("vllm.cpp PR #2556", summary: the selection is a
+ * function of the logit values alone).  logits [M,E] fp32, or bf16 bits
+ * (DR_BF16, widened exactly); the values are used as given.  E in {64, 128,
+ * 256, 512}, 1 <= k <= min(E, 32); ids required, weights and margins may be
+ * NULL; flags as in dr_route.
+ */
+dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, int64_t E, int32_t k,
+                          int32_t *ids, float *weights, dr_margin *margins, uint32_t flags,
+                          void *stream);
 
 /*
  * dr_gate_dot -- shared-expert gate ("Batch changed the model's mind",

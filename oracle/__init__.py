@@ -50,6 +50,8 @@ def bind(path: str) -> ctypes.CDLL:
     L.dro_logits.restype = None
     L.dro_route.argtypes = [P, c_int, P, i64, i64, i64, i32, i64, c_int, u32, P, P, P, P, c_int]
     L.dro_route.restype = c_int
+    L.dro_select.argtypes = [P, i64, i64, i32, u32, P, P, P, c_int]
+    L.dro_select.restype = c_int
     L.dro_route_split_by_m.argtypes = [P, c_int, P, i64, i64, i64, i32, c_int, u32, P, P, P, P, c_int]
     L.dro_route_split_by_m.restype = c_int
     L.dro_gate_dot.argtypes = [P, c_int, P, c_int, i64, i64, i64, P, P, c_int]
@@ -143,6 +145,20 @@ def route(x, W, k: int, kblock: int = 256, logits_bf16: bool = False, renormaliz
     if rc != 0:
         raise ValueError("dro_route rejected its arguments")
     return ids, w, lg, mg
+
+
+def select(logits, k: int, renormalize: bool = False, nthreads: int = 0):
+    """dro_select on logits [M,E] (fp32 values, used as given).  Returns
+    (ids [M,k] int32, weights [M,k] f32, margins [M] MARGIN_DTYPE)."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    M, E = lg.shape
+    ids = np.empty((M, k), dtype=np.int32)
+    w = np.empty((M, k), dtype=np.float32)
+    mg = np.empty((M,), dtype=MARGIN_DTYPE)
+    rc = lib().dro_select(_ptr(lg), M, E, k, 1 if renormalize else 0, _ptr(ids), _ptr(w), _ptr(mg), nthreads)
+    if rc != 0:
+        raise ValueError("dro_select rejected its arguments")
+    return ids, w, mg
 
 
 def gate_dot(x, w, kblock: int = 256, nthreads: int = 0):

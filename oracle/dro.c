@@ -258,6 +258,7 @@ struct job {
   int split_mode;
   int32_t *ids;
   float *weights, *sel_logits, *logits_out;
+  const float *logits_in;
   dro_margin *margins;
   /* gate / gemm */
   const void *w;
@@ -373,6 +374,37 @@ static int route_common(const void *x, int x_is_bf16, const float *W, int64_t M,
   j.margins = margins;
   int64_t nb = (K + kblock - 1) / kblock;
   j.scratch_bytes = (size_t)(4 * E + nb + 1) * sizeof(float) + (size_t)E * sizeof(ent_t) + 64;
+  run_rows(&j, nthreads);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ select */
+
+static void select_row(job_t *j, int64_t m, void *scratch) {
+  int64_t E = j->E;
+  float *l = (float *)scratch; /* E */
+  float *u = l + E;            /* 2E */
+  ent_t *ent = (ent_t *)(u + 2 * E);
+  route_token(j->logits_in + m * E, E, j->k, 0, j->flags, l, ent, u, j->ids + m * j->k,
+              j->weights ? j->weights + m * j->k : NULL, NULL, j->margins ? j->margins + m : NULL);
+}
+
+int dro_select(const float *logits, int64_t M, int64_t E, int32_t k, uint32_t flags, int32_t *ids,
+               float *weights, dro_margin *margins, int nthreads) {
+  if (M < 0 || E < 1 || k < 1 || k > E) return 1;
+  if (M > 0 && (!logits || !ids)) return 1;
+  job_t j;
+  memset(&j, 0, sizeof(j));
+  j.fn = select_row;
+  j.M = M;
+  j.E = E;
+  j.k = k;
+  j.flags = flags;
+  j.logits_in = logits;
+  j.ids = ids;
+  j.weights = weights;
+  j.margins = margins;
+  j.scratch_bytes = (size_t)(3 * E + 1) * sizeof(float) + (size_t)E * sizeof(ent_t) + 64;
   run_rows(&j, nthreads);
   return 0;
 }

@@ -83,6 +83,13 @@ int dro_route(const void *x, int x_is_bf16, const float *W, int64_t M, int64_t K
               int32_t k, int64_t kblock, int logits_bf16, uint32_t flags, int32_t *ids,
               float *weights, float *sel_logits, dro_margin *margins, int nthreads);
 
+/* Selection alone: the top-k, softmax weights and margins dro_route derives
+ * from a row's logits, here from given logits [M,E] f32 used as they are
+ * (a bf16-logit caller passes the widened bf16 values).  Same outputs and
+ * return convention as dro_route. */
+int dro_select(const float *logits, int64_t M, int64_t E, int32_t k, uint32_t flags, int32_t *ids,
+               float *weights, dro_margin *margins, int nthreads);
+
 /* POSITIVE CONTROL ONLY (never a product path): like dro_route, but each
  * row's logit is a left-to-right sum of s(M) contiguous K-slices, each a
  * sequential fmaf chain from +0, with s = 1 for M <= 64, 2 for 65 <= M <= 74

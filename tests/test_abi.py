@@ -75,6 +75,29 @@ def test_route_rejects(L, kw, status):
 def test_route_variant_rejects(L):
     assert _route(L, variant=9) == INVALID
     assert _route(L, E=1024, k=8, variant=2) == UNSUPPORTED  # the tiled family stops at E=512
+    # the split family writes the logits and reads them back: it needs that
+    # output, fp32 x in whole 16-byte pieces and E in {256, 512}
+    assert _route(L, lg=0, variant=3) == UNSUPPORTED
+    assert _route(L, xd=1, variant=3) == UNSUPPORTED
+    assert _route(L, K=2046, variant=3) == UNSUPPORTED
+    assert _route(L, E=128, k=8, variant=3) == UNSUPPORTED
+    assert _route(L, M=0, variant=3) == OK
+
+
+def test_halves_reject(L):
+    P = ctypes.c_void_p
+    assert L.dr_route_logits(P(A), P(A), 4, 2048, 256, 0, None, None) == INVALID       # no output
+    assert L.dr_route_logits(P(A), P(A), 4, 2048, 256, 5, P(A), None) == INVALID       # bad dtype
+    assert L.dr_route_logits(P(A), P(A + 4), 4, 2048, 256, 0, P(A), None) == INVALID   # misaligned
+    assert L.dr_route_logits(P(A), P(A), 4, 2046, 256, 0, P(A), None) == UNSUPPORTED   # K % 4
+    assert L.dr_route_logits(P(A), P(A), 4, 2048, 128, 0, P(A), None) == UNSUPPORTED   # E
+    assert L.dr_route_logits(None, None, 0, 2048, 256, 0, None, None) == OK
+    assert L.dr_route_select(P(A), 0, 4, 256, 8, None, None, None, 0, None) == INVALID  # no ids
+    assert L.dr_route_select(P(A), 0, 4, 256, 0, P(A), None, None, 0, None) == INVALID  # k = 0
+    assert L.dr_route_select(P(A), 0, 4, 256, 8, P(A), None, None, 2, None) == INVALID  # flags
+    assert L.dr_route_select(P(A), 0, 4, 1024, 8, P(A), None, None, 0, None) == UNSUPPORTED
+    assert L.dr_route_select(P(A), 0, 4, 256, 33, P(A), None, None, 0, None) == UNSUPPORTED
+    assert L.dr_route_select(None, 0, 0, 256, 8, None, None, None, 0, None) == OK
 
 
 def test_empty_batch_returns_ok_without_launch(L):
@@ -103,6 +126,11 @@ def test_auto_variant_is_a_function_of_shape(L):
     switches = sum(1 for a, b in zip(picks, picks[1:]) if a != b)
     assert switches == 1
     assert dr.auto_variant(8192, 2048, 1024) == "rowwise"
+    # large batches that ask for the logits take the two-kernel family
+    assert dr.auto_variant(8192, 2048, 256) == "split"
+    assert dr.auto_variant(8192, 2048, 256, logits=False) == "tiled"
+    assert dr.auto_variant(8192, 2048, 256, x_dtype="bf16") == "tiled"
+    assert dr.auto_variant(8192, 2046, 256) == "tiled"
 
 
 def test_contract(L):

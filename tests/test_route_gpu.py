@@ -38,7 +38,7 @@ def mscan_ref(router_w):
     return oracle_route(fx, router_w, TOPK)
 
 
-@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled"])
+@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled", "split"])
 def test_mscan_fixed_rows_bit_identical(dr, router_w, mscan_ref, variant):
     """Every M in 19..80, the fixed request placed first and last, ascending
     then descending: the fixed rows equal the oracle's solo run bit for bit."""
@@ -91,7 +91,7 @@ def test_sweep_every_m_matches_oracle(dr, router_w, sweep):
         assert_route_equal(got, tuple(r[:M] for r in ref), what=f"M={M}")
 
 
-@pytest.mark.parametrize("variant", ["rowwise", "tiled"])
+@pytest.mark.parametrize("variant", ["rowwise", "tiled", "split"])
 def test_sweep_forced_variants(dr, router_w, sweep, variant):
     x, ref = sweep
     Wd = dev(router_w)
@@ -140,6 +140,21 @@ def test_ragged_k(dr, Kx):
         assert_route_equal(got, ref, what=f"K={Kx} {variant}")
 
 
+@pytest.mark.parametrize("Kx", [4, 100, 256, 260, 1000, 1024, 4096, 5000])
+def test_ragged_k_split(dr, Kx):
+    """K tails and partial groups of blocks in the two-kernel family (which
+    takes fp32 x in whole 16-byte pieces, so K % 4 == 0), against the oracle
+    and the fused kernel; M = 70 leaves a ragged token tile."""
+    rng = np.random.default_rng(Kx + 1)
+    W = (rng.standard_normal((Kx, 256)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((70, Kx)).astype(np.float32)
+    ref = oracle_route(x, W, 6)
+    for variant in ("split", "tiled"):
+        note(f"ragged K={Kx} {variant}")
+        got = gpu_route_np(dr, dev(x), dev(W), 6, variant=variant)
+        assert_route_equal(got, ref, what=f"K={Kx} {variant}")
+
+
 @pytest.mark.parametrize("Ex,kx", [(64, 1), (64, 32), (128, 5), (256, 32), (512, 10), (1024, 8), (1024, 32)])
 def test_every_supported_e(dr, Ex, kx):
     rng = np.random.default_rng(Ex + kx)
@@ -147,8 +162,10 @@ def test_every_supported_e(dr, Ex, kx):
     W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
     x = rng.standard_normal((77, Kx)).astype(np.float32)
     ref = oracle_route(x, W, kx)
-    for variant in ("auto", "rowwise", "tiled"):
+    for variant in ("auto", "rowwise", "tiled", "split"):
         if variant == "tiled" and Ex == 1024:
+            continue
+        if variant == "split" and Ex not in (256, 512):
             continue
         note(f"E={Ex} k={kx} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
@@ -162,16 +179,17 @@ def test_modes(dr, router_w, sweep, mode):
     kw = {"logit_dtype": "bf16"} if mode == "bf16_logits" else {"renormalize": True}
     ref = oracle_route(x[:M], router_w, TOPK, logits_bf16=(mode == "bf16_logits"),
                        renormalize=(mode == "renormalize"))
-    for variant in ("rowwise", "tiled"):
+    for variant in ("rowwise", "tiled", "split"):
         note(f"mode {mode} {variant}")
         got = gpu_route_np(dr, dev(x[:M]), dev(router_w), TOPK, variant=variant, **kw)
         assert_route_equal(got, ref, what=f"{mode} {variant}")
 
 
-def test_special_values(dr):
+@pytest.mark.parametrize("Ex", [64, 256])
+def test_special_values(dr, Ex):
     """Signed zeros, subnormal products, huge cancelling terms, NaN and inf."""
     rng = np.random.default_rng(99)
-    Kx, Ex, kx = 600, 64, 4
+    Kx, kx = 600, 4
     x = rng.standard_normal((96, Kx)).astype(np.float32)
     W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
     x[0] = 0.0
@@ -185,8 +203,8 @@ def test_special_values(dr):
     W[:, 9] = -0.0
     W[:, 10] = W[:, 11]                        # exact ties
     ref = oracle_route(x, W, kx)
-    for variant in ("rowwise", "tiled"):
-        note(f"special values {variant}")
+    for variant in ("rowwise", "tiled") + (("split",) if Ex == 256 else ()):
+        note(f"special values E={Ex} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
         assert_route_equal(got, ref, what=f"special {variant}")
 
@@ -208,7 +226,9 @@ def test_rows_at_any_offset(dr, router_w, sweep):
     for shift in (1, 7, 16, 31, 40):
         filler = rng.standard_normal((shift, K)).astype(np.float32)
         xb = np.concatenate([filler, block, filler[: shift // 2]], axis=0)
-        note(f"offset shift={shift} M={xb.shape[0]}")
-        got = gpu_route_np(dr, dev(xb), Wd, TOPK)
-        rows = slice(shift, shift + 50)
-        assert_route_equal(tuple(g[rows] for g in got), tuple(r[1000:1050] for r in ref), what=f"shift={shift}")
+        for variant in ("auto", "split"):
+            note(f"offset shift={shift} M={xb.shape[0]} {variant}")
+            got = gpu_route_np(dr, dev(xb), Wd, TOPK, variant=variant)
+            rows = slice(shift, shift + 50)
+            assert_route_equal(tuple(g[rows] for g in got), tuple(r[1000:1050] for r in ref),
+                               what=f"shift={shift} {variant}")
