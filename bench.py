@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 M, K, E, TOPK = 8192, 2048, 256, 8
 PEAK_FP32_MATRIX_TFLOPS = 157.3   # MI355X dense fp32 matrix (and vector) peak
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_MATRIX_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "route_split_logits_M8192_K2048_E256_traffic.json")
 KERNEL_SOURCES = ["route_split.hip", "route_common.h", "lds_dma.h"]
 
@@ -54,12 +55,109 @@ def traffic_bytes():
     return rec.get("hbm_bytes_per_launch")
 
 
+def _time(fn, stream, torch, steps: int, warmup: int = 3) -> float:
+    """Average ms per call of fn() over `steps` back-to-back calls (HIP events
+    on `stream`)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def measure_suite(dr, wl, torch, np, xd, Wd, stream):
+    """Secondary measurements on the other workloads (outside the headline's
+    timed region): routed tokens/s across the M sweep, the tie-heavy router
+    with bf16 logits, the 40-layer prefill stack end to end, and the dense
+    bf16 GEMM and gate dot against their rooflines."""
+    dev = xd.device
+    log = lambda m: print(f"[suite] {m}", file=sys.stderr, flush=True)  # noqa: E731
+    suite = {}
+
+    sweep = []
+    for m in (1, 16, 64, 65, 75, 256, 1024, 4096, 8192):
+        xm = xd[:m].contiguous()
+        ms = _time(lambda: dr.route(xm, Wd, TOPK), stream, torch, steps=20)
+        sweep.append({"M": m, "variant": dr.auto_variant(m, K, E), "us": round(ms * 1e3, 2),
+                      "tokens_per_s": round(m / (ms * 1e-3), 1),
+                      "tflops": round(2.0 * m * K * E / (ms * 1e-3) / 1e12, 2)})
+    suite["m_sweep_K2048_E256_k8"] = sweep
+    log("m sweep done")
+
+    calib = json.load(open(os.path.join(ROOT, "tests", "golden", "tie_calibration.json")))
+    Wt = torch.from_numpy(wl.tie_weights(calib["pairs"])).to(dev)
+    xt = torch.from_numpy(wl.tie_x(4096)).to(dev)
+    ties = []
+    for m in (240, 4096):
+        xm = xt[:m].contiguous()
+        ms = _time(lambda: dr.route(xm, Wt, 10, logit_dtype="bf16"), stream, torch, steps=20)
+        ties.append({"M": m, "variant": dr.auto_variant(m, 4096, 512), "us": round(ms * 1e3, 2),
+                     "tokens_per_s": round(m / (ms * 1e-3), 1),
+                     "tflops": round(2.0 * m * 4096 * 512 / (ms * 1e-3) / 1e12, 2)})
+    suite["ties_K4096_E512_k10_bf16_logits"] = ties
+    del Wt, xt
+    log("tie-heavy router done")
+
+    import concurrent.futures
+
+    lengths = wl.stack_lengths()
+    layers = []
+    nthr = min(16, len(os.sched_getaffinity(0)))
+    with concurrent.futures.ThreadPoolExecutor(nthr) as ex:  # the generators release the GIL
+        for layer, xl in enumerate(ex.map(lambda l: wl.stack_layer_x(l, lengths, K), range(wl.STACK_LAYERS))):
+            layers.append((torch.from_numpy(wl.stack_layer_weights(layer, K, E)).to(dev),
+                           torch.from_numpy(xl).to(dev)))
+    Ms = layers[0][1].shape[0]
+    ids_out = torch.empty((Ms, TOPK), dtype=torch.int32, device=dev)
+
+    def stack():
+        for Wl, xl in layers:
+            dr.route(xl, Wl, TOPK, weights=False, logits=False, margins=False, out=(ids_out, None, None, None))
+    ms = _time(stack, stream, torch, steps=3, warmup=1)
+    suite["stack_40_layers_M16384_ids_only"] = {
+        "variant": dr.auto_variant(Ms, K, E, logits=False), "ms_end_to_end": round(ms, 3),
+        "tokens_per_s": round(Ms * wl.STACK_LAYERS / (ms * 1e-3), 1),
+        "note": "tokens x layers per second over 40 back-to-back dr_route calls, ids only"}
+    del layers, ids_out
+    log("40-layer stack done")
+
+    xb = torch.from_numpy(wl.dense_x_bits(4096).view(np.int16)).view(torch.bfloat16).to(dev)
+    Wb = torch.from_numpy(wl.dense_w_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+    gw = torch.from_numpy(wl.gate_w_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+    dense = []
+    for m in wl.DENSE_MS:
+        xm = xb[:m].contiguous()
+        o = torch.empty((m, wl.DENSE_N), dtype=torch.float32, device=dev)
+        ms = _time(lambda: dr.gemm_bf16(xm, Wb, out=o), stream, torch, steps=20)
+        fl = 2.0 * m * wl.DENSE_K * wl.DENSE_N
+        byt = (m * wl.DENSE_K + wl.DENSE_K * wl.DENSE_N) * 2 + m * wl.DENSE_N * 4
+        dense.append({"M": m, "us": round(ms * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+                      "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_MATRIX_TFLOPS, 4),
+                      "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)})
+    suite["dense_gemm_bf16_K4096_N4096"] = dense
+    ms = _time(lambda: dr.gate_dot(xb, gw), stream, torch, steps=20)
+    byt = 4096 * wl.DENSE_K * 2 + wl.DENSE_K * 2 + 4096 * 8
+    suite["gate_dot_bf16_M4096_K4096"] = {"us": round(ms * 1e3, 2), "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                                          "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    log("dense GEMM and gate done")
+    return suite
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-suite", action="store_true",
+                    help="skip the secondary measurements (M sweep, tie-heavy router, 40-layer stack, "
+                         "dense GEMM and gate)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 256 MiB device-to-device copy, the known-size reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
@@ -178,6 +276,10 @@ def main():
                             "flop_per_launch": flops},
         "m_invariance": inv,
     }
+
+    if not args.no_suite:
+        del out, lg_only
+        result["suite"] = measure_suite(dr, wl, torch, np, xd, Wd, stream)
 
     if not args.no_cpu_baseline:
         import oracle

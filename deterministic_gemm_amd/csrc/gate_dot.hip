@@ -4,10 +4,14 @@
 // under a shape-dependent library GEMM; here it is the router's canonical
 // order with E = 1, so it cannot move with M.
 //
-// One wavefront per row: lane b runs the fmaf chain of K-block b (nb <= 64
-// lanes), lanes past the last block hold -0.0, and the 64 partials are
-// combined by a xor butterfly -- level d adds lanes that differ in bit d, which
-// is the pairwise tree over the -0-padded leaves.
+// Lanes per row = the next power of two >= nb (<= 64), so a wavefront takes
+// 64 / that many rows: lane b of a row group runs the fmaf chain of K-block b
+// (lanes past the last block hold -0.0), and the group's partials combine by a
+// xor butterfly over its lanes -- level d adds lanes that differ in bit d,
+// which is the pairwise tree over the -0-padded leaves.  Each lane streams its
+// block with 16-byte loads (eight bf16 or four fp32 values per load) when rows
+// are 16-byte aligned, and element by element otherwise; the path is bound by
+// HBM (M*K elements of x read once).
 #include "route_common.h"
 #include "launch.h"
 
@@ -15,31 +19,72 @@ namespace drk {
 
 constexpr int GD_WAVES = 4;
 
-template <bool XB, bool WB>
+template <bool B>
+__device__ __forceinline__ float load_elem(const void *p, int64_t i) {
+  if constexpr (B) return bf16_to_f32(static_cast<const uint16_t *>(p)[i]);
+  else return static_cast<const float *>(p)[i];
+}
+
+// Widen one 16-byte piece: 8 bf16 or 4 fp32 values.
+template <bool B>
+__device__ __forceinline__ void unpack16(const uint4 &u, float (&v)[B ? 8 : 4]) {
+  if constexpr (B) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[2 * j] = u2f(w[j] << 16);
+      v[2 * j + 1] = u2f(w[j] & 0xFFFF0000u);
+    }
+  } else {
+    v[0] = u2f(u.x);
+    v[1] = u2f(u.y);
+    v[2] = u2f(u.z);
+    v[3] = u2f(u.w);
+  }
+}
+
+template <bool XB, bool WB, int LPR>
 __global__ __launch_bounds__(GD_WAVES * 64) void gate_dot_kernel(const void *__restrict__ x,
                                                                   const void *__restrict__ w,
                                                                   float *__restrict__ dot,
                                                                   float *__restrict__ gate, int64_t M,
-                                                                  int K) {
+                                                                  int K, int vec) {
+  constexpr int RPW = 64 / LPR;
   const int lane = threadIdx.x & 63;
-  const int64_t m = static_cast<int64_t>(blockIdx.x) * GD_WAVES + (threadIdx.x >> 6);
-  if (m >= M) return;
+  const int b = lane % LPR;
+  const int64_t m = (static_cast<int64_t>(blockIdx.x) * GD_WAVES + (threadIdx.x >> 6)) * RPW + lane / LPR;
   const int nb = (K + 255) / 256;
   float p = -0.0f;
-  if (lane < nb) {
+  if (m < M && b < nb) {
     p = 0.0f;
-    const int k0 = lane * 256;
+    const int k0 = b * 256;
     const int k1 = (K - k0 < 256) ? K : k0 + 256;
-    for (int kk = k0; kk < k1; ++kk) {
-      const int64_t off = m * K + kk;
-      const float xv = XB ? bf16_to_f32(static_cast<const uint16_t *>(x)[off]) : static_cast<const float *>(x)[off];
-      const float wv = WB ? bf16_to_f32(static_cast<const uint16_t *>(w)[kk]) : static_cast<const float *>(w)[kk];
-      p = __builtin_fmaf(xv, wv, p);
+    int kk = k0;
+    if constexpr (XB == WB) {
+      // both operands in 16-byte pieces of the same element count
+      constexpr int PE = XB ? 8 : 4;
+      if (vec) {
+        const uint4 *xs =
+            reinterpret_cast<const uint4 *>(static_cast<const char *>(x) + (m * K + k0) * (XB ? 2 : 4));
+        const uint4 *ws =
+            reinterpret_cast<const uint4 *>(static_cast<const char *>(w) + static_cast<int64_t>(k0) * (WB ? 2 : 4));
+        const int np = (k1 - k0) / PE;
+#pragma unroll 4
+        for (int i = 0; i < np; ++i) {
+          float xv[PE], wv[PE];
+          unpack16<XB>(xs[i], xv);
+          unpack16<WB>(ws[i], wv);
+#pragma unroll
+          for (int j = 0; j < PE; ++j) p = __builtin_fmaf(xv[j], wv[j], p);
+        }
+        kk = k0 + np * PE;
+      }
     }
+    for (; kk < k1; ++kk) p = __builtin_fmaf(load_elem<XB>(x, m * K + kk), load_elem<WB>(w, kk), p);
   }
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) p = p + __shfl_xor(p, d, 64);
-  if (lane == 0) {
+  for (int d = 1; d < LPR; d <<= 1) p = p + __shfl_xor(p, d, 64);
+  if (m < M && b == 0) {
     if (dot) dot[m] = p;
     if (gate) {
       const float e = route_exp(-__builtin_fabsf(p));
@@ -48,18 +93,37 @@ __global__ __launch_bounds__(GD_WAVES * 64) void gate_dot_kernel(const void *__r
   }
 }
 
+template <bool XB, bool WB, int LPR>
+static void launch_gd(const void *x, const void *w, float *dot, float *gate, int64_t M, int K, int vec,
+                      hipStream_t stream) {
+  constexpr int RPW = 64 / LPR;
+  const int64_t rows_per_block = static_cast<int64_t>(GD_WAVES) * RPW;
+  const dim3 grid(static_cast<uint32_t>((M + rows_per_block - 1) / rows_per_block)), block(GD_WAVES * 64);
+  hipLaunchKernelGGL((gate_dot_kernel<XB, WB, LPR>), grid, block, 0, stream, x, w, dot, gate, M, K, vec);
+}
+
+template <bool XB, bool WB>
+static void launch_gd_lpr(const void *x, const void *w, float *dot, float *gate, int64_t M, int K, int vec,
+                          hipStream_t stream) {
+  const int nb = (K + 255) / 256;
+  if (nb <= 1) launch_gd<XB, WB, 1>(x, w, dot, gate, M, K, vec, stream);
+  else if (nb <= 2) launch_gd<XB, WB, 2>(x, w, dot, gate, M, K, vec, stream);
+  else if (nb <= 4) launch_gd<XB, WB, 4>(x, w, dot, gate, M, K, vec, stream);
+  else if (nb <= 8) launch_gd<XB, WB, 8>(x, w, dot, gate, M, K, vec, stream);
+  else if (nb <= 16) launch_gd<XB, WB, 16>(x, w, dot, gate, M, K, vec, stream);
+  else if (nb <= 32) launch_gd<XB, WB, 32>(x, w, dot, gate, M, K, vec, stream);
+  else launch_gd<XB, WB, 64>(x, w, dot, gate, M, K, vec, stream);
+}
+
 hipError_t launch_gate_dot(const void *x, int x_bf16, const void *w, int w_bf16, float *dot,
                            float *gate, int64_t M, int64_t K, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>((M + GD_WAVES - 1) / GD_WAVES)), block(GD_WAVES * 64);
   const int k = static_cast<int>(K);
-  if (x_bf16 && w_bf16)
-    hipLaunchKernelGGL((gate_dot_kernel<true, true>), grid, block, 0, stream, x, w, dot, gate, M, k);
-  else if (x_bf16)
-    hipLaunchKernelGGL((gate_dot_kernel<true, false>), grid, block, 0, stream, x, w, dot, gate, M, k);
-  else if (w_bf16)
-    hipLaunchKernelGGL((gate_dot_kernel<false, true>), grid, block, 0, stream, x, w, dot, gate, M, k);
-  else
-    hipLaunchKernelGGL((gate_dot_kernel<false, false>), grid, block, 0, stream, x, w, dot, gate, M, k);
+  // 16-byte pieces need every row (and w) to start 16-byte aligned
+  const int vec = ((K * (x_bf16 ? 2 : 4)) % 16 == 0) ? 1 : 0;
+  if (x_bf16 && w_bf16) launch_gd_lpr<true, true>(x, w, dot, gate, M, k, vec, stream);
+  else if (x_bf16) launch_gd_lpr<true, false>(x, w, dot, gate, M, k, vec, stream);
+  else if (w_bf16) launch_gd_lpr<false, true>(x, w, dot, gate, M, k, vec, stream);
+  else launch_gd_lpr<false, false>(x, w, dot, gate, M, k, vec, stream);
   return hipGetLastError();
 }
 

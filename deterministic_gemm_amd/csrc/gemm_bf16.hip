@@ -7,110 +7,191 @@
 // same instruction sequence: one v_mfma_f32_16x16x32_bf16 per 32-wide K step,
 // k ascending, into one accumulator that starts at zero, with no split of K.
 // The tile over M and N only decides which lanes run that sequence, so a row
-// gets the same bits at every M and at every position in a tile.  The
-// matrix core's internal order of the 32 products of one step is the
-// hardware's; results are therefore compared with the exact product within a
-// tolerance, and with themselves across M bit for bit.
+// gets the same bits at every M, at every position in a tile and under every
+// tile configuration.  The matrix core's internal order of the 32 products of
+// one step is the hardware's; results are therefore compared with the exact
+// product within a tolerance, and with themselves across M bit for bit.
 //
-// Workgroup tile 128x128, four wavefronts of 64x64 (4x4 MFMA tiles), K staged
-// through LDS 32 at a time: x as [row][k], W transposed to [n][k] so that each
-// lane reads eight consecutive k of its column.
+// Data movement: x and W tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, 16 bytes per lane) through a ring of S stages of
+// BK steps of K, in their natural layouts -- x as [row][k], W as [k][n].  The
+// x operand of a 16x16x32 step is eight consecutive k of one row (one 16-byte
+// LDS read); the W operand is eight consecutive k of one column, which the
+// [k][n] layout stores 2N bytes apart, so it is read with the LDS transpose
+// read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
+// element i % 4 of the 8 bytes read by lane i / 4 + 4j, for j = 0..3.  With
+// lane i/4 + 4j reading row k0 + j at columns c0 + 4(i/4) .. +3, lane i gets
+// column c0 + i at rows k0 .. k0+3; two such reads give the eight k.  The
+// 16-byte units of each LDS row are XOR-swizzled by row so that the reads of
+// one instruction spread over the LDS banks; writer and readers apply the same
+// swizzle.
+#include "lds_dma.h"
 #include "launch.h"
 
 namespace drk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int GB_M = 128, GB_N = 128, GB_K = 32, GB_T = 256;
-constexpr int GB_P = GB_K + 8;  // LDS row pitch in bf16 elements
+static __device__ const Pad16 g_zero16 = {{0.0f, 0.0f, 0.0f, 0.0f}};
 
-__global__ __launch_bounds__(GB_T) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // rows, columns per wavefront
+  static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 tiles per wavefront
+  static constexpr int UA = BK / 8;                 // 16-byte units per x row of a stage
+  static constexpr int UB = BN / 8;                 // 16-byte units per W row of a stage
+  static constexpr int AU = BM * UA, BU = BK * UB;  // units per stage
+  static constexpr int ABYTES = AU * 16, STAGE = (AU + BU) * 16;
+  static constexpr int PER = (AU + BU) / 64 / NW;   // transfers per wavefront per stage
+  static_assert(FM >= 1 && FN >= 1 && TM * WM == BM && TN * WN == BN, "wavefront tiles");
+  static_assert(BK % 32 == 0 && (UA == 4 || UA == 8), "K steps per stage");
+  static_assert(UB == 4 || UB == 8 || UB == 16, "W row units");
+  static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
+  static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
+  // x rows: unit u of row r sits at u ^ swa(r); 16 consecutive rows reading
+  // the same unit then hit 16 distinct 16-byte bank groups.
+  __host__ __device__ static constexpr int swa(int r) { return (r / (16 / UA)) % UA; }
+  // W rows: the 16 rows one transpose read touches (k = 8g + j + c, g, j in
+  // 0..3) get distinct offsets within their bank-group classes.
+  __host__ __device__ static constexpr int swb(int k) {
+    return UB == 16 ? (k % 4) + 4 * ((k / 8) % 4) : UB == 8 ? ((k % 4) >> 1) + 2 * ((k / 8) % 4) : (k / 8) % 4;
+  }
+};
+
+template <class C>
+__device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
+                                           int64_t M, int K, int N, int64_t m0, int n0, int st, int nst,
+                                           int wave, int lane, char *stage) {
+  const int k0 = st * C::BK;
+  const bool live = st < nst;
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int p = (wave * C::PER + i) * 64 + lane;  // unit within the stage
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (wave * C::PER + i) * 1024)));
+    const void *src = &g_zero16;
+    if (p < C::AU) {
+      const int r = p / C::UA, up = p % C::UA;
+      const int u = up ^ C::swa(r);
+      const int64_t m = m0 + r;
+      const int k = k0 + 8 * u;
+      if (live && m < M && k < K) src = x + m * K + k;
+    } else {
+      const int q = p - C::AU;
+      const int kr = q / C::UB, up = q % C::UB;
+      const int u = up ^ C::swb(kr);
+      const int k = k0 + kr;
+      if (live && k < K) src = W + static_cast<int64_t>(k) * N + n0 + 8 * u;
+    }
+    dma16(src, lds);
+  }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ W,
                                                          float *__restrict__ out, int64_t M, int K,
                                                          int N) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[GB_M * GB_P];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[GB_N * GB_P];
-
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * GB_M;
-  const int n0 = blockIdx.x * GB_N;
+  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
+  constexpr int FM = C::FM, FN = C::FN, S = C::S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * C::BM;
+  const int n0 = blockIdx.x * C::BN;
+  const int nst = (K + C::BK - 1) / C::BK;
 
-  uint4 areg[2], breg[2];
-  auto load = [&](int k0) {
+  f32x4 acc[FM][FN];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = t + GB_T * i;
-      const int row = c >> 2, kc = (c & 3) * 8;
-      const int64_t m = m0 + row;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m < M) v = *reinterpret_cast<const uint4 *>(x + m * K + k0 + kc);
-      areg[i] = v;
-      const int kr = c >> 4, nc = (c & 15) * 8;
-      breg[i] = *reinterpret_cast<const uint4 *>(W + static_cast<int64_t>(k0 + kr) * N + n0 + nc);
-    }
-  };
-  auto store = [&]() {
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = t + GB_T * i;
-      const int row = c >> 2, kc = (c & 3) * 8;
-      *reinterpret_cast<uint4 *>(&As[row * GB_P + kc]) = areg[i];
-      const int kr = c >> 4, nc = (c & 15) * 8;
-      const uint32_t w4[4] = {breg[i].x, breg[i].y, breg[i].z, breg[i].w};
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // per-lane parts of the operand addresses
+  const int ta = lane & 15;          // transpose read: source lane within its group
+  const int tj = ta >> 2, tq = ta & 3;
+
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        Bs[(nc + 2 * j) * GB_P + kr] = static_cast<uint16_t>(w4[j] & 0xFFFFu);
-        Bs[(nc + 2 * j + 1) * GB_P + kr] = static_cast<uint16_t>(w4[j] >> 16);
+  for (int i = 0; i < S - 1; ++i) gemm_issue<C>(x, W, M, K, N, m0, n0, i, nst, wave, lane, smem + i * C::STAGE);
+
+  for (int st = 0; st < nst; ++st) {
+    compiler_fence();
+    wait_vmcnt<C::PER * (S - 2)>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    gemm_issue<C>(x, W, M, K, N, m0, n0, st + S - 1, nst, wave, lane, smem + ((st + S - 1) % S) * C::STAGE);
+    const char *As = smem + (st % S) * C::STAGE;
+    const char *Bs = As + C::ABYTES;
+    const int nsub = (K - st * C::BK) < C::BK ? (K - st * C::BK) / 32 : C::BK / 32;
+#pragma unroll
+    for (int kk = 0; kk < C::BK / 32; ++kk) {
+      if (kk < nsub) {
+        bf16x8 af[FM], bfv[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * C::TM + i * 16 + r16;
+          const int u = (kk * 4 + g4) ^ C::swa(r);
+          af[i] = *reinterpret_cast<const bf16x8 *>(As + (r * C::UA + u) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int col = wn * C::TN + j * 16 + 4 * tq;  // first of the 4 columns this lane reads
+          i16x4 h[2];
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int kr = kk * 32 + 8 * g4 + 4 * c + tj;
+            const int u = (col / 8) ^ C::swb(kr);
+            const char *a = Bs + (kr * C::UB + u) * 16 + (col % 8) * 2;
+            h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
+          }
+          const i16x4 lo = h[0], hi = h[1];
+          bfv[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
       }
     }
-  };
-
-  f32x4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += GB_K) {
-    __syncthreads();
-    store();
-    __syncthreads();
-    if (k0 + GB_K < K) load(k0 + GB_K);
-    bf16x8 af[4], bf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      af[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * 64 + i * 16 + r16) * GB_P + g4 * 8]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      bf[j] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * 64 + j * 16 + r16) * GB_P + g4 * 8]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
   }
+  // no transfer may still be writing this workgroup's LDS when it exits
+  compiler_fence();
+  wait_vmcnt<0>();
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int64_t m = m0 + wm * 64 + i * 16 + g4 * 4 + q;
+      const int64_t m = m0 + wm * C::TM + i * 16 + g4 * 4 + q;
       if (m >= M) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) out[m * N + n0 + wn * 64 + j * 16 + r16] = acc[i][j][q];
+      for (int j = 0; j < FN; ++j) out[m * N + n0 + wn * C::TN + j * 16 + r16] = acc[i][j][q];
     }
 }
 
-hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
-                            int64_t K, int64_t N, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(N / GB_N), static_cast<uint32_t>((M + GB_M - 1) / GB_M));
-  hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(GB_T), 0, stream, x, W, out, M, static_cast<int>(K),
+template <class C>
+static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K,
+                                int64_t N, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(N / C::BN), static_cast<uint32_t>((M + C::BM - 1) / C::BM));
+  hipLaunchKernelGGL((gemm_bf16_kernel<C>), grid, dim3(C::NT), 0, stream, x, W, out, M, static_cast<int>(K),
                      static_cast<int>(N));
   return hipGetLastError();
+}
+
+// The tile is chosen from M (a performance choice only: every configuration
+// runs the same per-output instruction sequence).  Small batches take narrow
+// column tiles so that more workgroups stream W from HBM at once.
+hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
+                            int64_t K, int64_t N, hipStream_t stream) {
+  if (M <= 32) return launch_gemm_c<GemmCfg<32, 32, 2, 1, 64, 4>>(x, W, out, M, K, N, stream);
+  if (M <= 128) return launch_gemm_c<GemmCfg<64, 64, 2, 2, 64, 4>>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<128, 128, 2, 2, 64, 3>>(x, W, out, M, K, N, stream);
 }
 
 }  // namespace drk
