@@ -48,17 +48,20 @@ struct GemmCfg {
   static constexpr int ABYTES = AU * 16, STAGE = (AU + BU) * 16;
   static constexpr int PER = (AU + BU) / 64 / NW;   // transfers per wavefront per stage
   static_assert(FM >= 1 && FN >= 1 && TM * WM == BM && TN * WN == BN, "wavefront tiles");
-  static_assert(BK % 32 == 0 && (UA == 4 || UA == 8), "K steps per stage");
-  static_assert(UB == 4 || UB == 8 || UB == 16, "W row units");
+  static_assert(BK % 32 == 0 && (UA == 4 || UA == 8 || UA == 16 || UA == 32), "K steps per stage");
+  static_assert(UB == 2 || UB == 4 || UB == 8 || UB == 16 || UB == 32, "W row units");
   static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
   static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
   // x rows: unit u of row r sits at u ^ swa(r); 16 consecutive rows reading
   // the same unit then hit 16 distinct 16-byte bank groups.
-  __host__ __device__ static constexpr int swa(int r) { return (r / (16 / UA)) % UA; }
+  __host__ __device__ static constexpr int swa(int r) { return UA >= 16 ? r % 16 : (r / (16 / UA)) % UA; }
   // W rows: the 16 rows one transpose read touches (k = 8g + j + c, g, j in
   // 0..3) get distinct offsets within their bank-group classes.
   __host__ __device__ static constexpr int swb(int k) {
-    return UB == 16 ? (k % 4) + 4 * ((k / 8) % 4) : UB == 8 ? ((k % 4) >> 1) + 2 * ((k / 8) % 4) : (k / 8) % 4;
+    return UB >= 16 ? (k % 4) + 4 * ((k / 8) % 4)
+           : UB == 8 ? ((k % 4) >> 1) + 2 * ((k / 8) % 4)
+           : UB == 4 ? (k / 8) % 4
+                     : (k / 8) % 2;
   }
 };
 
@@ -185,13 +188,15 @@ static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, float *out
 }
 
 // The tile is chosen from M (a performance choice only: every configuration
-// runs the same per-output instruction sequence).  Small batches take narrow
-// column tiles so that more workgroups stream W from HBM at once.
+// runs the same per-output instruction sequence).  Measured at K = N = 4096:
+// narrow tiles with deep K stages for small batches (more workgroups stream
+// W at once), 128x128 with eight wavefronts up to M = 1024, and 256x256 with
+// eight 128x64 wavefront tiles beyond.
 hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
                             int64_t K, int64_t N, hipStream_t stream) {
-  if (M <= 32) return launch_gemm_c<GemmCfg<32, 32, 2, 1, 64, 4>>(x, W, out, M, K, N, stream);
-  if (M <= 128) return launch_gemm_c<GemmCfg<64, 64, 2, 2, 64, 4>>(x, W, out, M, K, N, stream);
-  return launch_gemm_c<GemmCfg<128, 128, 2, 2, 64, 3>>(x, W, out, M, K, N, stream);
+  if (M <= 128) return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>>(x, W, out, M, K, N, stream);
+  if (M <= 1024 || N % 256 != 0) return launch_gemm_c<GemmCfg<128, 128, 4, 2, 64, 3>>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 32, 3>>(x, W, out, M, K, N, stream);
 }
 
 }  // namespace drk

@@ -57,7 +57,9 @@ def test_gemm_row_offsets(dense):
 def test_gemm_small_shapes_close_to_exact():
     dr = require_gpu()
     rng = np.random.default_rng(3)
-    for (M, K, N) in ((1, 32, 128), (3, 64, 256), (130, 96, 128)):
+    # every tile configuration, partial K stages, ragged M tiles
+    for (M, K, N) in ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
+                      (1500, 160, 256)):
         xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
         Wb = wl.to_bf16_bits(rng.standard_normal((K, N)).astype(np.float32))
         note(f"gemm small {M}x{K}x{N}")
