@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdr.so")
 
 DR_OK, DR_ERR_INVALID, DR_ERR_UNSUPPORTED, DR_ERR_DEVICE = 0, 1, 2, 3
 DR_F32, DR_BF16 = 0, 1
-VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3}
+VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3, "narrow": 4}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 DR_ROUTE_RENORMALIZE = 1
 

@@ -16,8 +16,8 @@ LIB = os.path.join(HERE, "libdr.so")
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["dr_api.cpp", "route_rowwise.hip", "route_tiled.hip", "route_split.hip", "gate_dot.hip",
-           "gemm_bf16.hip"]
+SOURCES = ["dr_api.cpp", "route_rowwise.hip", "route_tiled.hip", "route_split.hip", "route_narrow.hip",
+           "gate_dot.hip", "gemm_bf16.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -38,9 +38,12 @@ constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
 // inside the 19..80 token m-scan on purpose, so that scan crosses a dispatch
 // change and shows it cannot move a bit.
 constexpr int64_t kTiledMinM = 48;
-// Batches at or above this size that ask for the logits run as two kernels
-// (a squarer logits tile, then the selection); below it the fused kernel.
-constexpr int64_t kSplitMinM = 2048;
+// Calls that ask for the logits run as two kernels, the logits then the
+// selection.  Up to kNarrowMaxM tokens the logits spread over small (token,
+// expert) tiles with the K groups split between wavefronts; above it they use
+// 64 x 128 tiles (measured crossover at K=2048, E=256: between M=2048 and
+// M=3072).  Without the logits output the fused kernels run.
+constexpr int64_t kNarrowMaxM = 2560;
 
 dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
                      int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
@@ -55,7 +58,7 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
   if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
   if (variant != DR_VARIANT_AUTO && variant != DR_VARIANT_ROWWISE && variant != DR_VARIANT_TILED &&
-      variant != DR_VARIANT_SPLIT)
+      variant != DR_VARIANT_SPLIT && variant != DR_VARIANT_NARROW)
     return fail(DR_ERR_INVALID, "bad variant");
   if (M > 0 && (!x || !W || !ids)) return fail(DR_ERR_INVALID, "x, W and ids are required");
   if (!aligned16(x) || !aligned16(W) || !aligned16(ids) || !aligned16(weights) || !aligned16(logits) ||
@@ -71,6 +74,9 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   if (variant == DR_VARIANT_SPLIT && !drk::split_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
                 "split variant needs fp32 x, K %% 4 == 0, E in {256, 512} and the logits output");
+  if (variant == DR_VARIANT_NARROW && !drk::narrow_supports(E, K, x_dtype == DR_F32, logits != nullptr))
+    return fail(DR_ERR_UNSUPPORTED,
+                "narrow variant needs fp32 x, K %% 4 == 0, E <= 512 and the logits output");
   if (M == 0) return DR_OK;
 
   drk::RouteLaunch L;
@@ -88,9 +94,10 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   L.logits = logits;
   L.margins = margins;
   L.stream = static_cast<hipStream_t>(stream);
-  const hipError_t e = variant == DR_VARIANT_SPLIT   ? drk::launch_route_split(L)
-                       : variant == DR_VARIANT_TILED ? drk::launch_route_tiled(L)
-                                                     : drk::launch_route_rowwise(L);
+  const hipError_t e = variant == DR_VARIANT_SPLIT    ? drk::launch_route_split(L)
+                       : variant == DR_VARIANT_NARROW ? drk::launch_route_narrow(L)
+                       : variant == DR_VARIANT_TILED  ? drk::launch_route_tiled(L)
+                                                      : drk::launch_route_rowwise(L);
   return device_status(e, "route launch");
 }
 
@@ -99,7 +106,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
 extern "C" {
 
 dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits) {
-  if (M >= kSplitMinM && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
+  if (M > kNarrowMaxM && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
+  if (M <= kNarrowMaxM && drk::narrow_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_NARROW;
   if (M >= kTiledMinM && drk::tiled_supports(E, K)) return DR_VARIANT_TILED;
   return DR_VARIANT_ROWWISE;
 }
@@ -129,8 +137,8 @@ dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, 
   if (M > 0 && (!x || !W || !logits)) return fail(DR_ERR_INVALID, "x, W and logits are required");
   if (!aligned16(x) || !aligned16(W) || !aligned16(logits))
     return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
-  if (!drk::split_supports(E, K, true, true))
-    return fail(DR_ERR_UNSUPPORTED, "dr_route_logits needs K %% 4 == 0, K <= %lld and E in {256, 512}",
+  if (!drk::narrow_supports(E, K, true, true))
+    return fail(DR_ERR_UNSUPPORTED, "dr_route_logits needs K %% 4 == 0, K <= %lld and E in {64, 128, 256, 512}",
                 (long long)kMaxK);
   if (M == 0) return DR_OK;
   drk::RouteLaunch L{};
@@ -142,7 +150,8 @@ dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, 
   L.logit_bf16 = logit_dtype == DR_BF16;
   L.logits = logits;
   L.stream = static_cast<hipStream_t>(stream);
-  return device_status(drk::launch_route_logits(L), "logits launch");
+  const bool split = M > kNarrowMaxM && drk::split_supports(E, K, true, true);
+  return device_status(split ? drk::launch_route_logits(L) : drk::launch_route_narrow_logits(L), "logits launch");
 }
 
 dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, int64_t E, int32_t k,

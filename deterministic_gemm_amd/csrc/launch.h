@@ -29,6 +29,9 @@ hipError_t launch_route_tiled(const RouteLaunch &L);
 bool tiled_supports(int64_t E, int64_t K);
 hipError_t launch_route_split(const RouteLaunch &L);
 bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
+hipError_t launch_route_narrow(const RouteLaunch &L);
+hipError_t launch_route_narrow_logits(const RouteLaunch &L);
+bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
 // The two halves of the split family on their own.
 hipError_t launch_route_logits(const RouteLaunch &L);
 hipError_t launch_route_select(const RouteLaunch &L);

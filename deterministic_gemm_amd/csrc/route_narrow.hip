@@ -1,0 +1,281 @@
+// route_narrow.hip -- the router's logits for small batches, spread over
+// many workgroups.
+//
+// With few tokens the fused kernel gives one workgroup all E experts and all
+// of K, so a handful of CUs stream the whole of W and run every chain step in
+// sequence.  Here a workgroup owns a 16*AT-token x 16*BT-expert tile, and its
+// KG wavefronts split the groups of four K-blocks between them along the
+// canonical tree: with G groups padded to P = 2^ceil(log2 G) leaves, part q
+// takes groups [q*P/KG, (q+1)*P/KG) (those below G; a part may be empty), so
+// each part is a whole subtree of the canonical tree and
+//   logit = the pairwise tree over the KG part values,
+// exactly ("The Illusion of Determinism in Disaggregated Inference", section
+// "The anatomy of the missing numeric contract": any split that respects the
+// stated associative grouping is the same computation).  Inside a part the
+// chains, K-block slots, lane-local tree levels and group counter tree are
+// those of route_tiled.hip; an empty part is -0.0, the identity of the tree's
+// additions, and -0 padding beyond a part's own leaves changes no sum.
+//
+// Each wavefront streams its own x and W pieces global -> LDS through a
+// private ring of S stages (no workgroup barrier in the loop: a wavefront
+// reads only what it loaded).  The logits go to the caller's buffer; the
+// selection kernel of route_split.hip reads them back.
+#include "route_common.h"
+#include "lds_dma.h"
+#include "launch.h"
+
+namespace drk {
+
+template <int E_, int AT_, int BT_, int KG_, int KC_, int S_>
+struct NarrowCfg {
+  static constexpr int E = E_, AT = AT_, BT = BT_, KG = KG_, KC = KC_, S = S_;
+  static constexpr int TT = 16 * AT, ET = 16 * BT;  // tokens, experts per workgroup
+  static constexpr int NT = 64 * KG;
+  static constexpr int NET = E / ET;
+  static constexpr int HU = KC / 4;           // 16-byte x units per (slot, token) row
+  static constexpr int SW = KC * ET + 16;     // W slot stride (floats), +16 staggers banks
+  static constexpr int WST = 4 * SW;
+  static constexpr int XST = 4 * TT * KC;
+  static constexpr int STG = WST + XST;       // floats per stage
+  static constexpr int WU = KC * ET / 4;      // W units per slot
+  static constexpr int WI = 4 * WU / 64;      // W transfers per chunk
+  static constexpr int XI = TT * KC / 64;     // x transfers per chunk
+  static constexpr int PER = WI + XI;
+  static constexpr int CPG = 256 / KC;
+  static constexpr int NQ = AT * BT * 4;       // group partials per lane
+  static_assert(WU % 64 == 0 && WI >= 1 && XI >= 1 && XI * 64 == TT * KC, "whole transfers");
+  static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
+  static_assert(KC % 4 == 0 && 256 % KC == 0, "chunking");
+  static_assert(KG == 1 || KG == 2 || KG == 4, "parts");
+  __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
+};
+
+// Transfers of the wave's chunk ci (group g of its part, chunk cg within the
+// group) into `stage`; past the wave's last chunk, padding transfers keep the
+// count fixed.
+template <class C>
+__device__ __forceinline__ void narrow_issue(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+                                             int K, int64_t m0, int e0, int nb, int g0, int nch, int lane, int ci,
+                                             float *stage) {
+  constexpr int E = C::E, ET = C::ET, KC = C::KC, TT = C::TT, HU = C::HU;
+  const bool live = ci < nch;
+  const int g = g0 + ci / C::CPG;
+  const int kk0 = (ci % C::CPG) * KC;
+#pragma unroll
+  for (int i = 0; i < C::WI; ++i) {
+    const int s = (i * 64) / C::WU;             // slot
+    const int uo = (i * 64) % C::WU;            // first unit within the slot
+    const int u = uo + lane;
+    const int c = u / (ET / 4), e4 = u % (ET / 4);
+    const int blk = 4 * g + s;
+    const int kg = blk * 256 + kk0 + c;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + s * C::SW + uo * 4));
+    const void *src = &g_pad_neg;
+    if (live && blk < nb && kg < K) src = W + static_cast<int64_t>(kg) * E + e0 + 4 * e4;
+    dma16(src, lds);
+  }
+#pragma unroll
+  for (int i = 0; i < C::XI; ++i) {
+    const int u = i * 64 + lane;
+    const int s = u / (TT * HU);
+    const int rem = u % (TT * HU);
+    const int tok = rem / HU, hp = rem % HU;
+    const int h = hp ^ C::swz(tok);
+    const int blk = 4 * g + s;
+    const int kg = blk * 256 + kk0 + 4 * h;
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + C::WST + i * 64 * 4));
+    const int64_t m = m0 + tok;
+    const void *src = &g_pad_pos;
+    if (live && blk < nb && kg < K && m < M) src = xf + m * K + kg;
+    dma16(src, lds);
+  }
+}
+
+template <class C, int MAXL>
+__global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const float *__restrict__ xf,
+                                                                    const float *__restrict__ W, int64_t M, int K,
+                                                                    void *logits, int logit_bf16) {
+  constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, KC = C::KC, HU = C::HU;
+  constexpr int NQ = C::NQ;
+  __shared__ __attribute__((aligned(16))) float ring[C::KG * S * C::STG];
+  __shared__ __attribute__((aligned(16))) float parts[C::KG > 1 ? (C::KG - 1) * 64 * NQ : 4];
+
+  const int64_t bid = blockIdx.x;
+  const int et = static_cast<int>(bid % C::NET);
+  const int64_t m0 = (bid / C::NET) * TT;
+  const int e0 = et * ET;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int s_l = lane >> 4, r_l = lane & 15;
+  const int nb = (K + 255) / 256;
+  const int G = (nb + 3) / 4;
+  int P = 1;
+  while (P < G) P <<= 1;
+  const int span = P / C::KG;  // groups per part (P >= KG by the launcher's choice)
+  const int g0 = min(G, wave * span), g1 = min(G, (wave + 1) * span);
+  const int ng = g1 - g0;
+  const int nch = ng * C::CPG;
+  float *my = ring + wave * S * C::STG;
+
+  f32x16 acc[AT][BT];
+  float stk[MAXL][NQ];
+
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) narrow_issue<C>(xf, W, M, K, m0, e0, nb, g0, nch, lane, i, my + i * C::STG);
+
+  for (int ci = 0; ci < nch; ++ci) {
+    const int gi = ci / C::CPG, cg = ci % C::CPG;
+    const int g = g0 + gi;
+    if (cg == 0) {
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const float init = (4 * g + s < nb) ? 0.0f : -0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[a][b][4 * s + q] = init;
+          }
+    }
+    compiler_fence();
+    wait_vmcnt<C::PER * (S - 2)>();
+    compiler_fence();
+    narrow_issue<C>(xf, W, M, K, m0, e0, nb, g0, nch, lane, ci + S - 1, my + ((ci + S - 1) % S) * C::STG);
+    const float *cur = my + (ci % S) * C::STG;
+    const float *xs = cur + C::WST;
+#pragma unroll
+    for (int c4 = 0; c4 < KC / 4; ++c4) {
+      float4 av[AT];
+#pragma unroll
+      for (int a = 0; a < AT; ++a) {
+        const int tok = a * 16 + r_l;
+        av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+      }
+      float bw[BT][4];
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bw[b][q] = cur[s_l * C::SW + (4 * c4 + q) * ET + b * 16 + r_l];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int a = 0; a < AT; ++a)
+#pragma unroll
+          for (int b = 0; b < BT; ++b) {
+            const float aval = (q == 0) ? av[a].x : (q == 1) ? av[a].y : (q == 2) ? av[a].z : av[a].w;
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[b][q], acc[a][b], 0, 0, 0);
+          }
+    }
+    if (cg == C::CPG - 1) {
+      // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
+      float qv[NQ];
+#pragma unroll
+      for (int a = 0; a < AT; ++a)
+#pragma unroll
+        for (int b = 0; b < BT; ++b)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            qv[(a * BT + b) * 4 + q] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
+      tree_push<MAXL, NQ>(stk, qv, gi);
+    }
+  }
+  // no transfer may still be writing this workgroup's LDS past this point
+  compiler_fence();
+  wait_vmcnt<0>();
+
+  float part[NQ];
+  if (ng > 0) {
+    tree_final<MAXL, NQ>(stk, ng, part);
+  } else {
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) part[j] = -0.0f;  // an empty part: the tree's identity
+  }
+  if constexpr (C::KG > 1) {
+    // the top levels of the canonical tree: parts combined pairwise in order
+    if (wave > 0) {
+#pragma unroll
+      for (int j = 0; j < NQ; ++j) parts[((wave - 1) * NQ + j) * 64 + lane] = part[j];
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      float p[C::KG];
+      p[0] = part[j];
+#pragma unroll
+      for (int w = 1; w < C::KG; ++w) p[w] = parts[((w - 1) * NQ + j) * 64 + lane];
+      if constexpr (C::KG == 2) part[j] = p[0] + p[1];
+      else part[j] = (p[0] + p[1]) + (p[2] + p[3]);
+    }
+  }
+
+  // lane (s_l, r_l) holds token 16a + 4s_l + q at expert e0 + 16b + r_l
+#pragma unroll
+  for (int a = 0; a < AT; ++a)
+#pragma unroll
+    for (int b = 0; b < BT; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t m = m0 + a * 16 + 4 * s_l + q;
+        const float val = part[(a * BT + b) * 4 + q];
+        if (m < M) {
+          const int64_t idx = m * C::E + e0 + b * 16 + r_l;
+          if (logit_bf16) static_cast<uint16_t *>(logits)[idx] = f32_to_bf16(val);
+          else static_cast<float *>(logits)[idx] = val;
+        }
+      }
+}
+
+template <class C, int MAXL>
+static hipError_t launch_narrow_cm(const RouteLaunch &L) {
+  const int64_t nblk = (L.M + C::TT - 1) / C::TT * C::NET;
+  hipLaunchKernelGGL((route_narrow_logits_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0,
+                     L.stream, L.xf, L.W, L.M, static_cast<int>(L.K), L.logits, L.logit_bf16);
+  return hipGetLastError();
+}
+
+// groups per part, then the counter-stack depth for that many groups
+template <class C>
+static hipError_t launch_narrow_c(const RouteLaunch &L) {
+  const int64_t nb = (L.K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  int64_t P = 1;
+  while (P < G) P <<= 1;
+  const int64_t span = P / C::KG;
+  if (span <= 1) return launch_narrow_cm<C, 1>(L);
+  if (span <= 2) return launch_narrow_cm<C, 2>(L);
+  if (span <= 4) return launch_narrow_cm<C, 3>(L);
+  return launch_narrow_cm<C, 4>(L);
+}
+
+template <int E, int AT, int BT, int KC, int S>
+static hipError_t launch_narrow_e(const RouteLaunch &L) {
+  const int64_t nb = (L.K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  if (G >= 4) return launch_narrow_c<NarrowCfg<E, AT, BT, 4, KC, S>>(L);
+  if (G >= 2) return launch_narrow_c<NarrowCfg<E, AT, BT, 2, KC, S>>(L);
+  return launch_narrow_c<NarrowCfg<E, AT, BT, 1, KC, S>>(L);
+}
+
+bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
+  return (E == 64 || E == 128 || E == 256 || E == 512) && K >= 1 && K <= 16384 && (K % 4) == 0 && x_f32 &&
+         has_logits;
+}
+
+hipError_t launch_route_narrow_logits(const RouteLaunch &L) {
+  switch (L.E) {
+    case 64: return launch_narrow_e<64, 1, 1, 16, 4>(L);
+    case 128: return launch_narrow_e<128, 1, 1, 16, 4>(L);
+    case 256: return launch_narrow_e<256, 1, 1, 16, 4>(L);
+    case 512: return launch_narrow_e<512, 1, 1, 16, 4>(L);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_route_narrow(const RouteLaunch &L) {
+  const hipError_t e = launch_route_narrow_logits(L);
+  if (e != hipSuccess) return e;
+  return launch_route_select(L);
+}
+
+}  // namespace drk

@@ -58,9 +58,13 @@ typedef enum dr_variant {
   DR_VARIANT_AUTO = 0,
   DR_VARIANT_ROWWISE = 1, /* few tokens per workgroup, vector FMA (small M) */
   DR_VARIANT_TILED = 2,   /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
-  DR_VARIANT_SPLIT = 3    /* (token, expert) tiles on matrix cores writing the logits, then a
+  DR_VARIANT_SPLIT = 3,   /* (token, expert) tiles on matrix cores writing the logits, then a
                              selection kernel reading them back; needs fp32 x, K % 4 == 0,
                              E in {256, 512} and the logits output */
+  DR_VARIANT_NARROW = 4   /* small batches: 16-token x 16-expert tiles whose wavefronts split
+                             the K groups along the canonical tree, writing the logits, then
+                             the selection kernel; needs fp32 x, K % 4 == 0, E <= 512 and the
+                             logits output */
 } dr_variant;
 
 /* Divide the k selected weights by their sum (left to right in rank order). */
@@ -131,9 +135,10 @@ dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dty
 /*
  * dr_route_logits -- the first half of dr_route on its own: the canonical
  * logits [M,E] (fp32, or rounded to bf16 RNE when logit_dtype is DR_BF16),
- * bit-identical to dr_route's logits output.  Runs the (token, expert) tile
- * kernel of the split family: fp32 x, K % 4 == 0 and E in {256, 512}, else
- * DR_ERR_UNSUPPORTED.  logits is required.
+ * bit-identical to dr_route's logits output.  Runs the logits kernel of the
+ * split family (large M, E in {256, 512}) or of the narrow family: fp32 x,
+ * K % 4 == 0 and E in {64, 128, 256, 512}, else DR_ERR_UNSUPPORTED.  logits
+ * is required.
  */
 dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, int64_t E,
                           dr_dtype logit_dtype, void *logits, void *stream);

@@ -82,6 +82,10 @@ def test_route_variant_rejects(L):
     assert _route(L, K=2046, variant=3) == UNSUPPORTED
     assert _route(L, E=128, k=8, variant=3) == UNSUPPORTED
     assert _route(L, M=0, variant=3) == OK
+    # the narrow family has the same needs, with any E up to 512
+    assert _route(L, lg=0, variant=4) == UNSUPPORTED
+    assert _route(L, xd=1, variant=4) == UNSUPPORTED
+    assert _route(L, E=1024, k=8, variant=4) == UNSUPPORTED
 
 
 def test_halves_reject(L):
@@ -90,7 +94,7 @@ def test_halves_reject(L):
     assert L.dr_route_logits(P(A), P(A), 4, 2048, 256, 5, P(A), None) == INVALID       # bad dtype
     assert L.dr_route_logits(P(A), P(A + 4), 4, 2048, 256, 0, P(A), None) == INVALID   # misaligned
     assert L.dr_route_logits(P(A), P(A), 4, 2046, 256, 0, P(A), None) == UNSUPPORTED   # K % 4
-    assert L.dr_route_logits(P(A), P(A), 4, 2048, 128, 0, P(A), None) == UNSUPPORTED   # E
+    assert L.dr_route_logits(P(A), P(A), 4, 2048, 1024, 0, P(A), None) == UNSUPPORTED  # E
     assert L.dr_route_logits(None, None, 0, 2048, 256, 0, None, None) == OK
     assert L.dr_route_select(P(A), 0, 4, 256, 8, None, None, None, 0, None) == INVALID  # no ids
     assert L.dr_route_select(P(A), 0, 4, 256, 0, P(A), None, None, 0, None) == INVALID  # k = 0
@@ -120,12 +124,15 @@ def test_gate_and_gemm_reject(L):
 
 
 def test_auto_variant_is_a_function_of_shape(L):
-    picks = [dr.auto_variant(M, 2048, 256) for M in range(19, 81)]
+    picks = [dr.auto_variant(M, 2048, 256, logits=False) for M in range(19, 81)]
     assert picks[0] == "rowwise" and picks[-1] == "tiled"
     # exactly one switch, inside the m-scan range
     switches = sum(1 for a, b in zip(picks, picks[1:]) if a != b)
     assert switches == 1
     assert dr.auto_variant(8192, 2048, 1024) == "rowwise"
+    # small batches that ask for the logits spread over narrow tiles
+    assert {dr.auto_variant(M, 2048, 256) for M in range(1, 81)} == {"narrow"}
+    assert dr.auto_variant(19, 2048, 1024) == "rowwise"
     # large batches that ask for the logits take the two-kernel family
     assert dr.auto_variant(8192, 2048, 256) == "split"
     assert dr.auto_variant(8192, 2048, 256, logits=False) == "tiled"

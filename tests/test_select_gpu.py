@@ -18,7 +18,8 @@ def dr():
     return require_gpu()
 
 
-@pytest.mark.parametrize("E,K,M", [(256, 2048, 200), (256, 260, 70), (512, 1024, 130), (256, 4096, 65)])
+@pytest.mark.parametrize("E,K,M", [(256, 2048, 200), (256, 260, 70), (512, 1024, 130), (256, 4096, 65),
+                                   (64, 512, 40), (128, 1000, 33), (256, 2048, 2100)])
 def test_route_logits_matches_oracle(dr, E, K, M):
     rng = np.random.default_rng(E + K + M)
     x = rng.standard_normal((M, K)).astype(np.float32)
