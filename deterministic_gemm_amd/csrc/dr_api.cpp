@@ -167,7 +167,8 @@ dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, i
   if (!aligned16(logits) || !aligned16(ids) || !aligned16(weights) || !aligned16(margins))
     return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
   if (!drk::select_supports(E))
-    return fail(DR_ERR_UNSUPPORTED, "E=%lld: dr_route_select supports E in {64, 128, 256, 512}", (long long)E);
+    return fail(DR_ERR_UNSUPPORTED, "E=%lld: dr_route_select supports E in {64, 128, 256, 512, 1024}",
+                (long long)E);
   if (k > kMaxTopK) return fail(DR_ERR_UNSUPPORTED, "k=%d above %d", k, kMaxTopK);
   if (M == 0) return DR_OK;
   drk::RouteLaunch L{};

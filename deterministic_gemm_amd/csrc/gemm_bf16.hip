@@ -52,6 +52,7 @@ struct GemmCfg {
   static_assert(UB == 2 || UB == 4 || UB == 8 || UB == 16 || UB == 32, "W row units");
   static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
   static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
   // x rows: unit u of row r sits at u ^ swa(r); 16 consecutive rows reading
   // the same unit then hit 16 distinct 16-byte bank groups.
   __host__ __device__ static constexpr int swa(int r) { return UA >= 16 ? r % 16 : (r / (16 / UA)) % UA; }

@@ -47,6 +47,7 @@ struct NarrowCfg {
   static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
   static_assert(KC % 4 == 0 && 256 % KC == 0, "chunking");
   static_assert(KG == 1 || KG == 2 || KG == 4, "parts");
+  static_assert((KG * S * STG + (KG - 1) * 64 * NQ) * 4 <= 160 * 1024, "LDS");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
 };
 
@@ -248,13 +249,15 @@ static hipError_t launch_narrow_c(const RouteLaunch &L) {
   return launch_narrow_cm<C, 4>(L);
 }
 
-template <int E, int AT, int BT, int KC, int S>
+// Parts by group count.  Four stages per wavefront: deeper rings measured
+// slower (fewer workgroups fit on a CU).
+template <int E, int AT, int BT, int KC>
 static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
-  if (G >= 4) return launch_narrow_c<NarrowCfg<E, AT, BT, 4, KC, S>>(L);
-  if (G >= 2) return launch_narrow_c<NarrowCfg<E, AT, BT, 2, KC, S>>(L);
-  return launch_narrow_c<NarrowCfg<E, AT, BT, 1, KC, S>>(L);
+  if (G >= 4) return launch_narrow_c<NarrowCfg<E, AT, BT, 4, KC, 4>>(L);
+  if (G >= 2) return launch_narrow_c<NarrowCfg<E, AT, BT, 2, KC, 4>>(L);
+  return launch_narrow_c<NarrowCfg<E, AT, BT, 1, KC, 4>>(L);
 }
 
 bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
@@ -264,10 +267,10 @@ bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
 
 hipError_t launch_route_narrow_logits(const RouteLaunch &L) {
   switch (L.E) {
-    case 64: return launch_narrow_e<64, 1, 1, 16, 4>(L);
-    case 128: return launch_narrow_e<128, 1, 1, 16, 4>(L);
-    case 256: return launch_narrow_e<256, 1, 1, 16, 4>(L);
-    case 512: return launch_narrow_e<512, 1, 1, 16, 4>(L);
+    case 64: return launch_narrow_e<64, 1, 1, 16>(L);
+    case 128: return launch_narrow_e<128, 1, 1, 16>(L);
+    case 256: return launch_narrow_e<256, 1, 1, 16>(L);
+    case 512: return launch_narrow_e<512, 1, 1, 16>(L);
     default: return hipErrorInvalidValue;
   }
 }

@@ -57,6 +57,7 @@ struct SplitCfg {
   static_assert(KC % 4 == 0 && 256 % KC == 0 && S == 4, "chunking");
   static_assert(TT * LGP <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");
+  static_assert(S * STG * 4 <= 160 * 1024, "LDS");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
 };
 
@@ -338,6 +339,28 @@ __global__ __launch_bounds__(256) void route_split_epilogue_kernel(int64_t M, Ep
   route_select_row16<E>(v, scr[slot], m, live, ea);
 }
 
+// Small batches: one wavefront per token (the row-wise kernel's epilogue),
+// which finishes a token in fewer dependent steps than four tokens sharing a
+// wavefront; four tokens per workgroup.  The token's logits are widened into
+// an LDS row first; the epilogue then sees the values as given and writes no
+// logits.
+template <int E>
+__global__ __launch_bounds__(256) void route_select_wave_kernel(int64_t M, EpilogueArgs ea) {
+  __shared__ __attribute__((aligned(16))) float rows[4][E + 4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m = static_cast<int64_t>(blockIdx.x) * 4 + wave;
+  if (m >= M) return;
+  float *row = rows[wave];
+  for (int e = lane; e < E; e += 64)
+    row[e] = ea.logit_bf16 ? bf16_to_f32(static_cast<const uint16_t *>(ea.logits)[m * E + e])
+                           : static_cast<const float *>(ea.logits)[m * E + e];
+  __builtin_amdgcn_wave_barrier();
+  EpilogueArgs a = ea;
+  a.logits = nullptr;
+  a.logit_bf16 = 0;
+  route_token<E>(row, m, a);
+}
+
 template <class C, int MAXL>
 static hipError_t launch_logits_cm(const RouteLaunch &L) {
   const int64_t ntt = (L.M + C::TT - 1) / C::TT;
@@ -359,10 +382,20 @@ static hipError_t launch_logits_c(const RouteLaunch &L) {
   return launch_logits_cm<C, 5>(L);
 }
 
+// Batches up to this size select with one wavefront per token.
+constexpr int64_t kSelectWaveMaxM = 1024;
+
 template <int E>
 static hipError_t launch_select_e(const RouteLaunch &L) {
   EpilogueArgs ea{L.k, L.logit_bf16, L.flags, L.ids, L.weights, L.logits, L.margins};
-  hipLaunchKernelGGL((route_split_epilogue_kernel<E>), dim3(static_cast<uint32_t>((L.M + 15) / 16)), dim3(256), 0,
+  if constexpr (E <= 512) {
+    if (L.M > kSelectWaveMaxM) {
+      hipLaunchKernelGGL((route_split_epilogue_kernel<E>), dim3(static_cast<uint32_t>((L.M + 15) / 16)), dim3(256), 0,
+                         L.stream, L.M, ea);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((route_select_wave_kernel<E>), dim3(static_cast<uint32_t>((L.M + 3) / 4)), dim3(256), 0,
                      L.stream, L.M, ea);
   return hipGetLastError();
 }
@@ -371,7 +404,7 @@ bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
   return (E == 256 || E == 512) && K >= 1 && K <= 16384 && (K % 4) == 0 && x_f32 && has_logits;
 }
 
-bool select_supports(int64_t E) { return E == 64 || E == 128 || E == 256 || E == 512; }
+bool select_supports(int64_t E) { return E == 64 || E == 128 || E == 256 || E == 512 || E == 1024; }
 
 hipError_t launch_route_logits(const RouteLaunch &L) {
   switch (L.E) {
@@ -388,6 +421,7 @@ hipError_t launch_route_select(const RouteLaunch &L) {
     case 128: return launch_select_e<128>(L);
     case 256: return launch_select_e<256>(L);
     case 512: return launch_select_e<512>(L);
+    case 1024: return launch_select_e<1024>(L);
     default: return hipErrorInvalidValue;
   }
 }

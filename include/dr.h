@@ -149,8 +149,8 @@ dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, 
  * on its own logits ("vllm.cpp PR #2556", summary: the selection is a
  * function of the logit values alone).  logits [M,E] fp32, or bf16 bits
  * (DR_BF16, widened exactly); the values are used as given.  E in {64, 128,
- * 256, 512}, 1 <= k <= min(E, 32); ids required, weights and margins may be
- * NULL; flags as in dr_route.
+ * 256, 512, 1024}, 1 <= k <= min(E, 32); ids required, weights and margins may
+ * be NULL; flags as in dr_route.
  */
 dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, int64_t E, int32_t k,
                           int32_t *ids, float *weights, dr_margin *margins, uint32_t flags,

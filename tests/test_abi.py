@@ -99,7 +99,7 @@ def test_halves_reject(L):
     assert L.dr_route_select(P(A), 0, 4, 256, 8, None, None, None, 0, None) == INVALID  # no ids
     assert L.dr_route_select(P(A), 0, 4, 256, 0, P(A), None, None, 0, None) == INVALID  # k = 0
     assert L.dr_route_select(P(A), 0, 4, 256, 8, P(A), None, None, 2, None) == INVALID  # flags
-    assert L.dr_route_select(P(A), 0, 4, 1024, 8, P(A), None, None, 0, None) == UNSUPPORTED
+    assert L.dr_route_select(P(A), 0, 4, 2048, 8, P(A), None, None, 0, None) == UNSUPPORTED
     assert L.dr_route_select(P(A), 0, 4, 256, 33, P(A), None, None, 0, None) == UNSUPPORTED
     assert L.dr_route_select(None, 0, 0, 256, 8, None, None, None, 0, None) == OK
 

@@ -50,23 +50,26 @@ def _special_logits(rng, M, E):
     return lg
 
 
-@pytest.mark.parametrize("E,k", [(64, 1), (64, 32), (128, 8), (256, 8), (256, 32), (512, 10)])
-def test_route_select_matches_oracle(dr, E, k):
-    rng = np.random.default_rng(7 * E + k)
-    lg = _special_logits(rng, 90, E)
+@pytest.mark.parametrize("E,k,M", [(64, 1, 90), (64, 32, 90), (128, 8, 90), (256, 8, 90), (256, 32, 90),
+                                   (512, 10, 90), (1024, 8, 90), (256, 8, 1100), (64, 32, 1100), (512, 10, 1100)])
+def test_route_select_matches_oracle(dr, E, k, M):
+    """One wavefront per token (M <= 1024, and E = 1024) and four tokens per
+    wavefront (larger M) against the oracle."""
+    rng = np.random.default_rng(7 * E + k + M)
+    lg = _special_logits(rng, M, E)
     for renorm in (False, True):
         ids, w, mg = oracle.select(lg, k, renormalize=renorm)
-        note(f"route_select f32 E={E} k={k} renorm={renorm}")
+        note(f"route_select f32 E={E} k={k} M={M} renorm={renorm}")
         gi, gw, gm = dr.route_select(dev(lg), k, renormalize=renorm)
         got = (host(gi), host(gw), None, dr.margins_to_numpy(gm))
-        assert_route_equal(got, (ids, w, None, mg), what=f"select E={E} k={k} renorm={renorm}")
+        assert_route_equal(got, (ids, w, None, mg), what=f"select E={E} k={k} M={M} renorm={renorm}")
 
 
-@pytest.mark.parametrize("E", [64, 256])
-def test_route_select_bf16_logits(dr, E):
+@pytest.mark.parametrize("E,M", [(64, 70), (256, 70), (256, 1100), (1024, 70)])
+def test_route_select_bf16_logits(dr, E, M):
     """bf16 logits are widened exactly and used as they are."""
-    rng = np.random.default_rng(E)
-    lg = _special_logits(rng, 70, E)
+    rng = np.random.default_rng(E + M)
+    lg = _special_logits(rng, M, E)
     lg_t = torch.from_numpy(lg).to(torch.bfloat16)
     widened = lg_t.float().numpy()
     ids, w, mg = oracle.select(widened, 8)
