@@ -41,9 +41,9 @@ constexpr int64_t kTiledMinM = 48;
 // Calls that ask for the logits run as two kernels, the logits then the
 // selection.  Up to kNarrowMaxM tokens the logits spread over small (token,
 // expert) tiles with the K groups split between wavefronts; above it they use
-// 64 x 128 tiles (measured crossover at K=2048, E=256: between M=2048 and
-// M=3072).  Without the logits output the fused kernels run.
-constexpr int64_t kNarrowMaxM = 2560;
+// 64 x 64 or 64 x 128 tiles (measured crossover at K=2048, E=256: between
+// M=1024 and M=2048).  Without the logits output the fused kernels run.
+constexpr int64_t kNarrowMaxM = 1280;
 
 dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
                      int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,

@@ -26,36 +26,44 @@
 namespace drk {
 
 // A wavefront owns 16*AT tokens x 16*BT experts as AT x BT tiles of 16x16.
-template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_>
+// With KP = 2 the workgroup's wavefronts form two parts that run the two
+// halves of the canonical tree over K-groups (groups padded to P =
+// 2^ceil(log2 G) leaves, part q taking groups [qP/2, (q+1)P/2)), each part on
+// its own half of every stage; the two part values are added at the end,
+// which is the tree's top level, so the logits are the same bits.
+template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_, int KP_ = 1>
 struct SplitCfg {
-  static constexpr int E = E_, ET = ET_, AT = AT_, BT = BT_, WT = WT_, KC = KC_, S = S_;
+  static constexpr int E = E_, ET = ET_, AT = AT_, BT = BT_, WT = WT_, KC = KC_, S = S_, KP = KP_;
   static constexpr int EW = 16 * BT;          // experts per wavefront
   static constexpr int NWE = ET / EW;         // wavefronts across the expert tile
-  static constexpr int NW = NWE * WT;         // wavefronts per workgroup
+  static constexpr int NWP = NWE * WT;        // wavefronts per part
+  static constexpr int NW = NWP * KP;         // wavefronts per workgroup
   static constexpr int NT = NW * 64;          // threads per workgroup
   static constexpr int TW = 16 * AT;          // tokens per wavefront
   static constexpr int TT = WT * TW;          // tokens per workgroup
   static constexpr int NET = E / ET;          // expert tiles
   static constexpr int HU = KC / 4;           // 16-byte x units per (slot, token) row
   static constexpr int SW = KC * ET + 16;     // W slot stride (floats), +16 staggers banks
-  static constexpr int WST = 4 * SW;          // W floats per stage
-  static constexpr int XST = 4 * TT * KC;     // x floats per stage
-  static constexpr int STG = WST + XST;       // floats per stage
+  static constexpr int WST = 4 * SW;          // W floats per stage and part
+  static constexpr int XST = 4 * TT * KC;     // x floats per stage and part
+  static constexpr int PST = WST + XST;       // floats per stage and part
+  static constexpr int STG = KP * PST;        // floats per stage
   static constexpr int LGP = ET + 4;          // logit tile pitch (floats)
   static constexpr int WI = 4 * KC * ET / 256;  // W transfers (64 lanes x 16 B) per chunk
-  static constexpr int WIW = WI / NW;           // ... per wavefront
+  static constexpr int WIW = WI / NWP;          // ... per wavefront of the part
   static constexpr int XU = TT * KC;            // x 16-byte units per chunk
   static constexpr int XI = XU / 64;            // x transfers per chunk
-  static constexpr int XIW = XI / NW;           // ... per wavefront
+  static constexpr int XIW = XI / NWP;          // ... per wavefront of the part
   static constexpr int PER = WIW + XIW;         // transfers per chunk per wavefront
   static constexpr int CPG = 256 / KC;          // chunks per group of four K-blocks
   static_assert(NWE * EW == ET, "whole wavefront expert tiles");
-  static_assert(WIW * NW == WI && WIW >= 1, "W transfers split evenly");
-  static_assert(XI * 64 == XU && XIW * NW == XI && XIW >= 1, "x transfers split evenly");
+  static_assert(WIW * NWP == WI && WIW >= 1, "W transfers split evenly");
+  static_assert(XI * 64 == XU && XIW * NWP == XI && XIW >= 1, "x transfers split evenly");
+  static_assert(KP == 1 || KP == 2, "parts");
   static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
   static_assert(PER * (S - 2) <= 63, "vmcnt range");
   static_assert(KC % 4 == 0 && 256 % KC == 0 && S == 4, "chunking");
-  static_assert(TT * LGP <= S * STG, "the logit tile fits in the stages");
+  static_assert(TT * LGP + (KP - 1) * NWP * AT * BT * 4 * 64 <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");
   static_assert(S * STG * 4 <= 160 * 1024, "LDS");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
@@ -65,10 +73,13 @@ struct SplitCfg {
 // dma_issue (route_tiled.hip), with W columns e0 .. e0+ET-1 only.
 template <class C>
 __device__ __forceinline__ void split_issue(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
-                                            int K, int64_t m0, int e0, int nb, int nchunks, int wave, int lane,
-                                            int ci, float *stage) {
+                                            int K, int64_t m0, int e0, int nb, int nchunks, int span, int wave,
+                                            int lane, int ci, float *stage) {
   constexpr int E = C::E, ET = C::ET, KC = C::KC, TT = C::TT, HU = C::HU;
-  const int g = ci / C::CPG;
+  const int part = wave / C::NWP;
+  wave = wave % C::NWP;
+  stage += part * C::PST;
+  const int g = part * span + ci / C::CPG;
   const int kk0 = (ci % C::CPG) * KC;
   const bool live = ci < nchunks;
   const bool full_k = live && (4 * g + 3 < nb) && ((4 * g + 3) * 256 + kk0 + KC <= K);
@@ -119,15 +130,18 @@ __device__ __forceinline__ void split_issue(const float *__restrict__ xf, const 
 // the end of a group of four K-blocks, fold the group's partials.
 template <class C, int MAXL>
 __device__ __forceinline__ void split_step(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
-                                           int K, int64_t m0, int e0, int nb, int nchunks, int wave, int lane,
-                                           int ci, const float *cur, float *refill, f32x16 (&acc)[C::AT][C::BT],
-                                           f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
+                                           int K, int64_t m0, int e0, int nb, int nchunks, int span, int wave,
+                                           int lane, int ci, const float *cur, float *refill,
+                                           f32x16 (&acc)[C::AT][C::BT], f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, S = C::S, HU = C::HU;
   const int s_l = lane >> 4, r_l = lane & 15;
-  const int tb = (wave / C::NWE) * C::TW;
-  const int eb = (wave % C::NWE) * C::EW;
-  const int g = ci / C::CPG;
+  const int part = wave / C::NWP, wp = wave % C::NWP;
+  const int tb = (wp / C::NWE) * C::TW;
+  const int eb = (wp % C::NWE) * C::EW;
+  const int gi = ci / C::CPG;           // group within the part
+  const int g = part * span + gi;
   const int cg = ci % C::CPG;
+  cur += part * C::PST;
   if (cg == 0) {
 #pragma unroll
     for (int a = 0; a < AT; ++a)
@@ -144,7 +158,7 @@ __device__ __forceinline__ void split_step(const float *__restrict__ xf, const f
   wait_vmcnt<C::PER * (S - 2)>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + S - 1, refill);
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
 
   const float *xs = cur + C::WST;
 #pragma unroll
@@ -185,7 +199,7 @@ __device__ __forceinline__ void split_step(const float *__restrict__ xf, const f
           qv[o / 16][o % 16] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
         }
 #pragma unroll
-    for (int v = 0; v < NV; ++v) tree_push_vec<MAXL>(stk[v], qv[v], g);
+    for (int v = 0; v < NV; ++v) tree_push_vec<MAXL>(stk[v], qv[v], gi);
   }
 }
 
@@ -215,45 +229,71 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const float *
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int s_l = lane >> 4, r_l = lane & 15;
-  const int tb = (wave / C::NWE) * C::TW;
-  const int eb = (wave % C::NWE) * C::EW;
+  const int part = wave / C::NWP, wp = wave % C::NWP;
+  const int tb = (wp / C::NWE) * C::TW;
+  const int eb = (wp % C::NWE) * C::EW;
   const int nb = (K + 255) / 256;
   const int G = (nb + 3) / 4;
-  const int nchunks = G * C::CPG;  // a multiple of S
+  int P = 1;
+  while (P < G) P <<= 1;
+  // groups per part: all G with one part; half the padded tree with two (the
+  // launcher uses two parts only when G >= 2; groups past G are padding)
+  const int span = C::KP == 1 ? G : P / 2;
+  const int nchunks = span * C::CPG;  // a multiple of S
 
   f32x16 acc[AT][BT];
   f32x16 stk[AT * BT * 4 / 16][MAXL];
 
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, 0, stg0);
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, 1, stg1);
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, 2, stg2);
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, 0, stg0);
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, 1, stg1);
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, 2, stg2);
   for (int ci = 0; ci < nchunks; ci += 4) {
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 0, stg0, stg3, acc, stk);
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 1, stg1, stg0, acc, stk);
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 2, stg2, stg1, acc, stk);
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, wave, lane, ci + 3, stg3, stg2, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 0, stg0, stg3, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 1, stg1, stg0, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 2, stg2, stg1, acc, stk);
+    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 3, stg3, stg2, acc, stk);
   }
 
-  f32x16 outv[AT * BT * 4 / 16];
+  constexpr int NV = AT * BT * 4 / 16;
+  f32x16 outv[NV];
 #pragma unroll
-  for (int v = 0; v < AT * BT * 4 / 16; ++v) outv[v] = tree_final_vec<MAXL>(stk[v], G);
+  for (int v = 0; v < NV; ++v) outv[v] = tree_final_vec<MAXL>(stk[v], span);
 
   // drain the trailing padding transfers, then stage the tile for row stores
   compiler_fence();
   wait_vmcnt<0>();
   __syncthreads();
-  // lane (s_l, r_l) holds token tb + 16a + 4s_l + q at expert eb + 16b + r_l
   float *lg = smem;
+  if constexpr (C::KP == 2) {
+    // the tree's top level: part 0's value + part 1's value
+    float *comb = smem + TT * C::LGP;
+    if (part == 1) {
 #pragma unroll
-  for (int a = 0; a < AT; ++a)
+      for (int v = 0; v < NV; ++v)
 #pragma unroll
-    for (int b = 0; b < BT; ++b)
+        for (int j = 0; j < 16; ++j) comb[((wp * NV + v) * 16 + j) * 64 + lane] = outv[v][j];
+    }
+    __syncthreads();
+    if (part == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int tok = tb + a * 16 + 4 * s_l + q;
-        const int o = (a * BT + b) * 4 + q;
-        lg[tok * C::LGP + eb + b * 16 + r_l] = outv[o / 16][o % 16];
-      }
+      for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) outv[v][j] = outv[v][j] + comb[((wp * NV + v) * 16 + j) * 64 + lane];
+    }
+  }
+  // lane (s_l, r_l) holds token tb + 16a + 4s_l + q at expert eb + 16b + r_l
+  if (part == 0) {
+#pragma unroll
+    for (int a = 0; a < AT; ++a)
+#pragma unroll
+      for (int b = 0; b < BT; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tok = tb + a * 16 + 4 * s_l + q;
+          const int o = (a * BT + b) * 4 + q;
+          lg[tok * C::LGP + eb + b * 16 + r_l] = outv[o / 16][o % 16];
+        }
+  }
   __syncthreads();
   if (!logit_bf16) {
     float *out = static_cast<float *>(logits);
@@ -374,12 +414,25 @@ template <class C>
 static hipError_t launch_logits_c(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
-  // stack depth = bit length of the number of groups
-  if (G <= 1) return launch_logits_cm<C, 1>(L);
-  if (G <= 2) return launch_logits_cm<C, 2>(L);
-  if (G <= 4) return launch_logits_cm<C, 3>(L);
-  if (G <= 8) return launch_logits_cm<C, 4>(L);
+  int64_t P = 1;
+  while (P < G) P <<= 1;
+  const int64_t span = C::KP == 1 ? G : P / 2;
+  // stack depth = bit length of the number of groups a part folds
+  if (span <= 1) return launch_logits_cm<C, 1>(L);
+  if (span <= 2) return launch_logits_cm<C, 2>(L);
+  if (span <= 4) return launch_logits_cm<C, 3>(L);
+  if (span <= 8) return launch_logits_cm<C, 4>(L);
   return launch_logits_cm<C, 5>(L);
+}
+
+// The CUs of the current device (the 64 x 128 tiles fill MI355X's 256 at
+// M = 8192, E = 256).
+static int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
 }
 
 // Batches up to this size select with one wavefront per token.
@@ -407,9 +460,18 @@ bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
 bool select_supports(int64_t E) { return E == 64 || E == 128 || E == 256 || E == 512 || E == 1024; }
 
 hipError_t launch_route_logits(const RouteLaunch &L) {
+  // 64 x 64 tiles with the K-groups split between two parts while that many
+  // workgroups still fit the chip in one round (twice the workgroups of the
+  // 64 x 128 tiles); needs at least two K-groups.
+  const int64_t two_part_wgs = (L.M + 63) / 64 * (L.E / 64);
+  const bool two = L.K > 1024 && two_part_wgs <= device_cus();
   switch (L.E) {
-    case 256: return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4>>(L);
-    case 512: return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4>>(L);
+    case 256:
+      return two ? launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2>>(L)
+                 : launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4>>(L);
+    case 512:
+      return two ? launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2>>(L)
+                 : launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4>>(L);
     default: return hipErrorInvalidValue;
   }
 }
