@@ -31,9 +31,10 @@ namespace drk {
 // 2^ceil(log2 G) leaves, part q taking groups [qP/2, (q+1)P/2)), each part on
 // its own half of every stage; the two part values are added at the end,
 // which is the tree's top level, so the logits are the same bits.
-template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_, int KP_ = 1>
+template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_, int KP_ = 1, bool LATE_ = false>
 struct SplitCfg {
   static constexpr int E = E_, ET = ET_, AT = AT_, BT = BT_, WT = WT_, KC = KC_, S = S_, KP = KP_;
+  static constexpr bool LATE = LATE_;  // refill the freed stage after the chunk's matrix steps
   static constexpr int EW = 16 * BT;          // experts per wavefront
   static constexpr int NWE = ET / EW;         // wavefronts across the expert tile
   static constexpr int NWP = NWE * WT;        // wavefronts per part
@@ -62,7 +63,7 @@ struct SplitCfg {
   static_assert(KP == 1 || KP == 2, "parts");
   static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
   static_assert(PER * (S - 2) <= 63, "vmcnt range");
-  static_assert(KC % 4 == 0 && 256 % KC == 0 && S == 4, "chunking");
+  static_assert(KC % 4 == 0 && 256 % KC == 0 && (S == 3 || S == 4), "chunking");
   static_assert(TT * LGP + (KP - 1) * NWP * AT * BT * 4 * 64 <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");
   static_assert(S * STG * 4 <= 160 * 1024, "LDS");
@@ -158,7 +159,7 @@ __device__ __forceinline__ void split_step(const float *__restrict__ xf, const f
   wait_vmcnt<C::PER * (S - 2)>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
+  if constexpr (!C::LATE) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
 
   const float *xs = cur + C::WST;
 #pragma unroll
@@ -183,6 +184,12 @@ __device__ __forceinline__ void split_step(const float *__restrict__ xf, const f
           const float aval = (q == 0) ? av[a].x : (q == 1) ? av[a].y : (q == 2) ? av[a].z : av[a].w;
           acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[b][q], acc[a][b], 0, 0, 0);
         }
+  }
+
+  if constexpr (C::LATE) {
+    compiler_fence();
+    split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
+    compiler_fence();
   }
 
   if (cg == C::CPG - 1) {
@@ -213,10 +220,6 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const float *
                                                                    void *logits, int logit_bf16) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, STG = C::STG;
   __shared__ __attribute__((aligned(16))) float smem[S * STG];
-  float *const stg0 = smem;
-  float *const stg1 = smem + STG;
-  float *const stg2 = smem + 2 * STG;
-  float *const stg3 = smem + 3 * STG;
 
   const int64_t bid = blockIdx.x;
   const int64_t hi = bid / 8;
@@ -239,19 +242,20 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const float *
   // groups per part: all G with one part; half the padded tree with two (the
   // launcher uses two parts only when G >= 2; groups past G are padding)
   const int span = C::KP == 1 ? G : P / 2;
-  const int nchunks = span * C::CPG;  // a multiple of S
+  const int nchunks = span * C::CPG;
 
   f32x16 acc[AT][BT];
   f32x16 stk[AT * BT * 4 / 16][MAXL];
 
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, 0, stg0);
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, 1, stg1);
-  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, 2, stg2);
-  for (int ci = 0; ci < nchunks; ci += 4) {
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 0, stg0, stg3, acc, stk);
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 1, stg1, stg0, acc, stk);
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 2, stg2, stg1, acc, stk);
-    split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + 3, stg3, stg2, acc, stk);
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, i, smem + i * STG);
+  // unrolled by S so that every stage address is a compile-time constant
+  for (int ci = 0; ci < nchunks; ci += S) {
+#pragma unroll
+    for (int j = 0; j < S; ++j)
+      if (ci + j < nchunks)
+        split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + j, smem + j * STG,
+                            smem + ((j + S - 1) % S) * STG, acc, stk);
   }
 
   constexpr int NV = AT * BT * 4 / 16;
@@ -410,7 +414,8 @@ static hipError_t launch_logits_cm(const RouteLaunch &L) {
   return hipGetLastError();
 }
 
-template <class C>
+// LMAX: the deepest counter stack this configuration is launched with.
+template <class C, int LMAX = 5>
 static hipError_t launch_logits_c(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
@@ -420,9 +425,11 @@ static hipError_t launch_logits_c(const RouteLaunch &L) {
   // stack depth = bit length of the number of groups a part folds
   if (span <= 1) return launch_logits_cm<C, 1>(L);
   if (span <= 2) return launch_logits_cm<C, 2>(L);
-  if (span <= 4) return launch_logits_cm<C, 3>(L);
-  if (span <= 8) return launch_logits_cm<C, 4>(L);
-  return launch_logits_cm<C, 5>(L);
+  if (span <= 4 || LMAX <= 3) return launch_logits_cm<C, LMAX < 3 ? LMAX : 3>(L);
+  if constexpr (LMAX >= 4) {
+    if (span <= 8) return launch_logits_cm<C, 4>(L);
+  }
+  return launch_logits_cm<C, LMAX>(L);
 }
 
 // The CUs of the current device (the 64 x 128 tiles fill MI355X's 256 at
@@ -466,12 +473,17 @@ hipError_t launch_route_logits(const RouteLaunch &L) {
   const int64_t two_part_wgs = (L.M + 63) / 64 * (L.E / 64);
   const bool two = L.K > 1024 && two_part_wgs <= device_cus();
   switch (L.E) {
+    // chunk length, stage count and refill order as measured fastest; chunks
+    // of 16 steps need too many registers for the deeper counter stacks of
+    // K > 4096
     case 256:
-      return two ? launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2>>(L)
-                 : launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4>>(L);
+      if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true>>(L);
+      if (L.K > 4096) return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4, 1, true>>(L);
+      return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
     case 512:
-      return two ? launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2>>(L)
-                 : launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4>>(L);
+      if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true>>(L);
+      if (L.K > 4096) return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4, 1, true>>(L);
+      return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
     default: return hipErrorInvalidValue;
   }
 }
