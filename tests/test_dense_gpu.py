@@ -81,18 +81,19 @@ def test_gate_dot_bit_exact_and_m_invariant(dense):
 
 
 def test_gate_dot_f32_and_ragged_k():
-    """Row groups of 1..64 lanes (K up to 64 blocks), 16-byte and element-wise
-    loads (rows aligned or not), partial last blocks, mixed dtypes."""
+    """Row groups of 1..64 lanes (K up to 64 blocks), the LDS-staged kernel
+    (rows 16-byte aligned, one dtype) and the direct one (rows not aligned,
+    mixed dtypes), partial last blocks, M not a multiple of a workgroup's rows."""
     dr = require_gpu()
     rng = np.random.default_rng(8)
-    for K in (1, 255, 257, 1000, 3000, 16384):
+    for K in (1, 255, 257, 512, 1000, 2048, 3000, 8192, 16128, 16384):
         x = rng.standard_normal((33, K)).astype(np.float32)
         w = (rng.standard_normal(K) * 0.02).astype(np.float32)
         note(f"gate dot f32 K={K}")
         d, g = dr.gate_dot(dev(x), dev(w))
         rd, rg = oracle.gate_dot(x, w)
         assert f32_equal_bits(d.cpu().numpy(), rd) and f32_equal_bits(g.cpu().numpy(), rg)
-    for K in (260, 1000, 2048):
+    for K in (260, 264, 1000, 2048, 4096, 8000, 16384):
         xb = wl.to_bf16_bits(rng.standard_normal((70, K)).astype(np.float32))
         wb = wl.to_bf16_bits((rng.standard_normal(K) * 0.02).astype(np.float32))
         wf = wl.bf16_bits_to_f32(wb)
