@@ -188,16 +188,23 @@ static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, float *out
   return hipGetLastError();
 }
 
-// The tile is chosen from M (a performance choice only: every configuration
-// runs the same per-output instruction sequence).  Measured at K = N = 4096:
-// narrow tiles with deep K stages for small batches (more workgroups stream
-// W at once), 128x128 with eight wavefronts up to M = 1024, and 256x256 with
-// eight 128x64 wavefront tiles beyond.
+// The tile is chosen from the shape (a performance choice only: every
+// configuration runs the same per-output instruction sequence).  Narrow tiles
+// with deep K stages for small batches (more workgroups stream W at once);
+// otherwise the largest tile whose count still covers the CUs once: 256 x 256
+// (eight 128 x 64 wavefront tiles, K in stages of 64), then 256 x 128 (eight
+// 64 x 64), then 128 x 128 (eight 32 x 64, K in stages of 128).  Measured at
+// K = N = 4096 with the configurations interleaved: M = 4096 130 us (256 x
+// 256), M = 2048 90 us (256 x 128), M = 1024 54 us (128 x 128).
 hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
                             int64_t K, int64_t N, hipStream_t stream) {
   if (M <= 128) return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>>(x, W, out, M, K, N, stream);
-  if (M <= 1024 || N % 256 != 0) return launch_gemm_c<GemmCfg<128, 128, 4, 2, 64, 3>>(x, W, out, M, K, N, stream);
-  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 32, 3>>(x, W, out, M, K, N, stream);
+  const int64_t cus = device_cus();
+  const int64_t mt = (M + 255) / 256;
+  if (N % 256 == 0 && mt * (N / 256) >= cus)
+    return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2>>(x, W, out, M, K, N, stream);
+  if (mt * (N / 128) >= cus) return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>>(x, W, out, M, K, N, stream);
 }
 
 }  // namespace drk

@@ -24,6 +24,9 @@ struct RouteLaunch {
   hipStream_t stream;
 };
 
+// Compute units of the current device (256 if the query fails).
+int device_cus();
+
 hipError_t launch_route_rowwise(const RouteLaunch &L);
 hipError_t launch_route_tiled(const RouteLaunch &L);
 bool tiled_supports(int64_t E, int64_t K);

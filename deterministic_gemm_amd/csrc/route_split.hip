@@ -434,7 +434,7 @@ static hipError_t launch_logits_c(const RouteLaunch &L) {
 
 // The CUs of the current device (the 64 x 128 tiles fill MI355X's 256 at
 // M = 8192, E = 256).
-static int device_cus() {
+int device_cus() {
   int dev = 0, n = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)

@@ -30,7 +30,9 @@ def test_gemm_rows_invariant_across_m_and_close_to_exact(dense):
     xd, Wd = dev_bf16_bits(xb), dev_bf16_bits(Wb)
     note("gemm M=4096")
     full = dr.gemm_bf16(xd, Wd).cpu().numpy()
-    for M in wl.DENSE_MS:
+    # the sweep sizes plus 1024, 2048 and 3000: every tile configuration
+    # (32 x 32, 128 x 128, 256 x 128 with a ragged last tile, 256 x 256)
+    for M in sorted(set(wl.DENSE_MS) | {1024, 2048, 3000}):
         note(f"gemm M={M}")
         out = dr.gemm_bf16(xd[:M].contiguous(), Wd).cpu().numpy()
         assert f32_equal_bits(out, full[:M]), f"M={M} rows differ from the M=4096 run"
@@ -57,9 +59,10 @@ def test_gemm_row_offsets(dense):
 def test_gemm_small_shapes_close_to_exact():
     dr = require_gpu()
     rng = np.random.default_rng(3)
-    # every tile configuration, partial K stages, ragged M tiles
+    # every tile configuration, partial K stages, ragged M tiles (the last two
+    # take 256 x 128 and 256 x 256 tiles on a 256-CU device)
     for (M, K, N) in ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
-                      (1500, 160, 256)):
+                      (1500, 160, 256), (2100, 96, 4096), (4100, 160, 4096)):
         xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
         Wb = wl.to_bf16_bits(rng.standard_normal((K, N)).astype(np.float32))
         note(f"gemm small {M}x{K}x{N}")
