@@ -106,7 +106,12 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * C::BM;
-  const int n0 = blockIdx.x * C::BN;
+  // Workgroups go to the eight XCDs in turn.  With a multiple of eight column
+  // tiles, XCD j takes the j-th contiguous eighth of them, so neighbouring
+  // tiles that share 128-byte lines of W read them through one L2.
+  const int nx = gridDim.x;
+  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int n0 = bx * C::BN;
   const int nst = (K + C::BK - 1) / C::BK;
 
   f32x4 acc[FM][FN];

@@ -58,6 +58,12 @@ def bind(path: str) -> ctypes.CDLL:
     L.dro_gate_dot.restype = None
     L.dro_gemm_bf16_ref.argtypes = [P, P, P, i64, i64, i64, c_int]
     L.dro_gemm_bf16_ref.restype = None
+    L.dro_moe_permute.argtypes = [P, i64, i32, i32, P, P, P]
+    L.dro_moe_permute.restype = c_int
+    L.dro_moe_gather.argtypes = [P, i64, P, i64, i64, P]
+    L.dro_moe_gather.restype = None
+    L.dro_moe_combine.argtypes = [P, c_int, P, P, P, i64, P, c_int, P, i64, i32, i64, P, c_int]
+    L.dro_moe_combine.restype = c_int
     L.dro_default_threads.argtypes = []
     L.dro_default_threads.restype = c_int
     return L
@@ -183,4 +189,56 @@ def gemm_bf16_ref(x_bits, W_bits, nthreads: int = 0):
     assert K == K2
     out = np.empty((M, N), dtype=np.float32)
     lib().dro_gemm_bf16_ref(_ptr(x), _ptr(W), _ptr(out), M, K, N, nthreads)
+    return out
+
+
+def moe_permute(ids, E: int):
+    """dro_moe_permute: ids [M,k] int32 -> (offsets [E+1], rows [M*k], pos [M,k]), all int32."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    M, k = ids.shape
+    offsets = np.empty((E + 1,), dtype=np.int32)
+    rows = np.empty((M * k,), dtype=np.int32)
+    pos = np.empty((M, k), dtype=np.int32)
+    if lib().dro_moe_permute(_ptr(ids), M, k, E, _ptr(offsets), _ptr(rows), _ptr(pos)) != 0:
+        raise ValueError("dro_moe_permute rejected its arguments")
+    return offsets, rows, pos
+
+
+def moe_gather(x, rows):
+    """dro_moe_gather: x [M,D] (any dtype) -> xp [P,D] with xp[p] = x[rows[p]]."""
+    x = np.ascontiguousarray(x)
+    rows = np.ascontiguousarray(rows, dtype=np.int32)
+    D = x.shape[1]
+    xp = np.empty((rows.size, D), dtype=x.dtype)
+    lib().dro_moe_gather(_ptr(x), x.itemsize, _ptr(rows), rows.size, D, _ptr(xp))
+    return xp
+
+
+def _elem_arg(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return a, 1
+    if a.dtype != np.float32:
+        raise TypeError("expected float32 or uint16 (bf16 bits)")
+    return a, 0
+
+
+def moe_combine(y, weights, ids, pos, shared=None, gate=None, nthreads: int = 0):
+    """dro_moe_combine: y [P,D] (f32 or bf16 bits), weights/ids/pos [M,k],
+    optional shared [M,D] with gate [M] -> out [M,D] f32."""
+    y, yb = _elem_arg(y)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    M, k = ids.shape
+    P, D = y.shape
+    sb = 0
+    if shared is not None:
+        shared, sb = _elem_arg(shared)
+        gate = np.ascontiguousarray(gate, dtype=np.float32)
+    out = np.empty((M, D), dtype=np.float32)
+    rc = lib().dro_moe_combine(_ptr(y), yb, _ptr(weights), _ptr(ids), _ptr(pos), P, _ptr(shared), sb,
+                               _ptr(gate) if shared is not None else None, M, k, D, _ptr(out), nthreads)
+    if rc != 0:
+        raise ValueError("dro_moe_combine rejected its arguments")
     return out

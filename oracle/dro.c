@@ -495,3 +495,113 @@ void dro_gemm_bf16_ref(const uint16_t *x, const uint16_t *W, float *out, int64_t
   j.out = out;
   run_rows(&j, nthreads);
 }
+
+/* ------------------------------------------------- permutation, combine */
+
+int dro_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
+                    int32_t *rows, int32_t *pos) {
+  if (M < 0 || k < 1 || E < 1) return 1;
+  for (int64_t m = 0; m < M; ++m)
+    for (int32_t j = 0; j < k; ++j) {
+      int32_t e = ids[m * k + j];
+      if (e < 0 || e >= E) return 1;
+      for (int32_t i = 0; i < j; ++i)
+        if (ids[m * k + i] == e) return 1;
+    }
+  /* one pass per expert, in expert order; inside it, assignments in token order */
+  int64_t p = 0;
+  for (int32_t e = 0; e < E; ++e) {
+    offsets[e] = (int32_t)p;
+    for (int64_t m = 0; m < M; ++m)
+      for (int32_t j = 0; j < k; ++j)
+        if (ids[m * k + j] == e) {
+          rows[p] = (int32_t)m;
+          pos[m * k + j] = (int32_t)p;
+          ++p;
+        }
+  }
+  offsets[E] = (int32_t)p;
+  return 0;
+}
+
+void dro_moe_gather(const void *x, int64_t elem_bytes, const int32_t *rows, int64_t P, int64_t D,
+                    void *xp) {
+  const int64_t row_bytes = elem_bytes * D;
+  for (int64_t p = 0; p < P; ++p)
+    memcpy((char *)xp + p * row_bytes, (const char *)x + (int64_t)rows[p] * row_bytes, (size_t)row_bytes);
+}
+
+static float elem_at(const void *a, int is_bf16, int64_t i) {
+  return is_bf16 ? bf16_widen(((const uint16_t *)a)[i]) : ((const float *)a)[i];
+}
+
+typedef struct {
+  const void *y;
+  int y_is_bf16;
+  const float *weights;
+  const int32_t *ids;
+  const int32_t *pos;
+  const void *shared;
+  int shared_is_bf16;
+  const float *gate;
+  int32_t k;
+  int64_t D;
+  float *out;
+} combine_job;
+
+static void combine_token(const combine_job *c, int64_t m) {
+  /* the slots of token m in ascending (expert id, slot index) */
+  int32_t order[64];
+  int32_t k = c->k;
+  for (int32_t j = 0; j < k; ++j) order[j] = j;
+  for (int32_t a = 1; a < k; ++a)
+    for (int32_t b = a; b > 0; --b) {
+      int32_t s = order[b - 1], t = order[b];
+      int32_t es = c->ids[m * k + s], et = c->ids[m * k + t];
+      if (es > et || (es == et && s > t)) {
+        order[b - 1] = t;
+        order[b] = s;
+      }
+    }
+  for (int64_t d = 0; d < c->D; ++d) {
+    float acc = 0.0f;
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t s = order[i];
+      float yv = elem_at(c->y, c->y_is_bf16, (int64_t)c->pos[m * k + s] * c->D + d);
+      acc = fmaf(c->weights[m * k + s], yv, acc);
+    }
+    if (c->shared) acc = fmaf(c->gate[m], elem_at(c->shared, c->shared_is_bf16, m * c->D + d), acc);
+    c->out[m * c->D + d] = acc;
+  }
+}
+
+typedef struct {
+  const combine_job *c;
+  int64_t M;
+  int nthreads, tid;
+} combine_thread;
+
+static void *combine_main(void *p) {
+  combine_thread *t = (combine_thread *)p;
+  for (int64_t m = t->tid; m < t->M; m += t->nthreads) combine_token(t->c, m);
+  return NULL;
+}
+
+int dro_moe_combine(const void *y, int y_is_bf16, const float *weights, const int32_t *ids,
+                    const int32_t *pos, int64_t P, const void *shared, int shared_is_bf16,
+                    const float *gate, int64_t M, int32_t k, int64_t D, float *out, int nthreads) {
+  if (M < 0 || k < 1 || k > 64 || D < 0 || (shared && !gate)) return 1;
+  for (int64_t i = 0; i < M * k; ++i)
+    if (pos[i] < 0 || pos[i] >= P) return 1;
+  combine_job c = {y, y_is_bf16, weights, ids, pos, shared, shared_is_bf16, gate, k, D, out};
+  int n = nthreads > 0 ? nthreads : dro_default_threads();
+  if (n > 64) n = 64;
+  pthread_t th[64];
+  combine_thread ct[64];
+  for (int i = 0; i < n; ++i) {
+    ct[i] = (combine_thread){&c, M, n, i};
+    pthread_create(&th[i], NULL, combine_main, &ct[i]);
+  }
+  for (int i = 0; i < n; ++i) pthread_join(th[i], NULL);
+  return 0;
+}

@@ -111,6 +111,44 @@ void dro_gate_dot(const void *x, int x_is_bf16, const void *w, int w_is_bf16, in
 void dro_gemm_bf16_ref(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
                        int64_t K, int64_t N, int nthreads);
 
+/* ---- The step after routing: token permutation and the MoE combine ----
+ *
+ * Source: vllm.cpp PR #2556, section "Why a value tap could never have said
+ * this": the engine's MoE combine is order-invariant over a token's k slots,
+ * which is why two arms' selections compare as sets of sorted ids; the
+ * assembled per-slot expert outputs are one of the block's four axes (the
+ * table in section "The measurement").  The pages do not spell the combine
+ * out; the readings taken here are stated next to each function. */
+
+/* Group the M*k routing assignments (token m, slot j) -> expert ids[m,j] by
+ * expert.  Reading: experts ascending, and within an expert, tokens
+ * ascending (a stable grouping of the assignments in token order).
+ * offsets [E+1]: offsets[e] = number of assignments to experts < e, so
+ *   expert e owns grouped rows [offsets[e], offsets[e+1]) and offsets[E] = M*k.
+ * rows [M*k]: rows[p] = the token of grouped row p.
+ * pos [M,k]: pos[m,j] = the grouped row of assignment (m,j).
+ * Returns nonzero (and writes nothing) when an id is outside [0,E) or a row
+ * repeats an expert. */
+int dro_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
+                    int32_t *rows, int32_t *pos);
+
+/* xp[p,:] = x[rows[p],:] for p in [0,P): the activations in grouped order.
+ * Rows are D elements of elem_bytes bytes each, copied bit for bit. */
+void dro_moe_gather(const void *x, int64_t elem_bytes, const int32_t *rows, int64_t P, int64_t D,
+                    void *xp);
+
+/* out[m,d] for a token's k slots.  Reading: the slots are taken in ascending
+ * expert id (ascending slot index between equal ids), and
+ *   acc = +0;  for each slot s in that order: acc = fmaf(w[m,s], y[pos[m,s],d], acc)
+ * then, when `shared` is given, acc = fmaf(gate[m], shared[m,d], acc) last.
+ * The result therefore does not depend on the order of the k slots.  y is
+ * [P,D] (f32, or bf16 bits widened exactly), shared is [M,D] (same choice)
+ * or NULL, gate [M] (required with shared), out [M,D] f32.
+ * Returns nonzero when a pos entry is outside [0,P). */
+int dro_moe_combine(const void *y, int y_is_bf16, const float *weights, const int32_t *ids,
+                    const int32_t *pos, int64_t P, const void *shared, int shared_is_bf16,
+                    const float *gate, int64_t M, int32_t k, int64_t D, float *out, int nthreads);
+
 /* Number of threads nthreads<=0 resolves to. */
 int dro_default_threads(void);
 

@@ -19,6 +19,7 @@ from oracle import build as obuild
 import test_oracle_brute as tb
 import test_oracle_invariants as ti
 import test_oracle_math as tm
+import test_oracle_moe as tmoe
 
 SRC = os.path.join(os.path.dirname(obuild.__file__), "dro.c")
 HDR = os.path.join(os.path.dirname(obuild.__file__), "dro.h")
@@ -72,6 +73,22 @@ def _pins_batch():
     ti.test_thread_count_does_not_change_bits()
 
 
+def _pins_permute():
+    for case in ((5, 2, 4), (19, 8, 256), (300, 8, 64)):
+        tmoe.test_permute_matches_stable_argsort(*case)
+    tmoe.test_permute_closed_forms()
+
+
+def _pins_combine():
+    for kind in ("normal", "cancel", "tiny"):
+        tmoe.test_combine_matches_exact_rounding(kind)
+    tmoe.test_combine_does_not_depend_on_slot_order()
+    tmoe.test_combine_integer_inputs_are_exact()
+    tmoe.test_combine_zero_sum_is_positive_zero()
+    tmoe.test_combine_shared_term_comes_last()
+    tmoe.test_combine_ascending_expert_order_is_distinguished()
+
+
 # (name, text in dro.c, replacement, pins that must catch it)
 MUTATIONS = [
     ("tie_break_highest_index",
@@ -122,6 +139,30 @@ MUTATIONS = [
      "      raw[e] = canonical_dot(j->x, j->x_is_bf16, j->W, j->K, E, m, e, j->kblock, part);",
      "      raw[e] = canonical_dot(j->x, j->x_is_bf16, j->W, j->K, E, m, e, j->M > 1 ? j->kblock / 2 : j->kblock, part);",
      _pins_batch),
+    ("permute_tokens_descending",
+     "    for (int64_t m = 0; m < M; ++m)\n      for (int32_t j = 0; j < k; ++j)\n        if (ids[m * k + j] == e) {",
+     "    for (int64_t m = M - 1; m >= 0; --m)\n      for (int32_t j = 0; j < k; ++j)\n        if (ids[m * k + j] == e) {",
+     _pins_permute),
+    ("permute_offsets_inclusive",
+     "    offsets[e] = (int32_t)p;\n    for (int64_t m = 0; m < M; ++m)\n      for (int32_t j = 0; j < k; ++j)\n        if (ids[m * k + j] == e) {\n          rows[p] = (int32_t)m;\n          pos[m * k + j] = (int32_t)p;\n          ++p;\n        }\n  }",
+     "    for (int64_t m = 0; m < M; ++m)\n      for (int32_t j = 0; j < k; ++j)\n        if (ids[m * k + j] == e) {\n          rows[p] = (int32_t)m;\n          pos[m * k + j] = (int32_t)p;\n          ++p;\n        }\n    offsets[e] = (int32_t)p;\n  }",
+     _pins_permute),
+    ("combine_in_slot_order",
+     "      if (es > et || (es == et && s > t)) {",
+     "      if (s > t) {",
+     _pins_combine),
+    ("combine_starts_at_minus_zero",
+     "    float acc = 0.0f;\n    for (int32_t i = 0; i < k; ++i) {",
+     "    float acc = -0.0f;\n    for (int32_t i = 0; i < k; ++i) {",
+     _pins_combine),
+    ("combine_mul_then_add",
+     "      acc = fmaf(c->weights[m * k + s], yv, acc);",
+     "      acc = acc + c->weights[m * k + s] * yv;",
+     _pins_combine),
+    ("combine_shared_first",
+     "    float acc = 0.0f;\n    for (int32_t i = 0; i < k; ++i) {\n      int32_t s = order[i];\n      float yv = elem_at(c->y, c->y_is_bf16, (int64_t)c->pos[m * k + s] * c->D + d);\n      acc = fmaf(c->weights[m * k + s], yv, acc);\n    }\n    if (c->shared) acc = fmaf(c->gate[m], elem_at(c->shared, c->shared_is_bf16, m * c->D + d), acc);",
+     "    float acc = 0.0f;\n    if (c->shared) acc = fmaf(c->gate[m], elem_at(c->shared, c->shared_is_bf16, m * c->D + d), acc);\n    for (int32_t i = 0; i < k; ++i) {\n      int32_t s = order[i];\n      float yv = elem_at(c->y, c->y_is_bf16, (int64_t)c->pos[m * k + s] * c->D + d);\n      acc = fmaf(c->weights[m * k + s], yv, acc);\n    }",
+     _pins_combine),
 ]
 
 
