@@ -197,6 +197,33 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
                                           "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
                                           "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     log("dense GEMM and gate done")
+
+    # after routing, at the routing workload (M=8192, K=D=2048, E=256, k=8):
+    # grouping by expert, the bf16 activation gather into grouped order, and
+    # the combine of bf16 expert outputs with the gated bf16 shared expert
+    Mr = xd.shape[0]
+    Pr = Mr * TOPK
+    ids_r, w_r, _, _ = dr.route(xd, Wd, TOPK, logits=False, margins=False)
+    ms, ms_e = timed(lambda: dr.moe_permute(ids_r, E))
+    suite["moe_permute_M8192_k8_E256"] = {"us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2)}
+    _, rows_r, pos_r = dr.moe_permute(ids_r, E)
+    xb_r = xd.to(torch.bfloat16)
+    ms, ms_e = timed(lambda: (dr.moe_gather(xb_r, rows_r),))
+    byt = 2 * Pr * K * 2 + Pr * 4
+    suite["moe_gather_bf16_P65536_D2048"] = {"us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2),
+                                             "gbs": round(byt / (ms * 1e-3) / 1e9, 1),
+                                             "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)  # noqa: E731
+    y_r = bf(wl.moe_expert_out_bits(Pr, K))
+    sh_r = bf(wl.moe_shared_out_bits(Mr, K))
+    _, gate_r = dr.gate_dot(xb_r, bf(wl.moe_gate_w_bits(K)))
+    ms, ms_e = timed(lambda: (dr.moe_combine(y_r, w_r, ids_r, pos_r, sh_r, gate_r),))
+    byt = Pr * K * 2 + Mr * K * 2 + Mr * K * 4 + Pr * 12 + Mr * 4
+    suite["moe_combine_bf16_M8192_k8_D2048_shared"] = {
+        "us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2),
+        "gbs": round(byt / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del y_r, sh_r, xb_r
+    log("permute, gather, combine done")
     return suite
 
 

@@ -38,7 +38,8 @@ MARGIN_DTYPE = np.dtype(
 
 EXPORTED = (
     "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
-    "dr_gate_dot", "dr_gemm_bf16", "dr_contract", "dr_status_string", "dr_last_error",
+    "dr_gate_dot", "dr_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_contract",
+    "dr_status_string", "dr_last_error",
 )
 
 
@@ -80,6 +81,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dr_gate_dot.restype = ctypes.c_int
     L.dr_gemm_bf16.argtypes = [P, P, P, i64, i64, i64, P]
     L.dr_gemm_bf16.restype = ctypes.c_int
+    L.dr_moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P]
+    L.dr_moe_permute.restype = ctypes.c_int
+    L.dr_moe_gather.argtypes = [P, ctypes.c_int, i64, i64, P, i64, P, P]
+    L.dr_moe_gather.restype = ctypes.c_int
+    L.dr_moe_combine.argtypes = [P, ctypes.c_int, i64, P, P, P, P, ctypes.c_int, P, i64, i32, i64, P, P]
+    L.dr_moe_combine.restype = ctypes.c_int
     L.dr_contract.argtypes = [ctypes.POINTER(_Contract)]
     L.dr_contract.restype = None
     L.dr_status_string.argtypes = [ctypes.c_int]
@@ -223,6 +230,62 @@ def gate_dot(x, w, *, dot: bool = True, gate: bool = True):
                        DR_F32 if w.dtype == torch.float32 else DR_BF16, _ptr(d), _ptr(g), M, K, _stream(x.device))
     _check(st, "dr_gate_dot")
     return d, g
+
+
+def moe_permute(ids, E: int, out=None):
+    """dr_moe_permute: ids [M,k] int32 -> (offsets [E+1], rows [M*k], pos [M,k]), int32 device tensors."""
+    L = load_library()
+    _dev_tensor(ids, "ids", (torch.int32,))
+    if ids.dim() != 2:
+        raise ValueError("ids must be [M,k]")
+    M, k = ids.shape
+    dev = ids.device
+    if out is not None:
+        offsets, rows, pos = out
+    else:
+        offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        rows = torch.empty((M * k,), dtype=torch.int32, device=dev)
+        pos = torch.empty((M, k), dtype=torch.int32, device=dev)
+    st = L.dr_moe_permute(_ptr(ids), M, k, E, _ptr(offsets), _ptr(rows), _ptr(pos), _stream(dev))
+    _check(st, "dr_moe_permute")
+    return offsets, rows, pos
+
+
+def moe_gather(x, rows, out=None):
+    """dr_moe_gather: x [M,D] float32 or bfloat16, rows [P] int32 -> xp [P,D] with xp[p] = x[rows[p]]."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
+    _dev_tensor(rows, "rows", (torch.int32,))
+    M, D = x.shape
+    P = rows.numel()
+    xp = out if out is not None else torch.empty((P, D), dtype=x.dtype, device=x.device)
+    st = L.dr_moe_gather(_ptr(x), DR_F32 if x.dtype == torch.float32 else DR_BF16, M, D, _ptr(rows), P,
+                         _ptr(xp), _stream(x.device))
+    _check(st, "dr_moe_gather")
+    return xp
+
+
+def moe_combine(y, weights, ids, pos, shared=None, gate=None, out=None):
+    """dr_moe_combine: y [P,D] float32 or bfloat16, weights [M,k] float32, ids and
+    pos [M,k] int32, optional shared [M,D] with gate [M] -> out [M,D] float32."""
+    L = load_library()
+    _dev_tensor(y, "y", (torch.float32, torch.bfloat16))
+    _dev_tensor(weights, "weights", (torch.float32,))
+    _dev_tensor(ids, "ids", (torch.int32,))
+    _dev_tensor(pos, "pos", (torch.int32,))
+    P, D = y.shape
+    M, k = ids.shape
+    sdt = DR_F32
+    if shared is not None:
+        _dev_tensor(shared, "shared", (torch.float32, torch.bfloat16))
+        _dev_tensor(gate, "gate", (torch.float32,))
+        sdt = DR_F32 if shared.dtype == torch.float32 else DR_BF16
+    o = out if out is not None else torch.empty((M, D), dtype=torch.float32, device=y.device)
+    st = L.dr_moe_combine(_ptr(y), DR_F32 if y.dtype == torch.float32 else DR_BF16, P, _ptr(weights), _ptr(ids),
+                          _ptr(pos), _ptr(shared), sdt, _ptr(gate) if shared is not None else None, M, k, D,
+                          _ptr(o), _stream(y.device))
+    _check(st, "dr_moe_combine")
+    return o
 
 
 def gemm_bf16(x, W, out=None):

@@ -219,6 +219,54 @@ dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t
                        "gemm launch");
 }
 
+dr_status dr_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
+                         int32_t *rows, int32_t *pos, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || k < 1 || E < 1) return fail(DR_ERR_INVALID, "bad sizes");
+  if (!offsets || (M > 0 && (!ids || !rows || !pos))) return fail(DR_ERR_INVALID, "ids, offsets, rows and pos are required");
+  if (!aligned16(ids) || !aligned16(offsets) || !aligned16(rows) || !aligned16(pos))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (k > 32 || E > 1024 || M > INT32_MAX / k)
+    return fail(DR_ERR_UNSUPPORTED, "dr_moe_permute needs k <= 32, E <= 1024 and M*k < 2^31");
+  return device_status(drk::launch_moe_permute(ids, M, k, E, offsets, rows, pos, static_cast<hipStream_t>(stream)),
+                       "moe_permute launch");
+}
+
+dr_status dr_moe_gather(const void *x, dr_dtype dtype, int64_t M, int64_t D, const int32_t *rows,
+                        int64_t P, void *xp, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || D < 1 || P < 0) return fail(DR_ERR_INVALID, "bad sizes");
+  if (dtype != DR_F32 && dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad dtype");
+  if (P > 0 && (!x || !rows || !xp)) return fail(DR_ERR_INVALID, "x, rows and xp are required");
+  if (!aligned16(x) || !aligned16(rows) || !aligned16(xp)) return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (P > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "P must be below 2^31");
+  if (P == 0) return DR_OK;
+  return device_status(drk::launch_moe_gather(x, M, D * (dtype == DR_BF16 ? 2 : 4), rows, P, xp,
+                                              static_cast<hipStream_t>(stream)),
+                       "moe_gather launch");
+}
+
+dr_status dr_moe_combine(const void *y, dr_dtype y_dtype, int64_t P, const float *weights,
+                         const int32_t *ids, const int32_t *pos, const void *shared,
+                         dr_dtype shared_dtype, const float *gate, int64_t M, int32_t k, int64_t D,
+                         float *out, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || k < 1 || D < 1 || P < 0 || (M > 0 && P < 1)) return fail(DR_ERR_INVALID, "bad sizes");
+  if (y_dtype != DR_F32 && y_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad y_dtype");
+  if (shared && shared_dtype != DR_F32 && shared_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad shared_dtype");
+  if (M > 0 && (!y || !weights || !ids || !pos || !out)) return fail(DR_ERR_INVALID, "y, weights, ids, pos and out are required");
+  if (shared && !gate) return fail(DR_ERR_INVALID, "gate is required with shared");
+  if (!aligned16(y) || !aligned16(weights) || !aligned16(ids) || !aligned16(pos) || !aligned16(shared) ||
+      !aligned16(gate) || !aligned16(out))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (k > 32 || M > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "dr_moe_combine needs k <= 32 and M < 2^31");
+  if (M == 0) return DR_OK;
+  return device_status(drk::launch_moe_combine(y, y_dtype == DR_BF16, P, weights, ids, pos, shared,
+                                               shared && shared_dtype == DR_BF16, gate, M, k, D, out,
+                                               static_cast<hipStream_t>(stream)),
+                       "moe_combine launch");
+}
+
 void dr_contract(dr_contract_info *out) {
   if (!out) return;
   out->version = 1;

@@ -24,6 +24,14 @@ struct RouteLaunch {
   hipStream_t stream;
 };
 
+hipError_t launch_moe_permute(const int32_t *ids, int64_t M, int k, int E, int32_t *offsets, int32_t *rows,
+                              int32_t *pos, hipStream_t stream);
+hipError_t launch_moe_gather(const void *x, int64_t Mx, int64_t row_bytes, const int32_t *rows, int64_t P,
+                             void *xp, hipStream_t stream);
+hipError_t launch_moe_combine(const void *y, int y_bf16, int64_t P, const float *weights, const int32_t *ids,
+                              const int32_t *pos, const void *shared, int shared_bf16, const float *gate,
+                              int64_t M, int k, int64_t D, float *out, hipStream_t stream);
+
 // Compute units of the current device (256 if the query fails).
 int device_cus();
 

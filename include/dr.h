@@ -186,6 +186,67 @@ dr_status dr_gate_dot(const void *x, dr_dtype x_dtype, const void *w, dr_dtype w
 dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K,
                        int64_t N, void *stream);
 
+/*
+ * ---- After routing: token permutation and the MoE combine ----
+ *
+ * vllm.cpp PR #2556, section "Why a value tap could never have said this":
+ * the engine's MoE combine is order-invariant over a token's k slots, and the
+ * assembled per-slot expert outputs are one axis of the MoE block (its table
+ * in section "The measurement").  The pages stop there; the readings below
+ * fix the grouping order and the combine's arithmetic so that both are
+ * functions of a token's own routing alone.
+ *
+ * All pointers are caller-owned device memory, 16-byte aligned (else
+ * DR_ERR_INVALID); nothing is allocated, kept or synchronised; argument
+ * errors are reported before any launch.
+ */
+
+/*
+ * dr_moe_permute -- group a route's M*k assignments (token m, slot j) ->
+ * expert ids[m,j] by expert: experts ascending, and within an expert tokens
+ * ascending (the stable grouping in token order).
+ *   ids [M,k] int32, each row k distinct experts in [0,E) (as dr_route
+ *     writes them).
+ *   offsets [E+1] int32 out: expert e owns grouped rows [offsets[e],
+ *     offsets[e+1]); offsets[E] = M*k.
+ *   rows [M*k] int32 out: rows[p] = the token of grouped row p.
+ *   pos [M,k] int32 out: pos[m,j] = the grouped row of assignment (m,j).
+ * 1 <= k <= 32, 1 <= E <= 1024 and M*k < 2^31, else DR_ERR_UNSUPPORTED.
+ * M == 0 still writes offsets (all zero).  An id outside [0,E) gets pos -1
+ * and no grouped row; a row repeating an expert gets in-range but
+ * unspecified positions.  Cost: each workgroup of 1024 tokens reads all M*k
+ * ids once (quadratic in M; ~1 us per 8192 tokens at k = 8).
+ */
+dr_status dr_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
+                         int32_t *rows, int32_t *pos, void *stream);
+
+/*
+ * dr_moe_gather -- xp[p,:] = x[rows[p],:] for p in [0,P): activations in the
+ * grouped order, copied bit for bit.
+ *   x [M,D] of dtype (f32 or bf16 bits), rows [P] int32, xp [P,D] same dtype.
+ *   A rows entry outside [0,M) gives a zero row.  P < 2^31.
+ */
+dr_status dr_moe_gather(const void *x, dr_dtype dtype, int64_t M, int64_t D, const int32_t *rows,
+                        int64_t P, void *xp, void *stream);
+
+/*
+ * dr_moe_combine -- out[m,d] from token m's k slots, independent of their
+ * order: the slots are taken in ascending expert id (ascending slot index
+ * between equal ids) and
+ *   acc = +0; for each slot s in that order: acc = fmaf(w[m,s], y[pos[m,s],d], acc)
+ * then, with shared given, acc = fmaf(gate[m], shared[m,d], acc); out = acc.
+ *   y [P,D] f32 or bf16 (the expert outputs in grouped order), weights [M,k]
+ *   f32, ids [M,k] and pos [M,k] int32 (as dr_route and dr_moe_permute write
+ *   them), shared [M,D] f32 or bf16 or NULL, gate [M] f32 (required with
+ *   shared; dr_gate_dot's gate), out [M,D] f32.
+ *   1 <= k <= 32, D >= 1, P >= 1 when M > 0.  A pos entry outside [0,P)
+ *   leaves its slot out (outside the contract; nothing is read past y).
+ */
+dr_status dr_moe_combine(const void *y, dr_dtype y_dtype, int64_t P, const float *weights,
+                         const int32_t *ids, const int32_t *pos, const void *shared,
+                         dr_dtype shared_dtype, const float *gate, int64_t M, int32_t k, int64_t D,
+                         float *out, void *stream);
+
 void dr_contract(dr_contract_info *out);
 const char *dr_status_string(dr_status s);
 /* Text of the last failure on the calling thread ("" if none). */

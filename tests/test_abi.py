@@ -123,6 +123,35 @@ def test_gate_and_gemm_reject(L):
     assert L.dr_gemm_bf16(P(A), P(A), P(A), 0, 64, 128, None) == OK
 
 
+def test_moe_calls_reject(L):
+    P = ctypes.c_void_p
+    # dr_moe_permute(ids, M, k, E, offsets, rows, pos, stream); M == 0 still launches (offsets)
+    assert L.dr_moe_permute(P(A), 4, 0, 8, P(A), P(A), P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A), 4, 2, 0, P(A), P(A), P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A), -1, 2, 8, P(A), P(A), P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A), 4, 2, 8, None, P(A), P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A), 4, 2, 8, P(A), None, P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A + 4), 4, 2, 8, P(A), P(A), P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A), 4, 33, 64, P(A), P(A), P(A), None) == UNSUPPORTED
+    assert L.dr_moe_permute(P(A), 4, 2, 1025, P(A), P(A), P(A), None) == UNSUPPORTED
+    assert L.dr_moe_permute(P(A), 1 << 31, 1, 8, P(A), P(A), P(A), None) == UNSUPPORTED
+    assert L.dr_moe_permute(P(A), 1 << 30, 2, 8, P(A), P(A), P(A), None) == UNSUPPORTED
+    # dr_moe_gather(x, dtype, M, D, rows, P, xp, stream)
+    assert L.dr_moe_gather(P(A), 0, 4, 0, P(A), 8, P(A), None) == INVALID
+    assert L.dr_moe_gather(P(A), 7, 4, 16, P(A), 8, P(A), None) == INVALID
+    assert L.dr_moe_gather(None, 0, 4, 16, P(A), 8, P(A), None) == INVALID
+    assert L.dr_moe_gather(P(A), 0, 4, 16, P(A), 1 << 31, P(A), None) == UNSUPPORTED
+    assert L.dr_moe_gather(P(A), 0, 4, 16, P(A), 0, P(A), None) == OK
+    # dr_moe_combine(y, ydt, P, w, ids, pos, shared, sdt, gate, M, k, D, out, stream)
+    assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 4, 0, 16, P(A), None) == INVALID
+    assert L.dr_moe_combine(P(A), 0, 0, P(A), P(A), P(A), None, 0, None, 4, 2, 16, P(A), None) == INVALID
+    assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), P(A), 0, None, 4, 2, 16, P(A), None) == INVALID
+    assert L.dr_moe_combine(P(A), 3, 8, P(A), P(A), P(A), None, 0, None, 4, 2, 16, P(A), None) == INVALID
+    assert L.dr_moe_combine(P(A), 0, 8, P(A), None, P(A), None, 0, None, 4, 2, 16, P(A), None) == INVALID
+    assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 4, 33, 16, P(A), None) == UNSUPPORTED
+    assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 0, 2, 16, P(A), None) == OK
+
+
 def test_auto_variant_is_a_function_of_shape(L):
     picks = [dr.auto_variant(M, 2048, 256, logits=False) for M in range(19, 81)]
     assert picks[0] == "rowwise" and picks[-1] == "tiled"

@@ -178,3 +178,31 @@ def dense_w_bits(K: int = DENSE_K, N: int = DENSE_N) -> np.ndarray:
 
 def gate_w_bits(K: int = DENSE_K) -> np.ndarray:
     return to_bf16_bits(normal_f32(rng(SEED_DENSE + 2), (K,), W_STD))
+
+
+# ---- after routing: expert outputs for the combine (stand-ins; no trained
+# experts exist here).  D is the model width, the router's K.
+SEED_MOE = 8000
+
+
+def moe_expert_out_bits(P: int, D: int = 2048, seed: int = SEED_MOE) -> np.ndarray:
+    """Per-slot expert outputs y [P,D] in grouped order, bf16 bits, N(0,1)."""
+    return to_bf16_bits(normal_f32(rng(seed), (P, D)))
+
+
+def moe_shared_out_bits(M: int, D: int = 2048, seed: int = SEED_MOE + 1) -> np.ndarray:
+    """Shared-expert outputs [M,D], bf16 bits, N(0,1)."""
+    return to_bf16_bits(normal_f32(rng(seed), (M, D)))
+
+
+def moe_gate_w_bits(D: int = 2048, seed: int = SEED_MOE + 2) -> np.ndarray:
+    """Shared-expert gate vector [D], bf16 bits, N(0, 0.02)."""
+    return to_bf16_bits(normal_f32(rng(seed), (D,), W_STD))
+
+
+def random_routes(M: int, k: int, E: int, seed: int) -> np.ndarray:
+    """ids [M,k]: k distinct experts per token, uniformly drawn (rank order is
+    irrelevant to grouping and combine)."""
+    g = rng(seed)
+    keys = g.random((M, E))
+    return np.argsort(keys, axis=1, kind="stable")[:, :k].astype(np.int32)
