@@ -58,6 +58,8 @@ def bind(path: str) -> ctypes.CDLL:
     L.dro_gate_dot.restype = None
     L.dro_gemm_bf16_ref.argtypes = [P, P, P, i64, i64, i64, c_int]
     L.dro_gemm_bf16_ref.restype = None
+    L.dro_grouped_gemm_bf16_ref.argtypes = [P, i64, P, P, P, i64, i64, i64, i64, P, c_int]
+    L.dro_grouped_gemm_bf16_ref.restype = c_int
     L.dro_moe_permute.argtypes = [P, i64, i32, i32, P, P, P]
     L.dro_moe_permute.restype = c_int
     L.dro_moe_gather.argtypes = [P, i64, P, i64, i64, P]
@@ -241,4 +243,22 @@ def moe_combine(y, weights, ids, pos, shared=None, gate=None, nthreads: int = 0)
                                _ptr(gate) if shared is not None else None, M, k, D, _ptr(out), nthreads)
     if rc != 0:
         raise ValueError("dro_moe_combine rejected its arguments")
+    return out
+
+
+def grouped_gemm_bf16_ref(x_bits, W_bits, offsets, rows=None, nthreads: int = 0):
+    """dro_grouped_gemm_bf16_ref: x [Mx,K] bf16 bits, W [E,K,N] bf16 bits,
+    offsets [E+1], optional rows [P] -> out [P,N] f32 (P = offsets[E])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    W = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E, K, N = W.shape
+    Mx = x.shape[0]
+    P = int(offsets[-1])
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int32)
+    out = np.empty((P, N), dtype=np.float32)
+    rc = lib().dro_grouped_gemm_bf16_ref(_ptr(x), Mx, _ptr(r), _ptr(W), _ptr(offsets), E, P, K, N, _ptr(out),
+                                         nthreads)
+    if rc != 0:
+        raise ValueError("dro_grouped_gemm_bf16_ref rejected its arguments")
     return out

@@ -267,6 +267,8 @@ struct job {
   const uint16_t *xb, *Wb;
   int64_t N;
   float *out;
+  /* grouped gemm */
+  const int32_t *src_rows, *expert_of;
 };
 
 typedef struct {
@@ -494,6 +496,49 @@ void dro_gemm_bf16_ref(const uint16_t *x, const uint16_t *W, float *out, int64_t
   j.Wb = W;
   j.out = out;
   run_rows(&j, nthreads);
+}
+
+/* Row p of the grouped product: expert e = expert_of[p], source row
+ * src_rows[p] (or p), the same plain definition as gemm_row with W[e]. */
+static void grouped_row(job_t *j, int64_t p, void *scratch) {
+  (void)scratch;
+  const int64_t e = j->expert_of[p];
+  const int64_t r = j->src_rows ? j->src_rows[p] : p;
+  const uint16_t *We = j->Wb + e * j->K * j->N;
+  for (int64_t n = 0; n < j->N; ++n) {
+    double s = 0.0;
+    for (int64_t kk = 0; kk < j->K; ++kk)
+      s += (double)bf16_widen(j->xb[r * j->K + kk]) * (double)bf16_widen(We[kk * j->N + n]);
+    j->out[p * j->N + n] = (float)s;
+  }
+}
+
+int dro_grouped_gemm_bf16_ref(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                              const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
+                              float *out, int nthreads) {
+  if (E < 1 || P < 0 || K < 1 || N < 1 || offsets[0] != 0 || offsets[E] != P) return 1;
+  for (int64_t e = 0; e < E; ++e)
+    if (offsets[e + 1] < offsets[e]) return 1;
+  for (int64_t p = 0; p < P; ++p)
+    if (rows ? (rows[p] < 0 || rows[p] >= Mx) : (p >= Mx)) return 1;
+  int32_t *expert_of = (int32_t *)malloc(sizeof(int32_t) * (size_t)(P > 0 ? P : 1));
+  if (!expert_of) return 1;
+  for (int64_t e = 0; e < E; ++e)
+    for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) expert_of[p] = (int32_t)e;
+  job_t j;
+  memset(&j, 0, sizeof(j));
+  j.fn = grouped_row;
+  j.M = P;
+  j.K = K;
+  j.N = N;
+  j.xb = x;
+  j.Wb = W;
+  j.out = out;
+  j.src_rows = rows;
+  j.expert_of = expert_of;
+  run_rows(&j, nthreads);
+  free(expert_of);
+  return 0;
 }
 
 /* ------------------------------------------------- permutation, combine */

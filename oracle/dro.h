@@ -111,6 +111,22 @@ void dro_gate_dot(const void *x, int x_is_bf16, const void *w, int w_is_bf16, in
 void dro_gemm_bf16_ref(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
                        int64_t K, int64_t N, int nthreads);
 
+/* Grouped expert GEMM reference: for each expert e and each grouped row p in
+ * [offsets[e], offsets[e+1]), out[p,n] = sum_k x[r,k] * W[e,k,n] with
+ * r = rows[p] (or p when rows is NULL), evaluated like dro_gemm_bf16_ref
+ * (bf16 inputs, fp64 sum in k order, one rounding to fp32).  x is [Mx,K],
+ * W is [E,K,N] (bf16 bits), out is [P,N].  vllm.cpp PR #2556, section "The
+ * measurement", finds the grouped expert GEMM, not the router, to be where
+ * two arms' MoE outputs part; a batch-invariant one must give every row the
+ * same bits whatever the size and position of its group ("The Illusion of
+ * Determinism in Disaggregated Inference", section "The arithmetic cost of
+ * batch-invariant kernels").  This reference is the plain definition the
+ * matrix-core path is compared to within a tolerance.  Returns nonzero on
+ * inconsistent offsets or a source row outside [0,Mx). */
+int dro_grouped_gemm_bf16_ref(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                              const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
+                              float *out, int nthreads);
+
 /* ---- The step after routing: token permutation and the MoE combine ----
  *
  * Source: vllm.cpp PR #2556, section "Why a value tap could never have said

@@ -7,7 +7,9 @@ answer is known in closed form.  The combine is pinned by exact-rational
 recomputation of every fmaf on tiny inputs, by its defining property (the
 result does not depend on the order of a token's k slots; vllm.cpp PR #2556,
 section "Why a value tap could never have said this"), by integer inputs whose
-sums are exact, and by the sign of an all-zero sum.
+sums are exact, and by the sign of an all-zero sum.  The grouped expert GEMM
+reference is pinned per group to numpy's float64 matmul, to exact integer
+products, and to its own pre-gathered form.
 """
 import numpy as np
 import pytest
@@ -199,3 +201,56 @@ def test_combine_rejects_bad_positions():
     with pytest.raises(ValueError):
         oracle.moe_combine(np.zeros((2, 3), np.float32), np.ones((1, 2), np.float32),
                            np.array([[0, 1]], np.int32), np.array([[0, 2]], np.int32))
+
+
+# ---- grouped expert GEMM reference
+
+def _bf16_bits(a):
+    import workloads as wl
+    return wl.to_bf16_bits(np.asarray(a, dtype=np.float32))
+
+
+def _widen(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def test_grouped_gemm_ref_matches_numpy_per_group():
+    rng = np.random.default_rng(21)
+    E, K, N, Mx = 5, 96, 40, 30
+    counts = np.array([7, 0, 12, 1, 20])
+    offsets = np.r_[0, np.cumsum(counts)].astype(np.int32)
+    P = int(offsets[-1])
+    x = _bf16_bits(rng.standard_normal((Mx, K)))
+    W = _bf16_bits(rng.standard_normal((E, K, N)) * 0.1)
+    rows = rng.integers(0, Mx, P).astype(np.int32)
+    got = oracle.grouped_gemm_bf16_ref(x, W, offsets, rows)
+    for e in range(E):
+        seg = slice(offsets[e], offsets[e + 1])
+        want = (_widen(x)[rows[seg]].astype(np.float64) @ _widen(W[e]).astype(np.float64)).astype(np.float32)
+        assert np.allclose(got[seg], want, rtol=1e-6, atol=1e-6)
+
+
+def test_grouped_gemm_ref_exact_on_integers_and_rows_equal_pregathered():
+    rng = np.random.default_rng(22)
+    E, K, N, Mx = 3, 64, 16, 9
+    offsets = np.array([0, 4, 4, 11], np.int32)
+    x = _bf16_bits(rng.integers(-8, 8, (Mx, K)))
+    W = _bf16_bits(rng.integers(-8, 8, (E, K, N)))
+    rows = rng.integers(0, Mx, 11).astype(np.int32)
+    got = oracle.grouped_gemm_bf16_ref(x, W, offsets, rows)
+    xi = _widen(x).astype(np.int64)
+    Wi = _widen(W).astype(np.int64)
+    for e in range(E):
+        for p in range(offsets[e], offsets[e + 1]):
+            assert np.array_equal(got[p].astype(np.int64), xi[rows[p]] @ Wi[e])
+    pre = oracle.grouped_gemm_bf16_ref(np.ascontiguousarray(x[rows]), W, offsets)
+    assert np.array_equal(pre.view(np.uint32), got.view(np.uint32))
+
+
+def test_grouped_gemm_ref_rejects_inconsistent_offsets():
+    x = np.zeros((4, 32), np.uint16)
+    W = np.zeros((2, 32, 8), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_bf16_ref(x, W, np.array([0, 3, 2], np.int32))
+    with pytest.raises(ValueError):
+        oracle.grouped_gemm_bf16_ref(x, W, np.array([0, 2, 4], np.int32), rows=np.array([0, 1, 2, 9], np.int32))

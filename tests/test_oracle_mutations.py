@@ -89,6 +89,11 @@ def _pins_combine():
     tmoe.test_combine_ascending_expert_order_is_distinguished()
 
 
+def _pins_grouped():
+    tmoe.test_grouped_gemm_ref_matches_numpy_per_group()
+    tmoe.test_grouped_gemm_ref_exact_on_integers_and_rows_equal_pregathered()
+
+
 # (name, text in dro.c, replacement, pins that must catch it)
 MUTATIONS = [
     ("tie_break_highest_index",
@@ -159,6 +164,14 @@ MUTATIONS = [
      "      acc = fmaf(c->weights[m * k + s], yv, acc);",
      "      acc = acc + c->weights[m * k + s] * yv;",
      _pins_combine),
+    ("grouped_next_expert",
+     "    for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) expert_of[p] = (int32_t)e;",
+     "    for (int64_t p = offsets[e]; p < offsets[e + 1]; ++p) expert_of[p] = (int32_t)((e + 1) % E);",
+     _pins_grouped),
+    ("grouped_ignores_rows",
+     "  const int64_t r = j->src_rows ? j->src_rows[p] : p;",
+     "  const int64_t r = p < j->K ? p : 0;",
+     _pins_grouped),
     ("combine_shared_first",
      "    float acc = 0.0f;\n    for (int32_t i = 0; i < k; ++i) {\n      int32_t s = order[i];\n      float yv = elem_at(c->y, c->y_is_bf16, (int64_t)c->pos[m * k + s] * c->D + d);\n      acc = fmaf(c->weights[m * k + s], yv, acc);\n    }\n    if (c->shared) acc = fmaf(c->gate[m], elem_at(c->shared, c->shared_is_bf16, m * c->D + d), acc);",
      "    float acc = 0.0f;\n    if (c->shared) acc = fmaf(c->gate[m], elem_at(c->shared, c->shared_is_bf16, m * c->D + d), acc);\n    for (int32_t i = 0; i < k; ++i) {\n      int32_t s = order[i];\n      float yv = elem_at(c->y, c->y_is_bf16, (int64_t)c->pos[m * k + s] * c->D + d);\n      acc = fmaf(c->weights[m * k + s], yv, acc);\n    }",
