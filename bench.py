@@ -222,8 +222,26 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
     suite["moe_combine_bf16_M8192_k8_D2048_shared"] = {
         "us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2),
         "gbs": round(byt / (ms * 1e-3) / 1e9, 1), "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
-    del y_r, sh_r, xb_r
+    del y_r, sh_r
     log("permute, gather, combine done")
+
+    # grouped expert GEMM on the same routes: 65536 grouped rows, E=256
+    # experts of K=2048 x N=1024 bf16 weights (1 GiB, drawn on the device from
+    # a seeded generator), x read through the grouped rows (fused gather)
+    Ng = 1024
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.SEED_MOE + 4)
+    Wg = (torch.randn((E, K, Ng), device=dev, generator=gen) * float(wl.W_STD)).to(torch.bfloat16)
+    off_r, rows_r, _ = dr.moe_permute(ids_r, E)
+    ms, ms_e = timed(lambda: (dr.grouped_gemm_bf16(xb_r, Wg, off_r, rows_r),), steps=10)
+    fl = 2.0 * Pr * K * Ng
+    byt = E * K * Ng * 2 + Mr * K * 2 + Pr * Ng * 4
+    suite["grouped_gemm_bf16_P65536_K2048_N1024_E256"] = {
+        "us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2), "tflops": round(fl / (ms * 1e-3) / 1e12, 2),
+        "frac_bf16_peak": round(fl / (ms * 1e-3) / 1e12 / PEAK_BF16_MATRIX_TFLOPS, 4),
+        "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+    del Wg, xb_r
+    log("grouped expert GEMM done")
     return suite
 
 

@@ -38,7 +38,7 @@ MARGIN_DTYPE = np.dtype(
 
 EXPORTED = (
     "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
-    "dr_gate_dot", "dr_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_contract",
+    "dr_gate_dot", "dr_gemm_bf16", "dr_grouped_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_contract",
     "dr_status_string", "dr_last_error",
 )
 
@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dr_gate_dot.restype = ctypes.c_int
     L.dr_gemm_bf16.argtypes = [P, P, P, i64, i64, i64, P]
     L.dr_gemm_bf16.restype = ctypes.c_int
+    L.dr_grouped_gemm_bf16.argtypes = [P, i64, P, P, P, i64, i64, i64, i64, P, P]
+    L.dr_grouped_gemm_bf16.restype = ctypes.c_int
     L.dr_moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P]
     L.dr_moe_permute.restype = ctypes.c_int
     L.dr_moe_gather.argtypes = [P, ctypes.c_int, i64, i64, P, i64, P, P]
@@ -285,6 +287,31 @@ def moe_combine(y, weights, ids, pos, shared=None, gate=None, out=None):
                           _ptr(pos), _ptr(shared), sdt, _ptr(gate) if shared is not None else None, M, k, D,
                           _ptr(o), _stream(y.device))
     _check(st, "dr_moe_combine")
+    return o
+
+
+def grouped_gemm_bf16(x, W, offsets, rows=None, out=None):
+    """dr_grouped_gemm_bf16: x [Mx,K] bfloat16, W [E,K,N] bfloat16, offsets
+    [E+1] int32, rows [P] int32 or None (then P = Mx) -> out [P,N] float32."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.bfloat16,))
+    _dev_tensor(W, "W", (torch.bfloat16,))
+    _dev_tensor(offsets, "offsets", (torch.int32,))
+    Mx, K = x.shape
+    E, K2, N = W.shape
+    if K != K2:
+        raise ValueError("inner sizes differ")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must have E+1 entries")
+    if rows is not None:
+        _dev_tensor(rows, "rows", (torch.int32,))
+        P = rows.numel()
+    else:
+        P = Mx
+    o = out if out is not None else torch.empty((P, N), dtype=torch.float32, device=x.device)
+    st = L.dr_grouped_gemm_bf16(_ptr(x), Mx, _ptr(rows), _ptr(W), _ptr(offsets), E, P, K, N, _ptr(o),
+                                _stream(x.device))
+    _check(st, "dr_grouped_gemm_bf16")
     return o
 
 

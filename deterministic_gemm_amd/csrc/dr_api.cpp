@@ -219,6 +219,25 @@ dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t
                        "gemm launch");
 }
 
+dr_status dr_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                               const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
+                               float *out, void *stream) {
+  g_last_error[0] = '\0';
+  if (Mx < 0 || P < 0 || K < 1 || N < 1 || E < 1) return fail(DR_ERR_INVALID, "bad sizes");
+  if (!offsets || (P > 0 && (!x || !W || !out))) return fail(DR_ERR_INVALID, "x, W, offsets and out are required");
+  if (!rows && P > Mx) return fail(DR_ERR_INVALID, "without rows, x must hold the P grouped rows");
+  if (!aligned16(x) || !aligned16(rows) || !aligned16(W) || !aligned16(offsets) || !aligned16(out))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (K % 32 != 0 || N % 128 != 0) return fail(DR_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 128");
+  if (E > 1024 || P > INT32_MAX || Mx > INT32_MAX || K > (int64_t(1) << 30) || N > (int64_t(1) << 30) ||
+      (P + 127) / 128 + E > 65535)
+    return fail(DR_ERR_UNSUPPORTED, "size out of range");
+  if (P == 0) return DR_OK;
+  return device_status(drk::launch_grouped_gemm_bf16(x, Mx, rows, W, offsets, E, P, K, N, out,
+                                                     static_cast<hipStream_t>(stream)),
+                       "grouped gemm launch");
+}
+
 dr_status dr_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
                          int32_t *rows, int32_t *pos, void *stream) {
   g_last_error[0] = '\0';

@@ -66,9 +66,29 @@ struct GemmCfg {
   }
 };
 
+// Source row of each of this lane's x transfers (the same rows every stage):
+// tile row r -> output row m0 + r, read from x row rows[m0 + r] (or m0 + r),
+// or -1 past the tile's last row [mend) or for a source outside [0, Mx).
 template <class C>
-__device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const uint16_t *__restrict__ W,
-                                           int64_t M, int K, int N, int64_t m0, int n0, int st, int nst,
+__device__ __forceinline__ void gemm_arows(const int32_t *__restrict__ rows, int64_t Mx, int64_t m0, int64_t mend,
+                                           int wave, int lane, int32_t (&arow)[C::PER]) {
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int p = (wave * C::PER + i) * 64 + lane;
+    arow[i] = -1;
+    if (p < C::AU) {
+      const int64_t g = m0 + p / C::UA;
+      if (g < mend) {
+        const int64_t r = rows ? rows[g] : g;
+        arow[i] = (r >= 0 && r < Mx) ? static_cast<int32_t>(r) : -1;
+      }
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const int32_t (&arow)[C::PER],
+                                           const uint16_t *__restrict__ W, int K, int N, int n0, int st, int nst,
                                            int wave, int lane, char *stage) {
   const int k0 = st * C::BK;
   const bool live = st < nst;
@@ -81,9 +101,8 @@ __device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const
     if (p < C::AU) {
       const int r = p / C::UA, up = p % C::UA;
       const int u = up ^ C::swa(r);
-      const int64_t m = m0 + r;
       const int k = k0 + 8 * u;
-      if (live && m < M && k < K) src = x + m * K + k;
+      if (live && arow[i] >= 0 && k < K) src = x + static_cast<int64_t>(arow[i]) * K + k;
     } else {
       const int q = p - C::AU;
       const int kr = q / C::UB, up = q % C::UB;
@@ -95,23 +114,16 @@ __device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const
   }
 }
 
+// One output tile: rows [m0, min(m0 + BM, mend)) and columns [n0, n0 + BN) of
+// out = x[rows] . W, every output reduced by the same instruction sequence.
 template <class C>
-__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
-                                                         const uint16_t *__restrict__ W,
-                                                         float *__restrict__ out, int64_t M, int K,
-                                                         int N) {
-  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
+__device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
+                                          int64_t Mx, const uint16_t *__restrict__ W, float *__restrict__ out,
+                                          int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
   constexpr int FM = C::FM, FN = C::FN, S = C::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * C::BM;
-  // Workgroups go to the eight XCDs in turn.  With a multiple of eight column
-  // tiles, XCD j takes the j-th contiguous eighth of them, so neighbouring
-  // tiles that share 128-byte lines of W read them through one L2.
-  const int nx = gridDim.x;
-  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int n0 = bx * C::BN;
   const int nst = (K + C::BK - 1) / C::BK;
 
   f32x4 acc[FM][FN];
@@ -123,16 +135,18 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
   // per-lane parts of the operand addresses
   const int ta = lane & 15;          // transpose read: source lane within its group
   const int tj = ta >> 2, tq = ta & 3;
+  int32_t arow[C::PER];
+  gemm_arows<C>(rows, Mx, m0, mend, wave, lane, arow);
 
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i) gemm_issue<C>(x, W, M, K, N, m0, n0, i, nst, wave, lane, smem + i * C::STAGE);
+  for (int i = 0; i < S - 1; ++i) gemm_issue<C>(x, arow, W, K, N, n0, i, nst, wave, lane, smem + i * C::STAGE);
 
   for (int st = 0; st < nst; ++st) {
     compiler_fence();
     wait_vmcnt<C::PER * (S - 2)>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    gemm_issue<C>(x, W, M, K, N, m0, n0, st + S - 1, nst, wave, lane, smem + ((st + S - 1) % S) * C::STAGE);
+    gemm_issue<C>(x, arow, W, K, N, n0, st + S - 1, nst, wave, lane, smem + ((st + S - 1) % S) * C::STAGE);
     const char *As = smem + (st % S) * C::STAGE;
     const char *Bs = As + C::ABYTES;
     const int nsub = (K - st * C::BK) < C::BK ? (K - st * C::BK) / 32 : C::BK / 32;
@@ -169,7 +183,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
       }
     }
   }
-  // no transfer may still be writing this workgroup's LDS when it exits
+  // no transfer may still be writing this workgroup's LDS when it moves on
   compiler_fence();
   wait_vmcnt<0>();
 
@@ -178,10 +192,87 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t m = m0 + wm * C::TM + i * 16 + g4 * 4 + q;
-      if (m >= M) continue;
+      if (m >= mend) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) out[m * N + n0 + wn * C::TN + j * 16 + r16] = acc[i][j][q];
     }
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
+                                                         const uint16_t *__restrict__ W,
+                                                         float *__restrict__ out, int64_t M, int K,
+                                                         int N) {
+  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
+  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * C::BM;
+  // Workgroups go to the eight XCDs in turn.  With a multiple of eight column
+  // tiles, XCD j takes the j-th contiguous eighth of them, so neighbouring
+  // tiles that share 128-byte lines of W read them through one L2.
+  const int nx = gridDim.x;
+  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
+  gemm_tile<C>(x, nullptr, M, W, out, m0, M, K, N, bx * C::BN, smem);
+}
+
+// Grouped (per-expert) product: expert e owns output rows [offsets[e],
+// offsets[e+1]) and multiplies them by W[e].  Row tiles never straddle two
+// experts: expert e has ceil(count_e / BM) of them, numbered after those of
+// experts < e, and workgroup row index t (blockIdx.y) finds its expert by a
+// scan of the tile counts in LDS.  Workgroups past the last tile exit.  Every
+// output row is reduced by the dense kernel's instruction sequence, so a row
+// has the same bits whatever its group's size or position, and the same bits
+// as dr_gemm_bf16 of that row with W[e].
+constexpr int GG_EMAX = 1024;
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t *__restrict__ x, int64_t Mx,
+                                                                 const int32_t *__restrict__ rows,
+                                                                 const uint16_t *__restrict__ W,
+                                                                 const int32_t *__restrict__ offsets, int E,
+                                                                 int64_t P, float *__restrict__ out, int K, int N) {
+  constexpr int EPL = (GG_EMAX + C::NT - 1) / C::NT;  // experts per lane in the scan
+  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
+  __shared__ int32_t tstart[GG_EMAX + 1];
+  __shared__ int32_t wsum[C::NW];
+  __shared__ int32_t found;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int tile = blockIdx.y;
+  // row tiles of lane t's experts EPL*t .. EPL*t + EPL - 1, and their scan
+  int cnt[EPL], v = 0;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = EPL * t + i;
+    cnt[i] = (e < E) ? (offsets[e + 1] - offsets[e] + C::BM - 1) / C::BM : 0;
+    v += cnt[i];
+  }
+  const int mine = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) wsum[wave] = v;
+  if (t == 0) found = -1;
+  __syncthreads();
+  int start = v - mine;
+  for (int w = 0; w < wave; ++w) start += wsum[w];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = EPL * t + i;
+    if (e < E) {
+      if (tile >= start && tile < start + cnt[i]) found = e;
+      tstart[e] = start;
+    }
+    start += cnt[i];
+  }
+  __syncthreads();
+  const int e = found;
+  if (e < 0) return;  // past the last tile (uniform over the workgroup)
+  const int64_t lo = offsets[e], mend = offsets[e + 1];
+  if (lo < 0 || mend > P || mend < lo) return;  // inconsistent offsets: nothing is written outside out
+  const int64_t m0 = lo + static_cast<int64_t>(tile - tstart[e]) * C::BM;
+  const int nx = gridDim.x;
+  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
+  gemm_tile<C>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N, bx * C::BN, smem);
 }
 
 template <class C>
@@ -191,6 +282,24 @@ static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, float *out
   hipLaunchKernelGGL((gemm_bf16_kernel<C>), grid, dim3(C::NT), 0, stream, x, W, out, M, static_cast<int>(K),
                      static_cast<int>(N));
   return hipGetLastError();
+}
+
+template <class C>
+static hipError_t launch_grouped_c(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                                   const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N, float *out,
+                                   hipStream_t stream) {
+  // enough row tiles for any split of P rows over E experts
+  const int64_t tiles = (P + C::BM - 1) / C::BM + E;
+  const dim3 grid(static_cast<uint32_t>(N / C::BN), static_cast<uint32_t>(tiles));
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
+                     static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N));
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                                    const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
+                                    float *out, hipStream_t stream) {
+  return launch_grouped_c<GemmCfg<128, 128, 4, 2, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
 }
 
 // The tile is chosen from the shape (a performance choice only: every

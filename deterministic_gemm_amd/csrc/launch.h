@@ -24,6 +24,9 @@ struct RouteLaunch {
   hipStream_t stream;
 };
 
+hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                                    const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
+                                    float *out, hipStream_t stream);
 hipError_t launch_moe_permute(const int32_t *ids, int64_t M, int k, int E, int32_t *offsets, int32_t *rows,
                               int32_t *pos, hipStream_t stream);
 hipError_t launch_moe_gather(const void *x, int64_t Mx, int64_t row_bytes, const int32_t *rows, int64_t P,

@@ -247,6 +247,29 @@ dr_status dr_moe_combine(const void *y, dr_dtype y_dtype, int64_t P, const float
                          dr_dtype shared_dtype, const float *gate, int64_t M, int32_t k, int64_t D,
                          float *out, void *stream);
 
+/*
+ * dr_grouped_gemm_bf16 -- batch-invariant grouped expert GEMM on bf16 matrix
+ * cores (the expert GEMM is where two engines' MoE outputs part: vllm.cpp PR
+ * #2556, section "The measurement").  Expert e owns output rows p in
+ * [offsets[e], offsets[e+1]) and
+ *   out[p,n] = sum_k x[r,k] * W[e,k,n],  r = rows[p] (or p when rows is NULL)
+ * with fp32 accumulation.  Every output row is reduced by dr_gemm_bf16's
+ * instruction sequence, so a row's bits depend only on its x row and W[e]:
+ * not on the size or position of its group, nor on the batch, and they equal
+ * dr_gemm_bf16 of that one row with W[e].
+ *   x [Mx,K] bf16 bits (token order with rows, e.g. dr_moe_permute's rows,
+ *   which fuses the gather; grouped order without), W [E,K,N] bf16 bits,
+ *   offsets [E+1] int32 (as dr_moe_permute writes them: offsets[0] = 0,
+ *   non-decreasing, offsets[E] = P), out [P,N] fp32.
+ *   K % 32 == 0, N % 128 == 0, 1 <= E <= 1024, P < 2^31 and
+ *   ceil(P/128) + E <= 65535, else DR_ERR_UNSUPPORTED.  A rows entry outside
+ *   [0,Mx) reads a zero row.  Inconsistent offsets leave the affected rows
+ *   unwritten; nothing is written outside out.
+ */
+dr_status dr_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
+                               const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
+                               float *out, void *stream);
+
 void dr_contract(dr_contract_info *out);
 const char *dr_status_string(dr_status s);
 /* Text of the last failure on the calling thread ("" if none). */

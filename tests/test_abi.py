@@ -152,6 +152,20 @@ def test_moe_calls_reject(L):
     assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 0, 2, 16, P(A), None) == OK
 
 
+def test_grouped_gemm_rejects(L):
+    P = ctypes.c_void_p
+    # dr_grouped_gemm_bf16(x, Mx, rows, W, offsets, E, P, K, N, out, stream)
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), P(A), 0, 8, 64, 128, P(A), None) == INVALID
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), None, 4, 8, 64, 128, P(A), None) == INVALID
+    assert L.dr_grouped_gemm_bf16(P(A), 4, None, P(A), P(A), 4, 8, 64, 128, P(A), None) == INVALID  # P > Mx
+    assert L.dr_grouped_gemm_bf16(P(A + 8), 8, P(A), P(A), P(A), 4, 8, 64, 128, P(A), None) == INVALID
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), P(A), 4, 8, 48, 128, P(A), None) == UNSUPPORTED
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), P(A), 4, 8, 64, 96, P(A), None) == UNSUPPORTED
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), P(A), 1025, 8, 64, 128, P(A), None) == UNSUPPORTED
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), P(A), 4, 1 << 24, 64, 128, P(A), None) == UNSUPPORTED
+    assert L.dr_grouped_gemm_bf16(P(A), 8, P(A), P(A), P(A), 4, 0, 64, 128, P(A), None) == OK
+
+
 def test_auto_variant_is_a_function_of_shape(L):
     picks = [dr.auto_variant(M, 2048, 256, logits=False) for M in range(19, 81)]
     assert picks[0] == "rowwise" and picks[-1] == "tiled"

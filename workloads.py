@@ -206,3 +206,10 @@ def random_routes(M: int, k: int, E: int, seed: int) -> np.ndarray:
     g = rng(seed)
     keys = g.random((M, E))
     return np.argsort(keys, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+def expert_w_bits(E: int, K: int = 2048, N: int = 1024, seed: int = SEED_MOE + 3) -> np.ndarray:
+    """Expert weights W [E,K,N] for the grouped GEMM, bf16 bits, N(0, 0.02).
+    No expert width is given by the pages; N = 1024 (gate and up projections
+    of width 512 side by side) is the stand-in."""
+    return to_bf16_bits(normal_f32(rng(seed), (E, K, N), W_STD))
