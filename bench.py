@@ -150,8 +150,31 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
                      "tokens_per_s": round(m / (ms * 1e-3), 1),
                      "tflops": round(2.0 * m * 4096 * 512 / (ms * 1e-3) / 1e12, 2)})
     suite["ties_K4096_E512_k10_bf16_logits"] = ties
-    del Wt, xt
-    log("tie-heavy router done")
+
+    # the router as a plain bf16 linear layer (logits from the bf16 GEMM,
+    # rounded to bf16, then the same selection), beside the fp32 arm
+    bfr = {}
+    xtb, Wtb = xt.to(torch.bfloat16), Wt.to(torch.bfloat16)
+    ida, _, _, mga = dr.route(xt, Wt, 10, logit_dtype="bf16")
+    idb, _, _, mgb = dr.route_bf16_gemm(xtb, Wtb, 10)
+    ua, ub = dr.margins_to_numpy(mga)["ulps"], dr.margins_to_numpy(mgb)["ulps"]
+    flip = np.any(np.sort(ida.cpu().numpy(), 1) != np.sort(idb.cpu().numpy(), 1), axis=1)
+    bfr["arms_K4096_E512_k10_M4096"] = {
+        "tie_rate_fp32_arm": round(float(np.mean(ua == 0)), 4), "tie_rate_bf16_arm": round(float(np.mean(ub == 0)), 4),
+        "within_one_step_fp32_arm": round(float(np.mean(ua <= 1)), 4),
+        "within_one_step_bf16_arm": round(float(np.mean(ub <= 1)), 4),
+        "set_flip_rate": round(float(flip.mean()), 4),
+        "max_fp32_arm_ulps_at_a_flip": int(ua[flip].max()) if flip.any() else None}
+    ms, ms_e = timed(lambda: dr.route_bf16_gemm(xtb, Wtb, 10))
+    bfr["K4096_E512_k10_M4096"] = {"us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2),
+                                   "tokens_per_s": round(4096 / (ms * 1e-3), 1)}
+    xb8, Wb8 = xd.to(torch.bfloat16), Wd.to(torch.bfloat16)
+    ms, ms_e = timed(lambda: dr.route_bf16_gemm(xb8, Wb8, TOPK))
+    bfr["K2048_E256_k8_M8192"] = {"us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2),
+                                  "tokens_per_s": round(xd.shape[0] / (ms * 1e-3), 1)}
+    suite["bf16_gemm_router"] = bfr
+    del Wt, xt, xtb, Wtb, xb8, Wb8
+    log("tie-heavy router and bf16 GEMM router done")
 
     import concurrent.futures
 

@@ -38,7 +38,7 @@ MARGIN_DTYPE = np.dtype(
 
 EXPORTED = (
     "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
-    "dr_gate_dot", "dr_gemm_bf16", "dr_grouped_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_contract",
+    "dr_route_bf16_gemm", "dr_gate_dot", "dr_gemm_bf16", "dr_grouped_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_contract",
     "dr_status_string", "dr_last_error",
 )
 
@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dr_gate_dot.restype = ctypes.c_int
     L.dr_gemm_bf16.argtypes = [P, P, P, i64, i64, i64, P]
     L.dr_gemm_bf16.restype = ctypes.c_int
+    L.dr_route_bf16_gemm.argtypes = [P, P, i64, i64, i64, i32, P, P, P, P, u32, P]
+    L.dr_route_bf16_gemm.restype = ctypes.c_int
     L.dr_grouped_gemm_bf16.argtypes = [P, i64, P, P, P, i64, i64, i64, i64, P, P]
     L.dr_grouped_gemm_bf16.restype = ctypes.c_int
     L.dr_moe_permute.argtypes = [P, i64, i32, i32, P, P, P, P]
@@ -288,6 +290,28 @@ def moe_combine(y, weights, ids, pos, shared=None, gate=None, out=None):
                           _ptr(o), _stream(y.device))
     _check(st, "dr_moe_combine")
     return o
+
+
+def route_bf16_gemm(x, W, k: int, *, renormalize: bool = False, weights: bool = True, margins: bool = True):
+    """dr_route_bf16_gemm: x [M,K] bfloat16, W [K,E] bfloat16 -> (ids [M,k]
+    int32, weights [M,k] float32 or None, logits [M,E] bfloat16, margins
+    [M,4] int32 raw dr_margin records or None)."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.bfloat16,))
+    _dev_tensor(W, "W", (torch.bfloat16,))
+    M, K = x.shape
+    K2, E = W.shape
+    if K != K2:
+        raise ValueError("inner sizes differ")
+    dev = x.device
+    ids_t = torch.empty((M, k), dtype=torch.int32, device=dev)
+    w_t = torch.empty((M, k), dtype=torch.float32, device=dev) if weights else None
+    lg_t = torch.empty((M, E), dtype=torch.bfloat16, device=dev)
+    mg_t = torch.empty((M, 4), dtype=torch.int32, device=dev) if margins else None
+    st = L.dr_route_bf16_gemm(_ptr(x), _ptr(W), M, K, E, k, _ptr(ids_t), _ptr(w_t), _ptr(lg_t), _ptr(mg_t),
+                              DR_ROUTE_RENORMALIZE if renormalize else 0, _stream(dev))
+    _check(st, "dr_route_bf16_gemm")
+    return ids_t, w_t, lg_t, mg_t
 
 
 def grouped_gemm_bf16(x, W, offsets, rows=None, out=None):

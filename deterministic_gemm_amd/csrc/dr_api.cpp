@@ -219,6 +219,39 @@ dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t
                        "gemm launch");
 }
 
+dr_status dr_route_bf16_gemm(const uint16_t *x, const uint16_t *W, int64_t M, int64_t K, int64_t E,
+                             int32_t k, int32_t *ids, float *weights, uint16_t *logits, dr_margin *margins,
+                             uint32_t flags, void *stream) {
+  g_last_error[0] = '\0';
+  if (M < 0 || M > kMaxM) return fail(DR_ERR_INVALID, "M=%lld out of range", (long long)M);
+  if (K < 1 || E < 1) return fail(DR_ERR_INVALID, "bad sizes");
+  if (k < 1 || k > E) return fail(DR_ERR_INVALID, "k=%d must be in [1, E=%lld]", k, (long long)E);
+  if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
+  if (M > 0 && (!x || !W || !ids || !logits)) return fail(DR_ERR_INVALID, "x, W, ids and logits are required");
+  if (!aligned16(x) || !aligned16(W) || !aligned16(ids) || !aligned16(weights) || !aligned16(logits) ||
+      !aligned16(margins))
+    return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (K % 32 != 0 || E % 128 != 0 || !drk::select_supports(E) || K > (int64_t(1) << 30))
+    return fail(DR_ERR_UNSUPPORTED, "dr_route_bf16_gemm needs K %% 32 == 0 and E in {128, 256, 512, 1024}");
+  if (k > kMaxTopK) return fail(DR_ERR_UNSUPPORTED, "k=%d above %d", k, kMaxTopK);
+  if (M == 0) return DR_OK;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const dr_status s1 = device_status(drk::launch_gemm_bf16_out_bf16(x, W, logits, M, K, E, st), "gate gemm launch");
+  if (s1 != DR_OK) return s1;
+  drk::RouteLaunch L{};
+  L.M = M;
+  L.E = E;
+  L.k = k;
+  L.logit_bf16 = 1;
+  L.flags = flags;
+  L.ids = ids;
+  L.weights = weights;
+  L.logits = logits;
+  L.margins = margins;
+  L.stream = st;
+  return device_status(drk::launch_route_select(L), "select launch");
+}
+
 dr_status dr_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
                                const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
                                float *out, void *stream) {

@@ -114,11 +114,19 @@ __device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const
   }
 }
 
+// Round to nearest even on the 16 dropped bits (NaN -> 0x7FC0).
+__device__ __forceinline__ uint16_t gemm_f32_to_bf16(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
 // One output tile: rows [m0, min(m0 + BM, mend)) and columns [n0, n0 + BN) of
-// out = x[rows] . W, every output reduced by the same instruction sequence.
-template <class C>
+// out = x[rows] . W, every output reduced by the same instruction sequence;
+// stored as fp32, or rounded to bf16 (OutT = uint16_t).
+template <class C, class OutT = float>
 __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
-                                          int64_t Mx, const uint16_t *__restrict__ W, float *__restrict__ out,
+                                          int64_t Mx, const uint16_t *__restrict__ W, OutT *__restrict__ out,
                                           int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
   constexpr int FM = C::FM, FN = C::FN, S = C::S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -194,14 +202,17 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
       const int64_t m = m0 + wm * C::TM + i * 16 + g4 * 4 + q;
       if (m >= mend) continue;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) out[m * N + n0 + wn * C::TN + j * 16 + r16] = acc[i][j][q];
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (sizeof(OutT) == 2) out[m * N + n0 + wn * C::TN + j * 16 + r16] = gemm_f32_to_bf16(acc[i][j][q]);
+        else out[m * N + n0 + wn * C::TN + j * 16 + r16] = acc[i][j][q];
+      }
     }
 }
 
-template <class C>
+template <class C, class OutT>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ W,
-                                                         float *__restrict__ out, int64_t M, int K,
+                                                         OutT *__restrict__ out, int64_t M, int K,
                                                          int N) {
   __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * C::BM;
@@ -210,7 +221,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
   // tiles that share 128-byte lines of W read them through one L2.
   const int nx = gridDim.x;
   const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
-  gemm_tile<C>(x, nullptr, M, W, out, m0, M, K, N, bx * C::BN, smem);
+  gemm_tile<C, OutT>(x, nullptr, M, W, out, m0, M, K, N, bx * C::BN, smem);
 }
 
 // Grouped (per-expert) product: expert e owns output rows [offsets[e],
@@ -275,11 +286,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   gemm_tile<C>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N, bx * C::BN, smem);
 }
 
-template <class C>
-static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K,
+template <class C, class OutT = float>
+static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K,
                                 int64_t N, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(N / C::BN), static_cast<uint32_t>((M + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL((gemm_bf16_kernel<C>), grid, dim3(C::NT), 0, stream, x, W, out, M, static_cast<int>(K),
+  hipLaunchKernelGGL((gemm_bf16_kernel<C, OutT>), grid, dim3(C::NT), 0, stream, x, W, out, M, static_cast<int>(K),
                      static_cast<int>(N));
   return hipGetLastError();
 }
@@ -310,15 +321,28 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
 // 64 x 64), then 128 x 128 (eight 32 x 64, K in stages of 128).  Measured at
 // K = N = 4096 with the configurations interleaved: M = 4096 130 us (256 x
 // 256), M = 2048 90 us (256 x 128), M = 1024 54 us (128 x 128).
-hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M,
-                            int64_t K, int64_t N, hipStream_t stream) {
-  if (M <= 128) return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>>(x, W, out, M, K, N, stream);
+template <class OutT>
+static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
+                                  hipStream_t stream) {
+  if (M <= 128) return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>, OutT>(x, W, out, M, K, N, stream);
   const int64_t cus = device_cus();
   const int64_t mt = (M + 255) / 256;
   if (N % 256 == 0 && mt * (N / 256) >= cus)
-    return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2>>(x, W, out, M, K, N, stream);
-  if (mt * (N / 128) >= cus) return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>>(x, W, out, M, K, N, stream);
-  return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>>(x, W, out, M, K, N, stream);
+    return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2>, OutT>(x, W, out, M, K, N, stream);
+  if (mt * (N / 128) >= cus) return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>, OutT>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>, OutT>(x, W, out, M, K, N, stream);
+}
+
+hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K, int64_t N,
+                            hipStream_t stream) {
+  return launch_gemm_any<float>(x, W, out, M, K, N, stream);
+}
+
+// The same product with every output rounded to bf16 (round to nearest even):
+// the logits of a router that runs its gate as a plain bf16 linear layer.
+hipError_t launch_gemm_bf16_out_bf16(const uint16_t *x, const uint16_t *W, uint16_t *out, int64_t M, int64_t K,
+                                     int64_t N, hipStream_t stream) {
+  return launch_gemm_any<uint16_t>(x, W, out, M, K, N, stream);
 }
 
 }  // namespace drk

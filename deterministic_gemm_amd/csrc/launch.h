@@ -24,6 +24,8 @@ struct RouteLaunch {
   hipStream_t stream;
 };
 
+hipError_t launch_gemm_bf16_out_bf16(const uint16_t *x, const uint16_t *W, uint16_t *out, int64_t M, int64_t K,
+                                     int64_t N, hipStream_t stream);
 hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
                                     const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
                                     float *out, hipStream_t stream);

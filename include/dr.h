@@ -187,6 +187,27 @@ dr_status dr_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t
                        int64_t N, void *stream);
 
 /*
+ * dr_route_bf16_gemm -- the router as a plain bf16 linear layer, the arm
+ * vllm.cpp PR #2556 describes for upstream (section "Why it is not a
+ * defect": the gate is a bf16 linear layer and the widening to fp32 happens
+ * inside the top-k), next to the fp32 canonical router above.
+ *   logits[m,e] = bf16_rne(sum_k x[m,k] * W[k,e]) on bf16 matrix cores with
+ *   fp32 accumulation (dr_gemm_bf16's instruction sequence, so rows are
+ *   bit-identical across M), then dr_route_select on those bf16 logits: top-k
+ *   with the lowest-index tie-break, softmax weights, margin.
+ *   x [M,K] bf16 bits, W [K,E] bf16 bits, logits [M,E] bf16 out (required),
+ *   ids [M,k], weights [M,k] or NULL, margins [M] or NULL.
+ *   K % 32 == 0, E in {128, 256, 512, 1024}, k <= 32, else
+ *   DR_ERR_UNSUPPORTED.  The logits are the exact product rounded to bf16 up
+ *   to the fp32 accumulation's own rounding (the matrix core's internal order
+ *   is the hardware's); the selection, weights and margins are exact
+ *   functions of them.
+ */
+dr_status dr_route_bf16_gemm(const uint16_t *x, const uint16_t *W, int64_t M, int64_t K, int64_t E,
+                             int32_t k, int32_t *ids, float *weights, uint16_t *logits, dr_margin *margins,
+                             uint32_t flags, void *stream);
+
+/*
  * ---- After routing: token permutation and the MoE combine ----
  *
  * vllm.cpp PR #2556, section "Why a value tap could never have said this":

@@ -152,6 +152,19 @@ def test_moe_calls_reject(L):
     assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 0, 2, 16, P(A), None) == OK
 
 
+def test_route_bf16_gemm_rejects(L):
+    P = ctypes.c_void_p
+    # dr_route_bf16_gemm(x, W, M, K, E, k, ids, weights, logits, margins, flags, stream)
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 64, 256, 0, P(A), None, P(A), None, 0, None) == INVALID
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 64, 256, 8, P(A), None, None, None, 0, None) == INVALID
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 64, 256, 8, P(A), None, P(A), None, 4, None) == INVALID
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 48, 256, 8, P(A), None, P(A), None, 0, None) == UNSUPPORTED
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 64, 64, 8, P(A), None, P(A), None, 0, None) == UNSUPPORTED
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 64, 2048, 8, P(A), None, P(A), None, 0, None) == UNSUPPORTED
+    assert L.dr_route_bf16_gemm(P(A), P(A), 4, 64, 256, 33, P(A), None, P(A), None, 0, None) == UNSUPPORTED
+    assert L.dr_route_bf16_gemm(P(A), P(A), 0, 64, 256, 8, P(A), None, P(A), None, 0, None) == OK
+
+
 def test_grouped_gemm_rejects(L):
     P = ctypes.c_void_p
     # dr_grouped_gemm_bf16(x, Mx, rows, W, offsets, E, P, K, N, out, stream)
