@@ -138,12 +138,22 @@ def auto_variant(M: int, K: int, E: int, x_dtype: str = "f32", logits: bool = Tr
     return VARIANT_NAMES[load_library().dr_route_auto_variant(M, K, E, xd, int(bool(logits)))]
 
 
+def scratch_logits_used(M: int, K: int, E: int, x_dtype: str = "f32") -> bool:
+    """Whether route(..., logits=False) passes a temporary logits buffer: when
+    the library's dispatch with a logits buffer picks a two-kernel family
+    (narrow or split), which the fused families do not match for speed."""
+    return auto_variant(M, K, E, x_dtype, logits=True) in ("narrow", "split")
+
+
 def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, logits: bool = True,
-          weights: bool = True, margins: bool = True, variant: str = "auto", out=None):
+          weights: bool = True, margins: bool = True, variant: str = "auto", out=None,
+          scratch_logits: bool = True):
     """dr_route / dr_route_variant.  Returns (ids [M,k] int32, weights [M,k]
     float32 or None, logits [M,E] float32/bfloat16 or None, margins [M,4] int32
     raw dr_margin records or None).  `out` may pass preallocated tensors as a
-    tuple in the same order."""
+    tuple in the same order.  With logits=False, variant "auto" and
+    scratch_logits, a temporary logits tensor is passed (and dropped) when
+    that lets the library pick a faster family (scratch_logits_used)."""
     L = load_library()
     _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
     _dev_tensor(W, "W", (torch.float32,))
@@ -164,8 +174,12 @@ def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, 
     xd = DR_F32 if x.dtype == torch.float32 else DR_BF16
     flags = DR_ROUTE_RENORMALIZE if renormalize else 0
     v = VARIANTS[variant]
+    lg_pass = lg_t
+    if (lg_t is None and v == 0 and scratch_logits
+            and scratch_logits_used(M, K, E, "f32" if xd == DR_F32 else "bf16")):
+        lg_pass = torch.empty((M, E), dtype=torch.float32 if ldt == DR_F32 else torch.bfloat16, device=dev)
     if v == 0:
-        st = L.dr_route(_ptr(x), xd, _ptr(W), M, K, E, k, ldt, _ptr(ids_t), _ptr(w_t), _ptr(lg_t), _ptr(mg_t),
+        st = L.dr_route(_ptr(x), xd, _ptr(W), M, K, E, k, ldt, _ptr(ids_t), _ptr(w_t), _ptr(lg_pass), _ptr(mg_t),
                         flags, _stream(dev))
     else:
         st = L.dr_route_variant(_ptr(x), xd, _ptr(W), M, K, E, k, ldt, _ptr(ids_t), _ptr(w_t), _ptr(lg_t),

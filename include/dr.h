@@ -113,6 +113,11 @@ typedef struct dr_contract_info {
  *            pairwise tree in expert order, one IEEE division), gathered at
  *            ids; renormalised over the k when flags has DR_ROUTE_RENORMALIZE.
  *   logits   [M,E] of logit_dtype, or NULL: the values the selection saw.
+ *            The two-launch families (narrow, split) keep the logits between
+ *            their launches in this buffer, so without it the fused families
+ *            run: ~75-90 us below M = 48 against ~20 us, and slower for large
+ *            M.  A caller that does not need the logits but wants the faster
+ *            families passes a buffer anyway (the Python binding does).
  *   margins  [M] or NULL.
  *
  * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32.

@@ -56,9 +56,10 @@ def test_mscan_fixed_rows_bit_identical(dr, router_w, mscan_ref, variant):
                                what=f"M={M} first={fixed_first}")
             if variant == "auto":
                 # without the logits output AUTO picks the fused families; the
-                # switch between them lies inside the scanned range
+                # switch between them lies inside the scanned range (the
+                # binding's temporary logits buffer is turned off here)
                 seen_variants.add(dr.auto_variant(M, K, E, logits=False))
-                got = gpu_route_np(dr, dev(x), Wd, TOPK, logits=False)
+                got = gpu_route_np(dr, dev(x), Wd, TOPK, logits=False, scratch_logits=False)
                 assert_route_equal(tuple(None if g is None else g[rows] for g in got), mscan_ref,
                                    what=f"M={M} first={fixed_first} no logits")
     if variant == "auto":
