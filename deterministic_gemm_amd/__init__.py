@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdr.so")
 
 DR_OK, DR_ERR_INVALID, DR_ERR_UNSUPPORTED, DR_ERR_DEVICE = 0, 1, 2, 3
 DR_F32, DR_BF16 = 0, 1
-VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3, "narrow": 4}
+VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3, "narrow": 4, "tiny": 5}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 DR_ROUTE_RENORMALIZE = 1
 
@@ -141,8 +141,8 @@ def auto_variant(M: int, K: int, E: int, x_dtype: str = "f32", logits: bool = Tr
 def scratch_logits_used(M: int, K: int, E: int, x_dtype: str = "f32") -> bool:
     """Whether route(..., logits=False) passes a temporary logits buffer: when
     the library's dispatch with a logits buffer picks a two-kernel family
-    (narrow or split), which the fused families do not match for speed."""
-    return auto_variant(M, K, E, x_dtype, logits=True) in ("narrow", "split")
+    (tiny, narrow or split), which the fused families do not match for speed."""
+    return auto_variant(M, K, E, x_dtype, logits=True) in ("tiny", "narrow", "split")
 
 
 def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, logits: bool = True,

@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libdr.so")
 OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["dr_api.cpp", "route_rowwise.hip", "route_tiled.hip", "route_split.hip", "route_narrow.hip",
+SOURCES = ["dr_api.cpp", "route_rowwise.hip", "route_tiled.hip", "route_split.hip", "route_narrow.hip", "route_tiny.hip",
            "gate_dot.hip", "gemm_bf16.hip", "moe.hip"]
 
 FLAGS = [

@@ -58,7 +58,7 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
   if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
   if (variant != DR_VARIANT_AUTO && variant != DR_VARIANT_ROWWISE && variant != DR_VARIANT_TILED &&
-      variant != DR_VARIANT_SPLIT && variant != DR_VARIANT_NARROW)
+      variant != DR_VARIANT_SPLIT && variant != DR_VARIANT_NARROW && variant != DR_VARIANT_TINY)
     return fail(DR_ERR_INVALID, "bad variant");
   if (M > 0 && (!x || !W || !ids)) return fail(DR_ERR_INVALID, "x, W and ids are required");
   if (!aligned16(x) || !aligned16(W) || !aligned16(ids) || !aligned16(weights) || !aligned16(logits) ||
@@ -77,6 +77,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   if (variant == DR_VARIANT_NARROW && !drk::narrow_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
                 "narrow variant needs fp32 x, K %% 4 == 0, E <= 512 and the logits output");
+  if (variant == DR_VARIANT_TINY && !drk::tiny_supports(E, K, x_dtype == DR_F32, logits != nullptr))
+    return fail(DR_ERR_UNSUPPORTED, "tiny variant needs fp32 x, K %% 4 == 0, K <= 4096 and the logits output");
   if (M == 0) return DR_OK;
 
   drk::RouteLaunch L;
@@ -96,6 +98,7 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   L.stream = static_cast<hipStream_t>(stream);
   const hipError_t e = variant == DR_VARIANT_SPLIT    ? drk::launch_route_split(L)
                        : variant == DR_VARIANT_NARROW ? drk::launch_route_narrow(L)
+                       : variant == DR_VARIANT_TINY   ? drk::launch_route_tiny(L)
                        : variant == DR_VARIANT_TILED  ? drk::launch_route_tiled(L)
                                                       : drk::launch_route_rowwise(L);
   return device_status(e, "route launch");
@@ -107,6 +110,7 @@ extern "C" {
 
 dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits) {
   if (M > kNarrowMaxM && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
+  if (M <= drk::tiny_max_m() && drk::tiny_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_TINY;
   if (M <= kNarrowMaxM && drk::narrow_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_NARROW;
   if (M >= kTiledMinM && drk::tiled_supports(E, K)) return DR_VARIANT_TILED;
   return DR_VARIANT_ROWWISE;
@@ -151,7 +155,11 @@ dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, 
   L.logits = logits;
   L.stream = static_cast<hipStream_t>(stream);
   const bool split = M > kNarrowMaxM && drk::split_supports(E, K, true, true);
-  return device_status(split ? drk::launch_route_logits(L) : drk::launch_route_narrow_logits(L), "logits launch");
+  const bool tiny = M <= drk::tiny_max_m() && drk::tiny_supports(E, K, true, true);
+  return device_status(split  ? drk::launch_route_logits(L)
+                       : tiny ? drk::launch_route_tiny_logits(L)
+                              : drk::launch_route_narrow_logits(L),
+                       "logits launch");
 }
 
 dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, int64_t E, int32_t k,

@@ -61,10 +61,14 @@ typedef enum dr_variant {
   DR_VARIANT_SPLIT = 3,   /* (token, expert) tiles on matrix cores writing the logits, then a
                              selection kernel reading them back; needs fp32 x, K % 4 == 0,
                              E in {256, 512} and the logits output */
-  DR_VARIANT_NARROW = 4   /* small batches: 16-token x 16-expert tiles whose wavefronts split
+  DR_VARIANT_NARROW = 4,  /* small batches: 16-token x 16-expert tiles whose wavefronts split
                              the K groups along the canonical tree, writing the logits, then
                              the selection kernel; needs fp32 x, K % 4 == 0, E <= 512 and the
                              logits output */
+  DR_VARIANT_TINY = 5     /* a few tokens: each lane runs (expert, K-block) chains on the vector
+                             ALUs with the workgroup's W slice in LDS, the blocks combine across
+                             lanes, then the selection kernel; needs fp32 x, K % 4 == 0,
+                             K <= 4096 and the logits output */
 } dr_variant;
 
 /* Divide the k selected weights by their sum (left to right in rank order). */

@@ -38,7 +38,7 @@ def mscan_ref(router_w):
     return oracle_route(fx, router_w, TOPK)
 
 
-@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled", "split", "narrow"])
+@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled", "split", "narrow", "tiny"])
 def test_mscan_fixed_rows_bit_identical(dr, router_w, mscan_ref, variant):
     """Every M in 19..80, the fixed request placed first and last, ascending
     then descending: the fixed rows equal the oracle's solo run bit for bit."""
@@ -97,7 +97,7 @@ def test_sweep_every_m_matches_oracle(dr, router_w, sweep):
         assert_route_equal(got, tuple(r[:M] for r in ref), what=f"M={M}")
 
 
-@pytest.mark.parametrize("variant", ["rowwise", "tiled", "split", "narrow"])
+@pytest.mark.parametrize("variant", ["rowwise", "tiled", "split", "narrow", "tiny"])
 def test_sweep_forced_variants(dr, router_w, sweep, variant):
     x, ref = sweep
     Wd = dev(router_w)
@@ -155,7 +155,7 @@ def test_ragged_k_split(dr, Kx):
     W = (rng.standard_normal((Kx, 256)) * 0.05).astype(np.float32)
     x = rng.standard_normal((70, Kx)).astype(np.float32)
     ref = oracle_route(x, W, 6)
-    for variant in ("split", "narrow", "tiled"):
+    for variant in ("split", "narrow", "tiled") + (("tiny",) if Kx <= 4096 else ()):
         note(f"ragged K={Kx} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), 6, variant=variant)
         assert_route_equal(got, ref, what=f"K={Kx} {variant}")
@@ -168,7 +168,7 @@ def test_every_supported_e(dr, Ex, kx):
     W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
     x = rng.standard_normal((77, Kx)).astype(np.float32)
     ref = oracle_route(x, W, kx)
-    for variant in ("auto", "rowwise", "tiled", "split", "narrow"):
+    for variant in ("auto", "rowwise", "tiled", "split", "narrow", "tiny"):
         if variant in ("tiled", "narrow") and Ex == 1024:
             continue
         if variant == "split" and Ex not in (256, 512):
@@ -185,7 +185,7 @@ def test_modes(dr, router_w, sweep, mode):
     kw = {"logit_dtype": "bf16"} if mode == "bf16_logits" else {"renormalize": True}
     ref = oracle_route(x[:M], router_w, TOPK, logits_bf16=(mode == "bf16_logits"),
                        renormalize=(mode == "renormalize"))
-    for variant in ("rowwise", "tiled", "split", "narrow"):
+    for variant in ("rowwise", "tiled", "split", "narrow", "tiny"):
         note(f"mode {mode} {variant}")
         got = gpu_route_np(dr, dev(x[:M]), dev(router_w), TOPK, variant=variant, **kw)
         assert_route_equal(got, ref, what=f"{mode} {variant}")
@@ -209,7 +209,7 @@ def test_special_values(dr, Ex):
     W[:, 9] = -0.0
     W[:, 10] = W[:, 11]                        # exact ties
     ref = oracle_route(x, W, kx)
-    for variant in ("rowwise", "tiled", "narrow") + (("split",) if Ex == 256 else ()):
+    for variant in ("rowwise", "tiled", "narrow", "tiny") + (("split",) if Ex == 256 else ()):
         note(f"special values E={Ex} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
         assert_route_equal(got, ref, what=f"special {variant}")
@@ -232,7 +232,7 @@ def test_rows_at_any_offset(dr, router_w, sweep):
     for shift in (1, 7, 16, 31, 40):
         filler = rng.standard_normal((shift, K)).astype(np.float32)
         xb = np.concatenate([filler, block, filler[: shift // 2]], axis=0)
-        for variant in ("auto", "split", "narrow"):
+        for variant in ("auto", "split", "narrow", "tiny"):
             note(f"offset shift={shift} M={xb.shape[0]} {variant}")
             got = gpu_route_np(dr, dev(xb), Wd, TOPK, variant=variant)
             rows = slice(shift, shift + 50)
