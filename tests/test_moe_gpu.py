@@ -126,7 +126,7 @@ def _dev_elem(a):
 @pytest.mark.parametrize("y_bf16", [True, False])
 @pytest.mark.parametrize("shared_kind", [None, "bf16", "f32"])
 @pytest.mark.parametrize("M,k,D", [(1, 1, 1), (19, 8, 7), (19, 8, 8), (64, 10, 12), (300, 8, 2048),
-                                   (33, 32, 260), (5, 8, 4100)])
+                                   (33, 32, 260), (5, 8, 4100), (7, 8, 264), (3, 8, 4104)])
 def test_combine_matches_oracle(y_bf16, shared_kind, M, k, D):
     dr = require_gpu()
     ids, pos, w, y, shared, gate = _combine_case(M, k, 64, D, y_bf16, shared_kind, seed=M + 7 * k + D)
