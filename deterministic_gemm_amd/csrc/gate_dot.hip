@@ -122,6 +122,13 @@ struct GdLds {
   static_assert((GD_WAVES * S * UPC + WU) * 16 <= 160 * 1024, "LDS");
 };
 
+// x is read exactly once.  For fp32 rows its transfers carry the
+// non-temporal hint (measured in one process at M = K = 4096: 11.9 us
+// against 14.5 us); for bf16 rows the hint measured 3% slower.
+__device__ __forceinline__ void dma16_stream(const void *src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "s"(lds_base) : "memory");
+}
+
 template <class C>
 __device__ __forceinline__ void gd_issue(const char *__restrict__ x, int64_t M, int K, int64_t mrow0, int nb,
                                          int lane, int c, uint32_t slot) {
@@ -135,7 +142,8 @@ __device__ __forceinline__ void gd_issue(const char *__restrict__ x, int64_t M, 
     const int64_t mm = mrow0 + rr;
     const void *src = &g_pad_pos;
     if (c < C::NCH && mm < M && bb < nb && e < K) src = x + (mm * K + e) * C::ESZ;
-    dma16(src, slot + 1024 * t);
+    if constexpr (C::ESZ == 4) dma16_stream(src, slot + 1024 * t);
+    else dma16(src, slot + 1024 * t);
   }
 }
 
