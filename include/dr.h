@@ -244,8 +244,9 @@ dr_status dr_route_bf16_gemm(const uint16_t *x, const uint16_t *W, int64_t M, in
  * 1 <= k <= 32, 1 <= E <= 1024 and M*k < 2^31, else DR_ERR_UNSUPPORTED.
  * M == 0 still writes offsets (all zero).  An id outside [0,E) gets pos -1
  * and no grouped row; a row repeating an expert gets in-range but
- * unspecified positions.  Cost: each workgroup of 1024 tokens reads all M*k
- * ids once (quadratic in M; ~1 us per 8192 tokens at k = 8).
+ * unspecified positions.  Batches of several 512-token chunks run three
+ * launches (per-chunk expert histograms, kept in rows until the last launch
+ * overwrites it; placement; rows from pos), smaller ones a single launch.
  */
 dr_status dr_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
                          int32_t *rows, int32_t *pos, void *stream);
