@@ -118,7 +118,7 @@ struct GdLds {
   static constexpr int TPC = UPC / 64;            // transfers per chunk (8)
   static constexpr int WU = LPR * UPB;            // units of w held in LDS
   static constexpr int S = (GD_WAVES * 4 * UPC + WU) * 16 <= 160 * 1024 ? 4 : 3;  // ring stages
-  static_assert(NCH >= S - 1 && TPC * (S - 2) <= 63, "chunking");
+  static_assert(NCH >= S - 1 && TPC * (S - 1) <= 63, "chunking");
   static_assert((GD_WAVES * S * UPC + WU) * 16 <= 160 * 1024, "LDS");
 };
 

@@ -51,7 +51,7 @@ struct GemmCfg {
   static_assert(BK % 32 == 0 && (UA == 4 || UA == 8 || UA == 16 || UA == 32), "K steps per stage");
   static_assert(UB == 2 || UB == 4 || UB == 8 || UB == 16 || UB == 32, "W row units");
   static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
-  static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
+  static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
   // x rows: unit u of row r sits at u ^ swa(r); 16 consecutive rows reading
   // the same unit then hit 16 distinct 16-byte bank groups.

@@ -44,7 +44,7 @@ struct NarrowCfg {
   static constexpr int CPG = 256 / KC;
   static constexpr int NQ = AT * BT * 4;       // group partials per lane
   static_assert(WU % 64 == 0 && WI >= 1 && XI >= 1 && XI * 64 == TT * KC, "whole transfers");
-  static_assert(PER * (S - 2) <= 63 && S >= 2, "vmcnt range");
+  static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(KC % 4 == 0 && 256 % KC == 0, "chunking");
   static_assert(KG == 1 || KG == 2 || KG == 4, "parts");
   static_assert((KG * S * STG + (KG - 1) * 64 * NQ) * 4 <= 160 * 1024, "LDS");

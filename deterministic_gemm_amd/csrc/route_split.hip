@@ -62,7 +62,7 @@ struct SplitCfg {
   static_assert(XI * 64 == XU && XIW * NWP == XI && XIW >= 1, "x transfers split evenly");
   static_assert(KP == 1 || KP == 2, "parts");
   static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
-  static_assert(PER * (S - 2) <= 63, "vmcnt range");
+  static_assert(PER * (S - 1) <= 63, "vmcnt range");
   static_assert(KC % 4 == 0 && 256 % KC == 0 && (S == 3 || S == 4), "chunking");
   static_assert(TT * LGP + (KP - 1) * NWP * AT * BT * 4 * 64 <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");

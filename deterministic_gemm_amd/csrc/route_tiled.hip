@@ -244,7 +244,7 @@ struct DmaCfg {
   static_assert(WIW * NW == WI && WIW >= 1, "W transfers split evenly");
   static_assert(XI * 64 == XU && XIW * XW == XI, "x transfers split evenly");
   static_assert((KC * E / 4) % 64 == 0, "a W transfer stays inside one slot");
-  static_assert(PER_X * (S - 2) <= 63, "vmcnt range");
+  static_assert(PER_X * (S - 1) <= 63, "vmcnt range");
   static_assert(KC % 4 == 0 && 256 % KC == 0 && S >= 2, "chunking");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
 };

@@ -52,9 +52,12 @@ __global__ __launch_bounds__(64) void route_tiny_logits_kernel(const float *__re
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * T;
   const int nb = (K + 255) / 256;
 
-  // W slice: block b's rows k = 256 b .. 256 b + 255, ROWB bytes each
+  // W slice: block b's rows k = 256 b .. 256 b + 255, ROWB bytes each.  At
+  // most 32 transfers stay outstanding (the wait counter holds 63).
+  int issued = 0;
   for (int b = 0; b < nb; ++b)
     for (int i = 0; i < 256 / C::RPI; ++i) {
+      if (++issued > 32) wait_vmcnt<31>();
       const int r = i * C::RPI + lane / (C::ROWB / 16);  // row within the block
       const int u = lane % (C::ROWB / 16);               // 16-byte unit within the row
       const int kk = 256 * b + r;
@@ -65,6 +68,7 @@ __global__ __launch_bounds__(64) void route_tiny_logits_kernel(const float *__re
   // x rows: token t, block b: 256 values in one instruction
   for (int t = 0; t < T; ++t)
     for (int b = 0; b < nb; ++b) {
+      if (++issued > 32) wait_vmcnt<31>();
       const int kk = 256 * b + 4 * lane;
       const void *src = &g_pad_pos;
       if (m0 + t < M && kk < K) src = x + (m0 + t) * K + kk;
