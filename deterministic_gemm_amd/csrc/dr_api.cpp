@@ -32,7 +32,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxK = 16384;
 constexpr int32_t kMaxTopK = 32;
-constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
+// Rows (tokens) per call.  Every launch keeps its work-items per grid
+// dimension below 2^32 up to this bound (the largest is the narrow family at
+// E = 512: 2^18 workgroups x 32 expert tiles x 256 lanes).  At K = 2048 it is
+// 32 GiB of fp32 activations.
+constexpr int64_t kMaxM = int64_t(1) << 22;
 
 // Batches at or above this size run on the matrix-core kernel.  The value sits
 // inside the 19..80 token m-scan on purpose, so that scan crosses a dispatch
@@ -79,6 +83,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
                 "narrow variant needs fp32 x, K %% 4 == 0, E <= 512 and the logits output");
   if (variant == DR_VARIANT_TINY && !drk::tiny_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED, "tiny variant needs fp32 x, K %% 4 == 0, K <= 4096 and the logits output");
+  if (variant == DR_VARIANT_TINY && M > 4 * 65535)
+    return fail(DR_ERR_UNSUPPORTED, "tiny variant takes at most %d tokens", 4 * 65535);
   if (M == 0) return DR_OK;
 
   drk::RouteLaunch L;
@@ -282,7 +288,7 @@ dr_status dr_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *row
 dr_status dr_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
                          int32_t *rows, int32_t *pos, void *stream) {
   g_last_error[0] = '\0';
-  if (M < 0 || k < 1 || E < 1) return fail(DR_ERR_INVALID, "bad sizes");
+  if (M < 0 || k < 1 || E < 1 || M > kMaxM) return fail(DR_ERR_INVALID, "bad sizes");
   if (!offsets || (M > 0 && (!ids || !rows || !pos))) return fail(DR_ERR_INVALID, "ids, offsets, rows and pos are required");
   if (!aligned16(ids) || !aligned16(offsets) || !aligned16(rows) || !aligned16(pos))
     return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
@@ -299,7 +305,7 @@ dr_status dr_moe_gather(const void *x, dr_dtype dtype, int64_t M, int64_t D, con
   if (dtype != DR_F32 && dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad dtype");
   if (P > 0 && (!x || !rows || !xp)) return fail(DR_ERR_INVALID, "x, rows and xp are required");
   if (!aligned16(x) || !aligned16(rows) || !aligned16(xp)) return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
-  if (P > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "P must be below 2^31");
+  if (P > INT32_MAX || M > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "P and M must be below 2^31");
   if (P == 0) return DR_OK;
   return device_status(drk::launch_moe_gather(x, M, D * (dtype == DR_BF16 ? 2 : 4), rows, P, xp,
                                               static_cast<hipStream_t>(stream)),
@@ -319,7 +325,7 @@ dr_status dr_moe_combine(const void *y, dr_dtype y_dtype, int64_t P, const float
   if (!aligned16(y) || !aligned16(weights) || !aligned16(ids) || !aligned16(pos) || !aligned16(shared) ||
       !aligned16(gate) || !aligned16(out))
     return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
-  if (k > 32 || M > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "dr_moe_combine needs k <= 32 and M < 2^31");
+  if (k > 32 || M > kMaxM) return fail(DR_ERR_UNSUPPORTED, "dr_moe_combine needs k <= 32 and M <= 2^22");
   if (M == 0) return DR_OK;
   return device_status(drk::launch_moe_combine(y, y_dtype == DR_BF16, P, weights, ids, pos, shared,
                                                shared && shared_dtype == DR_BF16, gate, M, k, D, out,

@@ -258,30 +258,33 @@ hipError_t launch_moe_permute(const int32_t *ids, int64_t M, int k, int E, int32
 
 // ------------------------------------------------------------------ gather
 
-// One workgroup per grouped row: xp[p] = x[rows[p]] (a row index outside
-// [0, Mx) gives a zero row), in 16-byte pieces when rows allow it.
+// One workgroup per grouped row, the grid striding over rows past 65536:
+// xp[p] = x[rows[p]] (a row index outside [0, Mx) gives a zero row), in
+// 16-byte pieces when rows allow it.
 __global__ __launch_bounds__(256) void moe_gather_kernel(const char *__restrict__ x, int64_t Mx,
-                                                         const int32_t *__restrict__ rows, int64_t row_bytes,
-                                                         char *__restrict__ xp) {
-  const int64_t p = blockIdx.x;
-  const int32_t r = rows[p];
-  const bool ok = r >= 0 && r < Mx;
-  const int t = threadIdx.x;
-  if (row_bytes % 16 == 0) {
-    const uint4 *src = reinterpret_cast<const uint4 *>(x + static_cast<int64_t>(ok ? r : 0) * row_bytes);
-    uint4 *dst = reinterpret_cast<uint4 *>(xp + p * row_bytes);
-    for (int64_t i = t; i < row_bytes / 16; i += 256) dst[i] = ok ? src[i] : uint4{0u, 0u, 0u, 0u};
-  } else {
-    const uint16_t *src = reinterpret_cast<const uint16_t *>(x + static_cast<int64_t>(ok ? r : 0) * row_bytes);
-    uint16_t *dst = reinterpret_cast<uint16_t *>(xp + p * row_bytes);
-    for (int64_t i = t; i < row_bytes / 2; i += 256) dst[i] = ok ? src[i] : static_cast<uint16_t>(0);
+                                                         const int32_t *__restrict__ rows, int64_t P,
+                                                         int64_t row_bytes, char *__restrict__ xp) {
+  for (int64_t p = blockIdx.x; p < P; p += gridDim.x) {
+    const int32_t r = rows[p];
+    const bool ok = r >= 0 && r < Mx;
+    const int t = threadIdx.x;
+    if (row_bytes % 16 == 0) {
+      const uint4 *src = reinterpret_cast<const uint4 *>(x + static_cast<int64_t>(ok ? r : 0) * row_bytes);
+      uint4 *dst = reinterpret_cast<uint4 *>(xp + p * row_bytes);
+      for (int64_t i = t; i < row_bytes / 16; i += 256) dst[i] = ok ? src[i] : uint4{0u, 0u, 0u, 0u};
+    } else {
+      const uint16_t *src = reinterpret_cast<const uint16_t *>(x + static_cast<int64_t>(ok ? r : 0) * row_bytes);
+      uint16_t *dst = reinterpret_cast<uint16_t *>(xp + p * row_bytes);
+      for (int64_t i = t; i < row_bytes / 2; i += 256) dst[i] = ok ? src[i] : static_cast<uint16_t>(0);
+    }
   }
 }
 
 hipError_t launch_moe_gather(const void *x, int64_t Mx, int64_t row_bytes, const int32_t *rows, int64_t P,
                              void *xp, hipStream_t stream) {
-  hipLaunchKernelGGL(moe_gather_kernel, dim3(static_cast<uint32_t>(P)), dim3(256), 0, stream,
-                     static_cast<const char *>(x), Mx, rows, row_bytes, static_cast<char *>(xp));
+  const int64_t blocks = P < 65536 ? P : 65536;
+  hipLaunchKernelGGL(moe_gather_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                     static_cast<const char *>(x), Mx, rows, P, row_bytes, static_cast<char *>(xp));
   return hipGetLastError();
 }
 

@@ -124,7 +124,8 @@ typedef struct dr_contract_info {
  *            families passes a buffer anyway (the Python binding does).
  *   margins  [M] or NULL.
  *
- * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32.
+ * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32;
+ * 0 <= M <= 2^22 tokens per call (larger M is DR_ERR_INVALID).
  * Other shapes return DR_ERR_UNSUPPORTED (no silent change of numeric path).
  */
 dr_status dr_route(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
@@ -172,7 +173,7 @@ dr_status dr_route_select(const void *logits, dr_dtype logit_dtype, int64_t M, i
  * gate[m] = sigmoid(dot[m]) = 1/(1+e) for dot >= 0, e/(1+e) otherwise, with
  * e = exp(-|dot|) from the contract's exp.
  *   x [M,K] (f32 or bf16), w [K] (f32 or bf16), dot [M] fp32 or NULL,
- *   gate [M] fp32 or NULL.  1 <= K <= 16384.
+ *   gate [M] fp32 or NULL.  1 <= K <= 16384, M <= 2^22.
  */
 dr_status dr_gate_dot(const void *x, dr_dtype x_dtype, const void *w, dr_dtype w_dtype,
                       float *dot, float *gate, int64_t M, int64_t K, void *stream);

@@ -104,6 +104,15 @@ def test_halves_reject(L):
     assert L.dr_route_select(None, 0, 0, 256, 8, None, None, None, 0, None) == OK
 
 
+def test_row_bounds(L):
+    # 2^22 tokens per call at most; a forced vector-ALU call at most 4 * 65535
+    assert _route(L, M=(1 << 22) + 1) == INVALID
+    assert _route(L, M=4 * 65535 + 1, variant=dr.VARIANTS["tiny"]) == UNSUPPORTED
+    P = ctypes.c_void_p
+    assert L.dr_gate_dot(P(A), 0, P(A), 0, P(A), None, (1 << 22) + 1, 64, None) == INVALID
+    assert L.dr_moe_permute(P(A), (1 << 22) + 1, 1, 8, P(A), P(A), P(A), None) == INVALID
+
+
 def test_empty_batch_returns_ok_without_launch(L):
     assert _route(L, M=0) == OK
     assert _route(L, M=0, x=0, W=0, ids=0) == OK
@@ -134,8 +143,8 @@ def test_moe_calls_reject(L):
     assert L.dr_moe_permute(P(A + 4), 4, 2, 8, P(A), P(A), P(A), None) == INVALID
     assert L.dr_moe_permute(P(A), 4, 33, 64, P(A), P(A), P(A), None) == UNSUPPORTED
     assert L.dr_moe_permute(P(A), 4, 2, 1025, P(A), P(A), P(A), None) == UNSUPPORTED
-    assert L.dr_moe_permute(P(A), 1 << 31, 1, 8, P(A), P(A), P(A), None) == UNSUPPORTED
-    assert L.dr_moe_permute(P(A), 1 << 30, 2, 8, P(A), P(A), P(A), None) == UNSUPPORTED
+    assert L.dr_moe_permute(P(A), 1 << 31, 1, 8, P(A), P(A), P(A), None) == INVALID
+    assert L.dr_moe_permute(P(A), 1 << 30, 2, 8, P(A), P(A), P(A), None) == INVALID
     # dr_moe_gather(x, dtype, M, D, rows, P, xp, stream)
     assert L.dr_moe_gather(P(A), 0, 4, 0, P(A), 8, P(A), None) == INVALID
     assert L.dr_moe_gather(P(A), 7, 4, 16, P(A), 8, P(A), None) == INVALID
@@ -150,6 +159,7 @@ def test_moe_calls_reject(L):
     assert L.dr_moe_combine(P(A), 0, 8, P(A), None, P(A), None, 0, None, 4, 2, 16, P(A), None) == INVALID
     assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 4, 33, 16, P(A), None) == UNSUPPORTED
     assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, 0, 2, 16, P(A), None) == OK
+    assert L.dr_moe_combine(P(A), 0, 8, P(A), P(A), P(A), None, 0, None, (1 << 22) + 1, 2, 16, P(A), None) == UNSUPPORTED
 
 
 def test_route_bf16_gemm_rejects(L):
