@@ -277,7 +277,7 @@ dr_status dr_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *row
     return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
   if (K % 32 != 0 || N % 128 != 0) return fail(DR_ERR_UNSUPPORTED, "K must be a multiple of 32 and N of 128");
   if (E > 1024 || P > INT32_MAX || Mx > INT32_MAX || K > (int64_t(1) << 30) || N > (int64_t(1) << 30) ||
-      (P + 127) / 128 + E > 65535)
+      (P + 127) / 128 + E > 65535 || 8 * (((P + 127) / 128 + E + 7) / 8) * (N / 128) > int64_t(UINT32_MAX))
     return fail(DR_ERR_UNSUPPORTED, "size out of range");
   if (P == 0) return DR_OK;
   return device_status(drk::launch_grouped_gemm_bf16(x, Mx, rows, W, offsets, E, P, K, N, out,

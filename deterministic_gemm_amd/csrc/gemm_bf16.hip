@@ -121,6 +121,40 @@ __device__ __forceinline__ uint16_t gemm_f32_to_bf16(float v) {
   return static_cast<uint16_t>((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// One 32-wide K step of a wavefront's tile from the stage at As (x) / Bs (W).
+template <class C>
+__device__ __forceinline__ void gemm_kstep(const char *As, const char *Bs, int kk, int wm, int wn, int r16, int g4,
+                                           int tj, int tq, f32x4 (&acc)[C::FM][C::FN]) {
+  constexpr int FM = C::FM, FN = C::FN;
+  bf16x8 af[FM], bfv[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int r = wm * C::TM + i * 16 + r16;
+    const int u = (kk * 4 + g4) ^ C::swa(r);
+    af[i] = *reinterpret_cast<const bf16x8 *>(As + (r * C::UA + u) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = wn * C::TN + j * 16 + 4 * tq;  // first of the 4 columns this lane reads
+    i16x4 h[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int kr = kk * 32 + 8 * g4 + 4 * c + tj;
+      const int u = (col / 8) ^ C::swb(kr);
+      const char *a = Bs + (kr * C::UB + u) * 16 + (col % 8) * 2;
+      h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
+    }
+    const i16x4 lo = h[0], hi = h[1];
+    bfv[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                            lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+}
+
 // One output tile: rows [m0, min(m0 + BM, mend)) and columns [n0, n0 + BN) of
 // out = x[rows] . W, every output reduced by the same instruction sequence;
 // stored as fp32, or rounded to bf16 (OutT = uint16_t).
@@ -133,6 +167,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nst = (K + C::BK - 1) / C::BK;
+  // A wavefront whose rows all lie past the tile's last row (in a ragged
+  // tile) skips its LDS reads and matrix steps but still moves its share of
+  // the transfers and meets every barrier.
+  const bool wlive = __builtin_amdgcn_readfirstlane(static_cast<int>(m0 + static_cast<int64_t>(wm) * C::TM < mend)) != 0;
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -161,33 +199,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
 #pragma unroll
     for (int kk = 0; kk < C::BK / 32; ++kk) {
       if (kk < nsub) {
-        bf16x8 af[FM], bfv[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int r = wm * C::TM + i * 16 + r16;
-          const int u = (kk * 4 + g4) ^ C::swa(r);
-          af[i] = *reinterpret_cast<const bf16x8 *>(As + (r * C::UA + u) * 16);
-        }
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = wn * C::TN + j * 16 + 4 * tq;  // first of the 4 columns this lane reads
-          i16x4 h[2];
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int kr = kk * 32 + 8 * g4 + 4 * c + tj;
-            const int u = (col / 8) ^ C::swb(kr);
-            const char *a = Bs + (kr * C::UB + u) * 16 + (col % 8) * 2;
-            h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
-          }
-          const i16x4 lo = h[0], hi = h[1];
-          bfv[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
-                                                  lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-        }
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+        if (wlive) gemm_kstep<C>(As, Bs, kk, wm, wn, r16, g4, tj, tq, acc);
       }
     }
   }
@@ -227,11 +239,16 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 // Grouped (per-expert) product: expert e owns output rows [offsets[e],
 // offsets[e+1]) and multiplies them by W[e].  Row tiles never straddle two
 // experts: expert e has ceil(count_e / BM) of them, numbered after those of
-// experts < e, and workgroup row index t (blockIdx.y) finds its expert by a
-// scan of the tile counts in LDS.  Workgroups past the last tile exit.  Every
-// output row is reduced by the dense kernel's instruction sequence, so a row
-// has the same bits whatever its group's size or position, and the same bits
-// as dr_gemm_bf16 of that row with W[e].
+// experts < e, T in all; a workgroup finds the expert of its row tile by a
+// scan of the tile counts in LDS.  Workgroups go to the eight XCDs in turn
+// (linear index L to XCD L % 8); XCD c takes the c-th contiguous eighth of
+// the T row tiles with all their column tiles, one row tile's columns after
+// another.  So an expert's rows and weights are read into one XCD's L2 (a
+// column-major order makes every XCD read all of x).  The grid is sized for
+// the most row tiles any routing can give; workgroups past the last tile of
+// their XCD's share exit.  Every output row is reduced by the dense kernel's
+// instruction sequence, so a row has the same bits whatever its group's size
+// or position, and the same bits as dr_gemm_bf16 of that row with W[e].
 constexpr int GG_EMAX = 1024;
 
 template <class C>
@@ -239,14 +256,14 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
                                                                  const int32_t *__restrict__ rows,
                                                                  const uint16_t *__restrict__ W,
                                                                  const int32_t *__restrict__ offsets, int E,
-                                                                 int64_t P, float *__restrict__ out, int K, int N) {
+                                                                 int64_t P, float *__restrict__ out, int K, int N,
+                                                                 int ncol) {
   constexpr int EPL = (GG_EMAX + C::NT - 1) / C::NT;  // experts per lane in the scan
   __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
   __shared__ int32_t tstart[GG_EMAX + 1];
   __shared__ int32_t wsum[C::NW];
   __shared__ int32_t found;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int tile = blockIdx.y;
   // row tiles of lane t's experts EPL*t .. EPL*t + EPL - 1, and their scan
   int cnt[EPL], v = 0;
 #pragma unroll
@@ -264,8 +281,16 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   if (lane == 63) wsum[wave] = v;
   if (t == 0) found = -1;
   __syncthreads();
-  int start = v - mine;
-  for (int w = 0; w < wave; ++w) start += wsum[w];
+  int start = v - mine, total = 0;
+  for (int w = 0; w < C::NW; ++w) {
+    if (w < wave) start += wsum[w];
+    total += wsum[w];
+  }
+  // this workgroup's row tile and column tile
+  const int xcd = static_cast<int>(blockIdx.x % 8), slot = static_cast<int>(blockIdx.x / 8);
+  const int share = (total + 7) / 8;  // row tiles per XCD
+  const int tr = slot / ncol;
+  const int tile = (tr < share) ? xcd * share + tr : 0x7FFFFFFF;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = EPL * t + i;
@@ -281,9 +306,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   const int64_t lo = offsets[e], mend = offsets[e + 1];
   if (lo < 0 || mend > P || mend < lo) return;  // inconsistent offsets: nothing is written outside out
   const int64_t m0 = lo + static_cast<int64_t>(tile - tstart[e]) * C::BM;
-  const int nx = gridDim.x;
-  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
-  gemm_tile<C>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N, bx * C::BN, smem);
+  gemm_tile<C>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N, (slot % ncol) * C::BN, smem);
 }
 
 template <class C, class OutT = float>
@@ -299,17 +322,25 @@ template <class C>
 static hipError_t launch_grouped_c(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
                                    const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N, float *out,
                                    hipStream_t stream) {
-  // enough row tiles for any split of P rows over E experts
+  // enough row tiles for any split of P rows over E experts, in eight
+  // equal shares, each with all its column tiles
   const int64_t tiles = (P + C::BM - 1) / C::BM + E;
-  const dim3 grid(static_cast<uint32_t>(N / C::BN), static_cast<uint32_t>(tiles));
+  const int64_t ncol = N / C::BN;
+  const dim3 grid(static_cast<uint32_t>(8 * ((tiles + 7) / 8) * ncol));
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
-                     static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N));
+                     static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N), static_cast<int>(ncol));
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
                                     const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
                                     float *out, hipStream_t stream) {
+  // the dense kernel's large tile: at 65536 rows x 2048 x 1024 over 256
+  // experts of 193-324 rows it beats 128 x 128 tiles (eight 32 x 64
+  // wavefront tiles) by ~12%; configurations with more stages in flight
+  // need more than the 256 registers a wavefront has here
+  if (N % 256 == 0)
+    return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
   return launch_grouped_c<GemmCfg<128, 128, 4, 2, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
 }
 

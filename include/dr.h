@@ -294,7 +294,8 @@ dr_status dr_moe_combine(const void *y, dr_dtype y_dtype, int64_t P, const float
  *   offsets [E+1] int32 (as dr_moe_permute writes them: offsets[0] = 0,
  *   non-decreasing, offsets[E] = P), out [P,N] fp32.
  *   K % 32 == 0, N % 128 == 0, 1 <= E <= 1024, P < 2^31 and
- *   ceil(P/128) + E <= 65535, else DR_ERR_UNSUPPORTED.  A rows entry outside
+ *   T = ceil(P/128) + E <= 65535 and 8 ceil(T/8) (N/128) < 2^32 (the
+ *   workgroup count), else DR_ERR_UNSUPPORTED.  A rows entry outside
  *   [0,Mx) reads a zero row.  Inconsistent offsets leave the affected rows
  *   unwritten; nothing is written outside out.
  */

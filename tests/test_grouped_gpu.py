@@ -113,3 +113,37 @@ def test_grouped_out_of_range_rows_read_zero_rows():
     note("grouped gemm out-of-range rows")
     out = dr.grouped_gemm_bf16(x, W, off, rows).cpu().numpy()
     assert np.all(out[[0, 2, 4]] == K) and np.all(out[[1, 3]] == 0)
+
+
+def test_grouped_full_size_sampled():
+    """The routing workload's size: 8192 tokens, k=8 (65536 grouped rows, 193-324
+    per expert, so experts span one or two 256-row tiles), K=2048, N=1024,
+    E=256.  Sampled experts against the dense GEMM bit for bit, sampled rows
+    against the oracle within the tolerance."""
+    dr = require_gpu()
+    M, k, E, K, N = 8192, 8, 256, 2048, 1024
+    g = np.random.default_rng(41)
+    xb = wl.to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(41)
+    Wd = (torch.randn((E, K, N), device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    ids, off, rows, pos = _routes_and_groups(dr, M, k, E, seed=41)
+    note("grouped gemm full size (fused gather)")
+    out = dr.grouped_gemm_bf16(dev_bf16_bits(xb), Wd, off, rows)
+    got = _u32(out)
+    off_h, rows_h = off.cpu().numpy(), rows.cpu().numpy()
+    cnt = np.diff(off_h)
+    for e in sorted({int(np.argmax(cnt)), int(np.argmin(cnt)), 0, 77, E - 1}):
+        seg = slice(off_h[e], off_h[e + 1])
+        note(f"dense rows of expert {e} ({cnt[e]} rows)")
+        dense = dr.gemm_bf16(dev_bf16_bits(np.ascontiguousarray(xb[rows_h[seg]])), Wd[e].contiguous())
+        assert np.array_equal(got[seg], _u32(dense)), f"expert {e}"
+    sample = np.unique(np.r_[0, M * k - 1, off_h[1:-1], g.integers(0, M * k, 64)])
+    e_of = np.searchsorted(off_h, sample, side="right") - 1
+    Wh = {}
+    for e in np.unique(e_of):
+        Wh[e] = Wd[e].view(torch.int16).cpu().numpy().view(np.uint16)
+    outh = out.cpu().numpy()
+    for p, e in zip(sample, e_of):
+        ref = oracle.gemm_bf16_ref(xb[rows_h[p]][None, :], Wh[e])[0]
+        assert np.abs(outh[p].astype(np.float64) - ref).max() <= TOL, (p, e)
