@@ -157,8 +157,12 @@ __device__ __forceinline__ void gemm_kstep(const char *As, const char *Bs, int k
 
 // One output tile: rows [m0, min(m0 + BM, mend)) and columns [n0, n0 + BN) of
 // out = x[rows] . W, every output reduced by the same instruction sequence;
-// stored as fp32, or rounded to bf16 (OutT = uint16_t).
-template <class C, class OutT = float>
+// stored as fp32, or rounded to bf16 (OutT = uint16_t).  With SKIP, a
+// wavefront whose rows all lie past the tile's last row (in a ragged grouped
+// tile) skips its LDS reads and matrix steps but still moves its share of the
+// transfers and meets every barrier; the dense kernel, whose only partial
+// tile is the last, measured faster without the branch.
+template <class C, class OutT = float, bool SKIP = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
                                           int64_t Mx, const uint16_t *__restrict__ W, OutT *__restrict__ out,
                                           int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
@@ -167,10 +171,8 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nst = (K + C::BK - 1) / C::BK;
-  // A wavefront whose rows all lie past the tile's last row (in a ragged
-  // tile) skips its LDS reads and matrix steps but still moves its share of
-  // the transfers and meets every barrier.
-  const bool wlive = __builtin_amdgcn_readfirstlane(static_cast<int>(m0 + static_cast<int64_t>(wm) * C::TM < mend)) != 0;
+  const bool wlive =
+      !SKIP || __builtin_amdgcn_readfirstlane(static_cast<int>(m0 + static_cast<int64_t>(wm) * C::TM < mend)) != 0;
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -199,7 +201,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
 #pragma unroll
     for (int kk = 0; kk < C::BK / 32; ++kk) {
       if (kk < nsub) {
-        if (wlive) gemm_kstep<C>(As, Bs, kk, wm, wn, r16, g4, tj, tq, acc);
+        if (!SKIP || wlive) gemm_kstep<C>(As, Bs, kk, wm, wn, r16, g4, tj, tq, acc);
       }
     }
   }
@@ -306,7 +308,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   const int64_t lo = offsets[e], mend = offsets[e + 1];
   if (lo < 0 || mend > P || mend < lo) return;  // inconsistent offsets: nothing is written outside out
   const int64_t m0 = lo + static_cast<int64_t>(tile - tstart[e]) * C::BM;
-  gemm_tile<C>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N, (slot % ncol) * C::BN, smem);
+  gemm_tile<C, float, true>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N,
+                            (slot % ncol) * C::BN, smem);
 }
 
 template <class C, class OutT = float>
