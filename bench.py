@@ -99,6 +99,14 @@ def _time_graph(fn, check, stream, torch, calls: int = 20, replays: int = 10):
     return a.elapsed_time(b) / (calls * replays)
 
 
+def _ulps_hist(np, u):
+    """Counts of margin ULPs (selected minus rejected, in bf16 steps) by bucket."""
+    u = np.asarray(u, dtype=np.int64)
+    edges = [(0, 0), (1, 1), (2, 3), (4, 7), (8, 15), (16, 63), (64, 255), (256, 1 << 31)]
+    return {(f"{a}" if a == b else f"{a}-{b}" if b < (1 << 31) else f">={a}"): int(np.sum((u >= a) & (u <= b)))
+            for a, b in edges}
+
+
 def _bits_equal(torch, a, b):
     if a is None or b is None:
         return a is None and b is None
@@ -120,6 +128,7 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
     dev = xd.device
     log = lambda m: print(f"[suite] {m}", file=sys.stderr, flush=True)  # noqa: E731
     suite = {}
+    checks = {}  # GPU outputs the CPU baseline leg compares with the oracle
 
     def timed(fn, steps=20):
         """(device ms per call from graph replay, ms per eager back-to-back call)"""
@@ -134,7 +143,8 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
         sweep.append({"M": m, "variant": dr.auto_variant(m, K, E), "us": round(ms * 1e3, 2),
                       "us_host_bound": round(ms_e * 1e3, 2),
                       "tokens_per_s": round(m / (ms * 1e-3), 1),
-                      "tflops": round(2.0 * m * K * E / (ms * 1e-3) / 1e12, 2)})
+                      "tflops": round(2.0 * m * K * E / (ms * 1e-3) / 1e12, 2),
+                      "frac_fp32_peak": round(2.0 * m * K * E / (ms * 1e-3) / 1e12 / PEAK_FP32_MATRIX_TFLOPS, 4)})
     suite["m_sweep_K2048_E256_k8"] = sweep
     log("m sweep done")
 
@@ -148,8 +158,17 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
         ties.append({"M": m, "variant": dr.auto_variant(m, 4096, 512), "us": round(ms * 1e3, 2),
                      "us_host_bound": round(ms_e * 1e3, 2),
                      "tokens_per_s": round(m / (ms * 1e-3), 1),
-                     "tflops": round(2.0 * m * 4096 * 512 / (ms * 1e-3) / 1e12, 2)})
+                     "tflops": round(2.0 * m * 4096 * 512 / (ms * 1e-3) / 1e12, 2),
+                     "frac_fp32_peak": round(2.0 * m * 4096 * 512 / (ms * 1e-3) / 1e12 / PEAK_FP32_MATRIX_TFLOPS,
+                                             4)})
     suite["ties_K4096_E512_k10_bf16_logits"] = ties
+    ids_t, _, _, mg_t = dr.route(xt, Wt, 10, logit_dtype="bf16")
+    ut = dr.margins_to_numpy(mg_t)["ulps"]
+    suite["ties_K4096_E512_k10_margins_M4096"] = {
+        "tie_rate": round(float(np.mean(ut == 0)), 4), "within_one_step": round(float(np.mean(ut <= 1)), 4),
+        "ulps_hist": _ulps_hist(np, ut)}
+    checks["ties"] = (xt[:240].cpu().numpy(), Wt.cpu().numpy(), ids_t[:240].cpu().numpy(),
+                      mg_t[:240].cpu().numpy())
 
     # the router as a plain bf16 linear layer (logits from the bf16 GEMM,
     # rounded to bf16, then the same selection), beside the fp32 arm
@@ -265,7 +284,7 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
         "frac_hbm": round(byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     del Wg, xb_r
     log("grouped expert GEMM done")
-    return suite
+    return suite, checks
 
 
 def main():
@@ -372,7 +391,9 @@ def main():
 
     # M-invariance and oracle parity on sampled rows (outside the timed region)
     ids_full = out[0].cpu().numpy()
+    w_full = out[1].cpu().numpy()
     lg_full = out[2].cpu().numpy()
+    mg_full = dr.margins_to_numpy(out[3])
     inv = True
     for m_small in (1, 19, 65, 75, 1024, 4096):
         ids_s, _, lg_s, _ = dr.route(xd[:m_small].contiguous(), Wd, TOPK)
@@ -414,11 +435,16 @@ def main():
         "settle": {"steps": settle_blocks * 20,
                    "note": "untimed steps before the warm-up, until two blocks of 20 agree within 1%"},
         "m_invariance": inv,
+        "margins": {"tie_rate": round(float(np.mean(mg_full["ulps"] == 0)), 4),
+                    "within_one_step": round(float(np.mean(mg_full["ulps"] <= 1)), 4),
+                    "ulps_hist": _ulps_hist(np, mg_full["ulps"])},
     }
 
     if not args.no_suite:
         del out, lg_only
-        result["suite"] = measure_suite(dr, wl, torch, np, xd, Wd, stream)
+        result["suite"], checks = measure_suite(dr, wl, torch, np, xd, Wd, stream)
+    else:
+        checks = {}
 
     if not args.no_cpu_baseline:
         import oracle
@@ -428,12 +454,23 @@ def main():
         t0 = time.perf_counter()
         rids, rw, rlg, rmg = oracle.route(x[:sample], W, TOPK, nthreads=nthreads)
         dt = time.perf_counter() - t0
+        # every output bit for bit: ids, weights, logits, margin records
         parity = bool(np.array_equal(rids, ids_full[:sample]) and
-                      np.array_equal(rlg.view(np.uint32), lg_full[:sample].view(np.uint32)))
+                      np.array_equal(rw.view(np.uint32), w_full[:sample].view(np.uint32)) and
+                      np.array_equal(rlg.view(np.uint32), lg_full[:sample].view(np.uint32)) and
+                      np.array_equal(rmg.view(np.uint8), mg_full[:sample].view(np.uint8)))
         result["cpu_baseline"] = {"value": round(sample / dt, 1), "unit": "tokens/s", "cores": nthreads,
                                   "kind": "oracle",
                                   "sample": f"all {sample} tokens of the workload, one oracle call, wall clock"}
         result["oracle_parity"] = parity
+        result["oracle_ulps_hist_equal"] = _ulps_hist(np, rmg["ulps"]) == result["margins"]["ulps_hist"]
+        if "ties" in checks:
+            # the tie-heavy router's first 240 tokens (bf16 logits) against the oracle
+            xt240, Wt_h, ids_t, mg_t = checks["ties"]
+            tids, _, _, tmg = oracle.route(xt240, Wt_h, 10, logits_bf16=True, nthreads=nthreads)
+            result["oracle_parity_ties_M240"] = bool(np.array_equal(tids, ids_t) and
+                                                     np.array_equal(tmg.view(np.uint8).reshape(-1),
+                                                                    mg_t.view(np.uint8).reshape(-1)))
     print(json.dumps(result), flush=True)
 
 
