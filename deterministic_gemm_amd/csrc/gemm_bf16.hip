@@ -348,23 +348,30 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
 }
 
 // The tile is chosen from the shape (a performance choice only: every
-// configuration runs the same per-output instruction sequence).  Narrow tiles
-// with deep K stages for small batches (more workgroups stream W at once);
-// otherwise the largest tile whose count still covers the CUs once: 256 x 256
-// (eight 128 x 64 wavefront tiles, K in stages of 64), then 256 x 128 (eight
-// 64 x 64), then 128 x 128 (eight 32 x 64, K in stages of 128).  Measured at
-// K = N = 4096 with the configurations interleaved: M = 4096 130 us (256 x
-// 256), M = 2048 90 us (256 x 128), M = 1024 54 us (128 x 128).
+// configuration runs the same per-output instruction sequence): the smallest
+// tile whose count still fits the CUs, since a launch whose tiles all run at
+// once takes about one tile's time.  In order: 32 x 32 (4 wavefronts, K in
+// stages of 128 x 4) while there are at most two tiles per CU; 64 x 64 (4
+// wavefronts, 128 x 3), 64 x 128 (8 wavefronts of 16 x 64, 64 x 2), 128 x
+// 128 (8 of 32 x 64, 128 x 2) and 256 x 128 (8 of 64 x 64, 64 x 3) while
+// their tiles fit the CUs once; else 256 x 256 (8 of 128 x 64, 64 x 2).
+// Measured against the best of the six at 30 shapes (M = 192..6144 at K = N
+// = 4096, N = 256..14336): within ~1 us or 2% everywhere; e.g. K = N = 4096:
+// M = 256 38 us, 512 43, 1024 56, 2048 90, 3072 124, 4096 142; K = 2048, N =
+// 256: M = 1024 13 us, 8192 25.
 template <class OutT>
 static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
                                   hipStream_t stream) {
-  if (M <= 128) return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>, OutT>(x, W, out, M, K, N, stream);
   const int64_t cus = device_cus();
-  const int64_t mt = (M + 255) / 256;
-  if (N % 256 == 0 && mt * (N / 256) >= cus)
-    return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2>, OutT>(x, W, out, M, K, N, stream);
-  if (mt * (N / 128) >= cus) return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>, OutT>(x, W, out, M, K, N, stream);
-  return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>, OutT>(x, W, out, M, K, N, stream);
+  const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * (N / bn); };
+  if (M <= 128 || tiles(32, 32) <= 2 * cus)
+    return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>, OutT>(x, W, out, M, K, N, stream);
+  if (tiles(64, 64) <= cus) return launch_gemm_c<GemmCfg<64, 64, 2, 2, 128, 3>, OutT>(x, W, out, M, K, N, stream);
+  if (tiles(64, 128) <= cus) return launch_gemm_c<GemmCfg<64, 128, 4, 2, 64, 2>, OutT>(x, W, out, M, K, N, stream);
+  if (tiles(128, 128) <= cus) return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>, OutT>(x, W, out, M, K, N, stream);
+  if (tiles(256, 128) <= cus || N % 256 != 0)
+    return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>, OutT>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2>, OutT>(x, W, out, M, K, N, stream);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K, int64_t N,

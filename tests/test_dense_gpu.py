@@ -1,7 +1,7 @@
 """Batch-invariant dense bf16 GEMM and the shared-expert gate dot on the GPU.
 
-GEMM: rows bit-identical across M in {19, 65, 75, 512, 4096} and across row
-offsets inside a batch; every sampled output within 1e-2 absolute of the
+GEMM: rows bit-identical across M (19 to 4096, every tile configuration) and
+across row offsets inside a batch; every sampled output within 1e-2 absolute of the
 exact product (the oracle's fp64 evaluation), the tolerance the matrix core's
 internal order allows.  Gate dot: the canonical order with one output, bit
 for bit against the oracle, across M.
@@ -30,9 +30,11 @@ def test_gemm_rows_invariant_across_m_and_close_to_exact(dense):
     xd, Wd = dev_bf16_bits(xb), dev_bf16_bits(Wb)
     note("gemm M=4096")
     full = dr.gemm_bf16(xd, Wd).cpu().numpy()
-    # the sweep sizes plus 1024, 2048 and 3000: every tile configuration
-    # (32 x 32, 128 x 128, 256 x 128 with a ragged last tile, 256 x 256)
-    for M in sorted(set(wl.DENSE_MS) | {1024, 2048, 3000}):
+    # the sweep sizes plus others so that, on a 256-CU device, every tile
+    # configuration runs: 32 x 32 (M <= 128), 64 x 64 (200, 256), 64 x 128
+    # (512), 128 x 128 (1000, 1024), 256 x 128 (2048), 256 x 256 (3000, 4096),
+    # several with a ragged last tile
+    for M in sorted(set(wl.DENSE_MS) | {200, 256, 1000, 1024, 2048, 3000}):
         note(f"gemm M={M}")
         out = dr.gemm_bf16(xd[:M].contiguous(), Wd).cpu().numpy()
         assert f32_equal_bits(out, full[:M]), f"M={M} rows differ from the M=4096 run"
@@ -59,10 +61,12 @@ def test_gemm_row_offsets(dense):
 def test_gemm_small_shapes_close_to_exact():
     dr = require_gpu()
     rng = np.random.default_rng(3)
-    # every tile configuration, partial K stages, ragged M tiles (the last two
-    # take 256 x 128 and 256 x 256 tiles on a 256-CU device)
+    # partial K stages and ragged M tiles in every tile configuration (on a
+    # 256-CU device: 32 x 32 for the first six, then 64 x 64, 64 x 128,
+    # 128 x 128, 256 x 128 and twice 256 x 256)
     for (M, K, N) in ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
-                      (1500, 160, 256), (2100, 96, 4096), (4100, 160, 4096)):
+                      (1500, 160, 256), (200, 160, 4096), (450, 96, 4096), (900, 224, 4096), (1800, 96, 4096),
+                      (2100, 96, 4096), (4100, 160, 4096)):
         xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
         Wb = wl.to_bf16_bits(rng.standard_normal((K, N)).astype(np.float32))
         note(f"gemm small {M}x{K}x{N}")
