@@ -338,11 +338,14 @@ static hipError_t launch_grouped_c(const uint16_t *x, int64_t Mx, const int32_t 
 hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
                                     const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N,
                                     float *out, hipStream_t stream) {
-  // the dense kernel's large tile: at 65536 rows x 2048 x 1024 over 256
-  // experts of 193-324 rows it beats 128 x 128 tiles (eight 32 x 64
-  // wavefront tiles) by ~12%; configurations with more stages in flight
-  // need more than the 256 registers a wavefront has here
-  if (N % 256 == 0)
+  // From 128 rows per expert on average, the dense kernel's large tile: at
+  // 65536 rows x 2048 x 1024 over 256 experts of 193-324 rows it beats 128 x
+  // 128 tiles (eight 32 x 64 wavefront tiles) by ~12% (configurations with
+  // more stages in flight need more than the 256 registers a wavefront has
+  // here).  Below that the weights dominate and 128 x 128 tiles stream them
+  // faster: 24 vs 48 us at 8 rows, 171 vs 194 us at 512 rows (864 MiB of
+  // weights), 223 vs 250 us at 16384 rows; even at 32768.
+  if (N % 256 == 0 && P >= 128 * E)
     return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
   return launch_grouped_c<GemmCfg<128, 128, 4, 2, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
 }

@@ -32,8 +32,10 @@ def _routes_and_groups(dr, M, k, E, seed):
     return ids, off, rows, pos
 
 
+# 128 x 128 tiles below 128 rows per expert on average, 256 x 256 from there
+# (the last case: ragged groups of ~300 rows and a partial K stage)
 @pytest.mark.parametrize("M,k,E,K,N", [(1, 1, 1, 32, 128), (5, 2, 8, 96, 128), (300, 4, 16, 256, 256),
-                                       (700, 8, 64, 160, 384), (2048, 8, 256, 2048, 256)])
+                                       (700, 8, 64, 160, 384), (2048, 8, 256, 2048, 256), (1200, 8, 32, 160, 256)])
 def test_grouped_matches_dense_rows_and_oracle(M, k, E, K, N):
     dr = require_gpu()
     g = np.random.default_rng(M + E)
@@ -82,7 +84,8 @@ def test_grouped_matches_oracle_reference_whole():
 
 def test_grouped_rows_do_not_depend_on_the_batch():
     """A token routed alone-ish (37 tokens) and inside 4096 tokens: its rows
-    sit in groups of different sizes at different offsets, with the same bits."""
+    sit in groups of different sizes at different offsets, with the same bits
+    (the two batches also run different tile configurations)."""
     dr = require_gpu()
     M, k, E, K, N = 4096, 8, 64, 512, 256
     g = np.random.default_rng(9)
