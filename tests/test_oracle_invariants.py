@@ -226,3 +226,25 @@ def test_invalid_arguments_rejected():
         oracle.route(x, W, 0)
     ids, w, lg, mg = oracle.route(x[:0], W, 2)  # M = 0 is fine
     assert ids.shape == (0, 2)
+
+
+@pytest.mark.parametrize("nb,G", [(8, 2), (8, 4), (8, 8), (4, 2), (16, 4)])
+def test_k_shards_are_aligned_subtrees(nb, G):
+    """With nb blocks and G shards of nb/G blocks (powers of two), the logits of
+    each K shard are one aligned subtree of the canonical tree, so adding the
+    shard logits pairwise, adjacent shards first, rebuilds the full logits
+    bit for bit.  The expert shards' logits are the full logits' columns.  (The
+    identity sharded routing relies on; a tree that carried odd partials up
+    differently, or a chain over blocks, would fail it.)"""
+    K, E, M = 256 * nb, 8, 24
+    g = np.random.default_rng(nb * 10 + G)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    W = (g.standard_normal((K, E)) * 0.05).astype(np.float32)
+    full = oracle.route(x, W, 2)[2]
+    ks = K // G
+    parts = [oracle.route(x[:, i * ks:(i + 1) * ks], W[i * ks:(i + 1) * ks], 2)[2] for i in range(G)]
+    while len(parts) > 1:
+        parts = [(parts[i] + parts[i + 1]).astype(np.float32) for i in range(0, len(parts), 2)]
+    assert np.array_equal(parts[0].view(np.uint32), full.view(np.uint32))
+    cols = np.concatenate([oracle.route(x, np.ascontiguousarray(W[:, c:c + 4]), 1)[2] for c in (0, 4)], axis=1)
+    assert np.array_equal(cols.view(np.uint32), full.view(np.uint32))
