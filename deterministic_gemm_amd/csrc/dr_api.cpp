@@ -43,11 +43,10 @@ constexpr int64_t kMaxM = int64_t(1) << 22;
 // change and shows it cannot move a bit.
 constexpr int64_t kTiledMinM = 48;
 // Calls that ask for the logits run as two kernels, the logits then the
-// selection.  Up to kNarrowMaxM tokens the logits spread over small (token,
-// expert) tiles with the K groups split between wavefronts; above it they use
-// 64 x 64 or 64 x 128 tiles (measured crossover at K=2048, E=256: between
-// M=1024 and M=2048).  Without the logits output the fused kernels run.
-constexpr int64_t kNarrowMaxM = 1280;
+// selection.  Up to drk::narrow_max_m(E, K) tokens the logits spread over
+// small (token, expert) tiles with the K groups split between wavefronts;
+// above it they use 64 x 64 or 64 x 128 tiles.  Without the logits output the
+// fused kernels run.
 
 dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
                      int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
@@ -115,9 +114,10 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
 extern "C" {
 
 dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits) {
-  if (M > kNarrowMaxM && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
+  const int64_t narrow_max = drk::narrow_max_m(E, K);
+  if (M > narrow_max && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
   if (M <= drk::tiny_max_m() && drk::tiny_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_TINY;
-  if (M <= kNarrowMaxM && drk::narrow_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_NARROW;
+  if (M <= narrow_max && drk::narrow_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_NARROW;
   if (M >= kTiledMinM && drk::tiled_supports(E, K)) return DR_VARIANT_TILED;
   return DR_VARIANT_ROWWISE;
 }
@@ -160,7 +160,7 @@ dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, 
   L.logit_bf16 = logit_dtype == DR_BF16;
   L.logits = logits;
   L.stream = static_cast<hipStream_t>(stream);
-  const bool split = M > kNarrowMaxM && drk::split_supports(E, K, true, true);
+  const bool split = M > drk::narrow_max_m(E, K) && drk::split_supports(E, K, true, true);
   const bool tiny = M <= drk::tiny_max_m() && drk::tiny_supports(E, K, true, true);
   return device_status(split  ? drk::launch_route_logits(L)
                        : tiny ? drk::launch_route_tiny_logits(L)

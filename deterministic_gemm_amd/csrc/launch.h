@@ -38,6 +38,7 @@ hipError_t launch_moe_combine(const void *y, int y_bf16, int64_t P, const float 
                               int64_t M, int k, int64_t D, float *out, hipStream_t stream);
 
 // Compute units of the current device (256 if the query fails).
+int64_t narrow_max_m(int64_t E, int64_t K);
 int device_cus();
 
 hipError_t launch_route_rowwise(const RouteLaunch &L);

@@ -249,6 +249,24 @@ static hipError_t launch_narrow_c(const RouteLaunch &L) {
   return launch_narrow_cm<C, 4>(L);
 }
 
+// Two parts (two K-groups, 1024 < K <= 2048): the smallest of three tiles
+// whose workgroups all fit on the CUs at once (each takes 66-76 KiB of LDS,
+// two per CU) -- 16 x 16 tokens x experts (16-step chunks, four stages), 32 x
+// 16 (16-step chunks, three stages), then 32 x 32 (8-step chunks, four
+// stages), which also serves larger batches.  A larger tile gives each
+// wavefront two or four independent chains and reads fewer operand bytes per
+// product; a smaller one fills the CUs sooner.  Measured at K = 2048, logits
+// kernel alone: E = 256: M = 512 16 us, 1024 24 us (16 x 16: 30), 2048 38 us
+// (the split kernels: 44); E = 512: M = 1024 35 us (16 x 16: 56).
+template <int E>
+static hipError_t launch_narrow_two_parts(const RouteLaunch &L) {
+  const int64_t slots = 2 * static_cast<int64_t>(device_cus());
+  const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
+  if (wgs(16, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4>>(L);
+  if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, 16, 3>>(L);
+  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, 8, 4>>(L);
+}
+
 // Parts by group count.  Four stages per wavefront: deeper rings measured
 // slower (fewer workgroups fit on a CU).
 template <int E, int AT, int BT, int KC>
@@ -256,8 +274,19 @@ static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
   if (G >= 4) return launch_narrow_c<NarrowCfg<E, AT, BT, 4, KC, 4>>(L);
-  if (G >= 2) return launch_narrow_c<NarrowCfg<E, AT, BT, 2, KC, 4>>(L);
+  if (G >= 2) return launch_narrow_two_parts<E>(L);
   return launch_narrow_c<NarrowCfg<E, AT, BT, 1, KC, 4>>(L);
+}
+
+// The largest batch the narrow family takes before the split kernels: with
+// two parts and E in {256, 512}, as long as its 32 x 32 tiles fit on the CUs
+// at once (M = 2048 at E = 256, 1024 at E = 512 on 256 CUs); otherwise 1280,
+// measured at K = 2048, E = 256 with 16 x 16 tiles.
+int64_t narrow_max_m(int64_t E, int64_t K) {
+  const int64_t nb = (K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  if (G == 2 && (E == 256 || E == 512)) return 2 * static_cast<int64_t>(device_cus()) * 32 / (E / 32);
+  return 1280;
 }
 
 bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
