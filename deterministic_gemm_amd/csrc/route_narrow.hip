@@ -249,43 +249,44 @@ static hipError_t launch_narrow_c(const RouteLaunch &L) {
   return launch_narrow_cm<C, 4>(L);
 }
 
-// Two parts (two K-groups, 1024 < K <= 2048): the smallest of three tiles
-// whose workgroups all fit on the CUs at once (each takes 66-76 KiB of LDS,
-// two per CU) -- 16 x 16 tokens x experts (16-step chunks, four stages), 32 x
-// 16 (16-step chunks, three stages), then 32 x 32 (8-step chunks, four
-// stages), which also serves larger batches.  A larger tile gives each
-// wavefront two or four independent chains and reads fewer operand bytes per
-// product; a smaller one fills the CUs sooner.  Measured at K = 2048, logits
-// kernel alone: E = 256: M = 512 16 us, 1024 24 us (16 x 16: 30), 2048 38 us
-// (the split kernels: 44); E = 512: M = 1024 35 us (16 x 16: 56).
+// With two to four K-groups (1024 < K <= 4096): the smallest of three tiles
+// whose workgroups all fit on the CUs at once, two per CU (66-76 KiB of LDS
+// each) --
+//   16 x 16 tokens x experts: one part per group (two, or four with a
+//     two-stage ring), 16-step chunks;
+//   32 x 16: two parts, 16-step chunks, three stages;
+//   32 x 32: two parts, 8-step chunks, four stages (also for larger batches).
+// A larger tile gives each wavefront two or four independent chains and reads
+// fewer operand bytes per product; a smaller one fills the CUs sooner.  Logits
+// kernel alone, bits identical across the tiles: K = 2048, E = 256: M = 1024
+// 24 us (16 x 16 tiles: 30), 2048 38 us (the split kernels: 44); K = 4096, E =
+// 512: M = 240 22 us (four parts with four stages: 31), 512 40 us (59), 1024
+// 65 us (115).  More groups keep one part per group and four stages.
 template <int E>
-static hipError_t launch_narrow_two_parts(const RouteLaunch &L) {
+static hipError_t launch_narrow_e(const RouteLaunch &L) {
+  const int64_t nb = (L.K + 255) / 256;
+  const int64_t G = (nb + 3) / 4;
+  if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4>>(L);
+  if (G > 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4>>(L);
   const int64_t slots = 2 * static_cast<int64_t>(device_cus());
   const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
-  if (wgs(16, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4>>(L);
+  if (wgs(16, 16) <= slots) {
+    if (G == 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4>>(L);
+  }
   if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, 16, 3>>(L);
   return launch_narrow_c<NarrowCfg<E, 2, 2, 2, 8, 4>>(L);
 }
 
-// Parts by group count.  Four stages per wavefront: deeper rings measured
-// slower (fewer workgroups fit on a CU).
-template <int E, int AT, int BT, int KC>
-static hipError_t launch_narrow_e(const RouteLaunch &L) {
-  const int64_t nb = (L.K + 255) / 256;
-  const int64_t G = (nb + 3) / 4;
-  if (G >= 4) return launch_narrow_c<NarrowCfg<E, AT, BT, 4, KC, 4>>(L);
-  if (G >= 2) return launch_narrow_two_parts<E>(L);
-  return launch_narrow_c<NarrowCfg<E, AT, BT, 1, KC, 4>>(L);
-}
-
-// The largest batch the narrow family takes before the split kernels: with
-// two parts and E in {256, 512}, as long as its 32 x 32 tiles fit on the CUs
-// at once (M = 2048 at E = 256, 1024 at E = 512 on 256 CUs); otherwise 1280,
-// measured at K = 2048, E = 256 with 16 x 16 tiles.
+// The largest batch the narrow family takes before the split kernels: at
+// 1024 < K <= 4096 with E in {256, 512}, as long as its 32 x 32 tiles fit on
+// the CUs at once (M = 2048 at E = 256, 1024 at E = 512 on 256 CUs; measured
+// crossovers at K = 2048 and 4096); otherwise 1280, measured at K = 2048, E =
+// 256 with 16 x 16 tiles.
 int64_t narrow_max_m(int64_t E, int64_t K) {
   const int64_t nb = (K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
-  if (G == 2 && (E == 256 || E == 512)) return 2 * static_cast<int64_t>(device_cus()) * 32 / (E / 32);
+  if (G >= 2 && G <= 4 && (E == 256 || E == 512)) return 2 * static_cast<int64_t>(device_cus()) * 32 / (E / 32);
   return 1280;
 }
 
@@ -296,10 +297,10 @@ bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
 
 hipError_t launch_route_narrow_logits(const RouteLaunch &L) {
   switch (L.E) {
-    case 64: return launch_narrow_e<64, 1, 1, 16>(L);
-    case 128: return launch_narrow_e<128, 1, 1, 16>(L);
-    case 256: return launch_narrow_e<256, 1, 1, 16>(L);
-    case 512: return launch_narrow_e<512, 1, 1, 16>(L);
+    case 64: return launch_narrow_e<64>(L);
+    case 128: return launch_narrow_e<128>(L);
+    case 256: return launch_narrow_e<256>(L);
+    case 512: return launch_narrow_e<512>(L);
     default: return hipErrorInvalidValue;
   }
 }

@@ -203,13 +203,15 @@ def test_auto_variant_is_a_function_of_shape(L):
     assert dr.auto_variant(40, 2048, 1024) == "rowwise"
     assert dr.auto_variant(19, 8192, 256) == "narrow"   # K above the vector family's 4096
     # large batches that ask for the logits take the two-kernel family: at
-    # K = 2048 above 2048 tokens for E = 256 and 1024 for E = 512 (where the
-    # narrow family's largest tile stops fitting 256 CUs at once), above 1280
-    # at other K
+    # 1024 < K <= 4096 above 2048 tokens for E = 256 and 1024 for E = 512
+    # (where the narrow family's largest tile stops fitting 256 CUs at once),
+    # above 1280 at other K
     assert dr.auto_variant(8192, 2048, 256) == "split"
     assert [dr.auto_variant(M, 2048, 256) for M in (1280, 2048, 2049)] == ["narrow", "narrow", "split"]
     assert [dr.auto_variant(M, 2048, 512) for M in (1024, 1025)] == ["narrow", "split"]
-    assert [dr.auto_variant(M, 4096, 512) for M in (240, 1280, 1281)] == ["narrow", "narrow", "split"]
+    assert [dr.auto_variant(M, 4096, 512) for M in (240, 1024, 1025)] == ["narrow", "narrow", "split"]
+    assert [dr.auto_variant(M, 8192, 256) for M in (1280, 1281)] == ["narrow", "split"]
+    assert [dr.auto_variant(M, 1024, 256) for M in (1280, 1281)] == ["narrow", "split"]
     assert dr.auto_variant(8192, 2048, 256, logits=False) == "tiled"
     assert dr.auto_variant(8192, 2048, 256, x_dtype="bf16") == "tiled"
     assert dr.auto_variant(8192, 2046, 256) == "tiled"

@@ -107,22 +107,25 @@ def test_sweep_forced_variants(dr, router_w, sweep, variant):
         assert_route_equal(got, tuple(r[:M] for r in ref), what=f"{variant} M={M}")
 
 
-@pytest.mark.parametrize("Ex,M", [(256, 600), (256, 1500), (256, 2048), (512, 300), (512, 700), (128, 2000),
-                                  (64, 3000)])
-def test_narrow_tiles_match_oracle(dr, Ex, M):
-    """The narrow family's three tiles at K = 2048 (16 x 16, 32 x 16 and 32 x
-    32 tokens x experts, picked by how many workgroups fit on the CUs), each
-    with a ragged last token tile: every output equals the oracle's, and the
-    split family's where it exists."""
-    W = wl.router_weights(K, Ex) if Ex == E else (np.random.default_rng(Ex).standard_normal((K, Ex)) *
-                                                  0.02).astype(np.float32)
-    x = wl.sweep_x(M, K)
-    note(f"narrow tiles E={Ex} M={M}")
+@pytest.mark.parametrize("Kx,Ex,M", [(2048, 256, 600), (2048, 256, 1500), (2048, 256, 2048), (2048, 512, 300),
+                                     (2048, 512, 700), (2048, 128, 2000), (2048, 64, 3000), (4096, 512, 240),
+                                     (4096, 512, 500), (4096, 512, 1000), (4096, 256, 1000), (3072, 256, 100),
+                                     (3000, 256, 700)])
+def test_narrow_tiles_match_oracle(dr, Kx, Ex, M):
+    """The narrow family's tiles (16 x 16 with two or four parts, 32 x 16 and
+    32 x 32 tokens x experts, picked by how many workgroups fit on the CUs),
+    each with a ragged last token tile, at two, three and four K-groups: every
+    output equals the oracle's, and the split family's where it exists."""
+    rng = np.random.default_rng(Kx + Ex)
+    W = wl.router_weights(Kx, Ex) if Ex == E else (rng.standard_normal((Kx, Ex)) * 0.02).astype(np.float32)
+    x = wl.sweep_x(M, Kx)
+    note(f"narrow tiles K={Kx} E={Ex} M={M}")
     got = gpu_route_np(dr, dev(x), dev(W), TOPK, variant="narrow")
-    assert_route_equal(got, oracle_route(x, W, TOPK), what=f"narrow E={Ex} M={M}")
+    assert_route_equal(got, oracle_route(x, W, TOPK), what=f"narrow K={Kx} E={Ex} M={M}")
     if Ex in (256, 512):
-        note(f"split family E={Ex} M={M}")
-        assert_route_equal(gpu_route_np(dr, dev(x), dev(W), TOPK, variant="split"), got, what=f"split E={Ex} M={M}")
+        note(f"split family K={Kx} E={Ex} M={M}")
+        assert_route_equal(gpu_route_np(dr, dev(x), dev(W), TOPK, variant="split"), got,
+                           what=f"split K={Kx} E={Ex} M={M}")
 
 
 def test_bf16_input_storage_is_bit_identical(dr, router_w, sweep):
