@@ -43,18 +43,27 @@
 extern "C" {
 #endif
 
-typedef enum dr_status {
+/* Under C++ the enumerations take a fixed 32-bit underlying type, so any int
+ * a caller passes is a value of the type and the range checks below are well
+ * defined; C sees plain enums of the same size. */
+#ifdef __cplusplus
+#define DR_ENUM(name) enum name : int32_t
+#else
+#define DR_ENUM(name) enum name
+#endif
+
+typedef DR_ENUM(dr_status) {
   DR_OK = 0,
   DR_ERR_INVALID = 1,      /* NULL required pointer, bad size, k > E, misaligned pointer */
   DR_ERR_UNSUPPORTED = 2,  /* a shape the GPU path does not implement (see each call) */
   DR_ERR_DEVICE = 3        /* a HIP call or launch failed */
 } dr_status;
 
-typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+typedef DR_ENUM(dr_dtype) { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
 
 /* Kernel families for dr_route.  All produce identical bits; AUTO picks one
  * from M and E only.  Forcing one is a test seam, never a numeric switch. */
-typedef enum dr_variant {
+typedef DR_ENUM(dr_variant) {
   DR_VARIANT_AUTO = 0,
   DR_VARIANT_ROWWISE = 1, /* few tokens per workgroup, vector FMA (small M) */
   DR_VARIANT_TILED = 2,   /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
