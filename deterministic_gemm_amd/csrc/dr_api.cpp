@@ -116,7 +116,7 @@ extern "C" {
 dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits) {
   const int64_t narrow_max = drk::narrow_max_m(E, K);
   if (M > narrow_max && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
-  if (M <= drk::tiny_max_m() && drk::tiny_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_TINY;
+  if (M <= drk::tiny_max_m(E, K) && drk::tiny_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_TINY;
   if (M <= narrow_max && drk::narrow_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_NARROW;
   if (M >= kTiledMinM && drk::tiled_supports(E, K)) return DR_VARIANT_TILED;
   return DR_VARIANT_ROWWISE;
@@ -161,7 +161,7 @@ dr_status dr_route_logits(const float *x, const float *W, int64_t M, int64_t K, 
   L.logits = logits;
   L.stream = static_cast<hipStream_t>(stream);
   const bool split = M > drk::narrow_max_m(E, K) && drk::split_supports(E, K, true, true);
-  const bool tiny = M <= drk::tiny_max_m() && drk::tiny_supports(E, K, true, true);
+  const bool tiny = M <= drk::tiny_max_m(E, K) && drk::tiny_supports(E, K, true, true);
   return device_status(split  ? drk::launch_route_logits(L)
                        : tiny ? drk::launch_route_tiny_logits(L)
                               : drk::launch_route_narrow_logits(L),

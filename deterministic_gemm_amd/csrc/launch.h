@@ -49,7 +49,7 @@ bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
 hipError_t launch_route_tiny(const RouteLaunch &L);
 hipError_t launch_route_tiny_logits(const RouteLaunch &L);
 bool tiny_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
-int64_t tiny_max_m();
+int64_t tiny_max_m(int64_t E, int64_t K);
 hipError_t launch_route_narrow(const RouteLaunch &L);
 hipError_t launch_route_narrow_logits(const RouteLaunch &L);
 bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);

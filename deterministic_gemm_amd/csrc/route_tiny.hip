@@ -23,7 +23,12 @@
 
 namespace drk {
 
-constexpr int64_t kTinyMaxM = 32;  // measured at K=2048, E=256: 14.6 us at M=32 (narrow 19.8), 22.8 at M=48 (19.9)
+// Batches this family takes: up to 48 tokens when a workgroup's W slice
+// leaves room for six tokens' x (K <= 2048) and E <= 512, else 32.  Measured at K=2048,
+// E=256, logits kernel alone: 10.1 us at M=32 (four tokens per workgroup),
+// 12.2 us at M=40..48 with six (four: 19.0; the narrow family: 14.7), 14.9 us
+// at M=64 with eight (narrow: 14.8).
+constexpr int64_t kTinyMaxM = 32, kTinyMaxM6 = 48;
 
 template <int P, int T>
 struct TinyCfg {
@@ -133,6 +138,9 @@ template <int P>
 static hipError_t launch_tiny_p(const RouteLaunch &L) {
   if (L.M <= 1) return launch_tiny_pt<P, 1>(L);
   if (L.M <= 2) return launch_tiny_pt<P, 2>(L);
+  if constexpr (P <= 8) {
+    if (L.M > kTinyMaxM) return launch_tiny_pt<P, 6>(L);
+  }
   return launch_tiny_pt<P, 4>(L);
 }
 
@@ -155,6 +163,6 @@ hipError_t launch_route_tiny(const RouteLaunch &L) {
   return launch_route_select(L);
 }
 
-int64_t tiny_max_m() { return kTinyMaxM; }
+int64_t tiny_max_m(int64_t E, int64_t K) { return ((K + 255) / 256 <= 8 && E <= 512) ? kTinyMaxM6 : kTinyMaxM; }
 
 }  // namespace drk

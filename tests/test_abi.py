@@ -196,9 +196,11 @@ def test_auto_variant_is_a_function_of_shape(L):
     switches = sum(1 for a, b in zip(picks, picks[1:]) if a != b)
     assert switches == 1
     assert dr.auto_variant(8192, 2048, 1024) == "rowwise"
-    # small batches that ask for the logits: the vector-ALU family up to 32
-    # tokens, then narrow tiles (the switch lies inside the m-scan range)
-    assert [dr.auto_variant(M, 2048, 256) for M in (1, 19, 32, 33, 80)] == ["tiny"] * 3 + ["narrow"] * 2
+    # small batches that ask for the logits: the vector-ALU family up to 48
+    # tokens at K <= 2048 and E <= 512 (else 32), then narrow tiles (the
+    # switch lies inside the m-scan range)
+    assert [dr.auto_variant(M, 2048, 256) for M in (1, 19, 32, 33, 48, 49, 80)] == ["tiny"] * 5 + ["narrow"] * 2
+    assert [dr.auto_variant(M, 4096, 256) for M in (32, 33)] == ["tiny", "narrow"]
     assert dr.auto_variant(19, 2048, 1024) == "tiny"
     assert dr.auto_variant(40, 2048, 1024) == "rowwise"
     assert dr.auto_variant(19, 8192, 256) == "narrow"   # K above the vector family's 4096
