@@ -4,6 +4,7 @@
 // the same canonical order.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -110,6 +111,25 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
 }
 
 }  // namespace
+
+namespace drk {
+
+// The CUs of the current device (the 64 x 128 tiles fill MI355X's 256 at
+// M = 8192, E = 256), queried once per device; 256 when no device answers.
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev >= 0 && dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace drk
 
 extern "C" {
 

@@ -19,8 +19,6 @@
 // one).  In bf16-logit mode the logits are stored rounded and the epilogue
 // selects on those stored values, which are the values the fused kernel
 // selects on.
-#include <atomic>
-
 #include "route_common.h"
 #include "lds_dma.h"
 #include "launch.h"
@@ -432,21 +430,6 @@ static hipError_t launch_logits_c(const RouteLaunch &L) {
     if (span <= 8) return launch_logits_cm<C, 4>(L);
   }
   return launch_logits_cm<C, LMAX>(L);
-}
-
-// The CUs of the current device (the 64 x 128 tiles fill MI355X's 256 at
-// M = 8192, E = 256), queried once per device; 256 when no device answers.
-int device_cus() {
-  static std::atomic<int> cached[64];
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 256;
-  if (dev >= 0 && dev < 64) {
-    const int c = cached[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
-  if (dev >= 0 && dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
 }
 
 // Batches up to this size select with one wavefront per token.
