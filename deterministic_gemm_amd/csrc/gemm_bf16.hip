@@ -114,6 +114,74 @@ __device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const
   }
 }
 
+// The same transfers through buffer descriptors (the path for operands under
+// 4 GiB).  A lane keeps one 32-bit byte offset per transfer for the whole
+// tile; each stage moves the descriptors' bases (scalar work) to K-step k0 and
+// shrinks their ranges to what is left of the operand.  A transfer whose
+// offset lies past the range reads zeros without touching memory (checked
+// per 4-byte word), which covers rows that read a zero row, W rows past K and
+// stages past the last; x units past K in a partial stage read the next row's
+// data, which no matrix step consumes.  Fewer registers than 64-bit
+// addresses, so deeper rings fit a wavefront's budget.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kGemmFarOff = 0xFFFFFFF0u;  // past every range
+
+__device__ __forceinline__ u32x4 gemm_rsrc(const void *base, int64_t nbytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint64_t n = nbytes <= 0 ? 0 : (nbytes >= kGemmFarOff ? kGemmFarOff : static_cast<uint64_t>(nbytes));
+  u32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));  // stride 0: a raw byte range
+  r[2] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(n));
+  r[3] = 0x00020000u;
+  return r;
+}
+
+// Every active lane moves the 16 bytes at byte offset voff of the descriptor's
+// range (zeros past it) to LDS address lds_base + 16 * lane; inline assembly
+// for the reason given at dma16.
+__device__ __forceinline__ void dma16_buf(uint32_t voff, u32x4 rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory");
+}
+
+template <class C>
+__device__ __forceinline__ void gemm_voffs(const int32_t (&arow)[C::PER], int K, int N, int n0, int wave, int lane,
+                                           uint32_t (&voff)[C::PER]) {
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const int p = (wave * C::PER + i) * 64 + lane;
+    if (p < C::AU) {
+      const int r = p / C::UA, up = p % C::UA;
+      const int u = up ^ C::swa(r);
+      voff[i] = arow[i] >= 0 ? static_cast<uint32_t>((static_cast<int64_t>(arow[i]) * K + 8 * u) * 2) : kGemmFarOff;
+    } else {
+      const int q = p - C::AU;
+      const int kr = q / C::UB, up = q % C::UB;
+      const int u = up ^ C::swb(kr);
+      voff[i] = static_cast<uint32_t>((static_cast<int64_t>(kr) * N + n0 + 8 * u) * 2);
+    }
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void gemm_issue_buf(const uint16_t *__restrict__ x, int64_t Mx,
+                                               const uint16_t *__restrict__ W, int K, int N,
+                                               const uint32_t (&voff)[C::PER], int st, int nst, int wave,
+                                               char *stage) {
+  const int64_t k0 = static_cast<int64_t>(st) * C::BK;
+  const bool live = st < nst;
+  const u32x4 xr = gemm_rsrc(x + k0, live ? (Mx * K - k0) * 2 : 0);
+  const u32x4 wr = gemm_rsrc(W + k0 * N, live ? (K - k0) * static_cast<int64_t>(N) * 2 : 0);
+#pragma unroll
+  for (int i = 0; i < C::PER; ++i) {
+    const uint32_t lds = __builtin_amdgcn_readfirstlane(
+        static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (wave * C::PER + i) * 1024)));
+    // a transfer is all x or all W (AU is a multiple of 64)
+    dma16_buf(voff[i], (wave * C::PER + i) * 64 < C::AU ? xr : wr, lds);
+  }
+}
+
 // Round to nearest even on the 16 dropped bits (NaN -> 0x7FC0).
 __device__ __forceinline__ uint16_t gemm_f32_to_bf16(float v) {
   const uint32_t u = __float_as_uint(v);
@@ -162,12 +230,12 @@ __device__ __forceinline__ void gemm_kstep(const char *As, const char *Bs, int k
 // tile) skips its LDS reads and matrix steps but still moves its share of the
 // transfers and meets every barrier; the dense kernel, whose only partial
 // tile is the last, measured faster without the branch.
-template <class C, class OutT = float, bool SKIP = false>
+template <class C, class OutT = float, bool SKIP = false, bool BUF = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
                                           int64_t Mx, const uint16_t *__restrict__ W, OutT *__restrict__ out,
                                           int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
   constexpr int FM = C::FM, FN = C::FN, S = C::S;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int nst = (K + C::BK - 1) / C::BK;
@@ -185,16 +253,23 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
   const int tj = ta >> 2, tq = ta & 3;
   int32_t arow[C::PER];
   gemm_arows<C>(rows, Mx, m0, mend, wave, lane, arow);
+  uint32_t voff[C::PER];
+  if constexpr (BUF) gemm_voffs<C>(arow, K, N, n0, wave, lane, voff);
+  const auto issue = [&](int st) {
+    char *stage = smem + (st % S) * C::STAGE;
+    if constexpr (BUF) gemm_issue_buf<C>(x, Mx, W, K, N, voff, st, nst, wave, stage);
+    else gemm_issue<C>(x, arow, W, K, N, n0, st, nst, wave, lane, stage);
+  };
 
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i) gemm_issue<C>(x, arow, W, K, N, n0, i, nst, wave, lane, smem + i * C::STAGE);
+  for (int i = 0; i < S - 1; ++i) issue(i);
 
   for (int st = 0; st < nst; ++st) {
     compiler_fence();
     wait_vmcnt<C::PER * (S - 2)>();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    gemm_issue<C>(x, arow, W, K, N, n0, st + S - 1, nst, wave, lane, smem + ((st + S - 1) % S) * C::STAGE);
+    issue(st + S - 1);
     const char *As = smem + (st % S) * C::STAGE;
     const char *Bs = As + C::ABYTES;
     const int nsub = (K - st * C::BK) < C::BK ? (K - st * C::BK) / 32 : C::BK / 32;
@@ -223,7 +298,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
     }
 }
 
-template <class C, class OutT>
+template <class C, class OutT, bool BUF>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ W,
                                                          OutT *__restrict__ out, int64_t M, int K,
@@ -235,7 +310,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
   // tiles that share 128-byte lines of W read them through one L2.
   const int nx = gridDim.x;
   const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
-  gemm_tile<C, OutT>(x, nullptr, M, W, out, m0, M, K, N, bx * C::BN, smem);
+  gemm_tile<C, OutT, false, BUF>(x, nullptr, M, W, out, m0, M, K, N, bx * C::BN, smem);
 }
 
 // Grouped (per-expert) product: expert e owns output rows [offsets[e],
@@ -253,7 +328,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 // or position, and the same bits as dr_gemm_bf16 of that row with W[e].
 constexpr int GG_EMAX = 1024;
 
-template <class C>
+template <class C, bool BUF>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t *__restrict__ x, int64_t Mx,
                                                                  const int32_t *__restrict__ rows,
                                                                  const uint16_t *__restrict__ W,
@@ -303,21 +378,31 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
     start += cnt[i];
   }
   __syncthreads();
-  const int e = found;
+  const int e = __builtin_amdgcn_readfirstlane(found);
   if (e < 0) return;  // past the last tile (uniform over the workgroup)
   const int64_t lo = offsets[e], mend = offsets[e + 1];
   if (lo < 0 || mend > P || mend < lo) return;  // inconsistent offsets: nothing is written outside out
   const int64_t m0 = lo + static_cast<int64_t>(tile - tstart[e]) * C::BM;
-  gemm_tile<C, float, true>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N,
-                            (slot % ncol) * C::BN, smem);
+  gemm_tile<C, float, true, BUF>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N,
+                                 (slot % ncol) * C::BN, smem);
+}
+
+// Buffer descriptors address 32-bit byte ranges: operands under 4 GiB take
+// them, larger ones the 64-bit addresses.
+static bool gemm_buf_ok(int64_t rows, int64_t K, int64_t N) {
+  return rows * K * 2 < kGemmFarOff && K * N * 2 < kGemmFarOff;
 }
 
 template <class C, class OutT = float>
 static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K,
                                 int64_t N, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(N / C::BN), static_cast<uint32_t>((M + C::BM - 1) / C::BM));
-  hipLaunchKernelGGL((gemm_bf16_kernel<C, OutT>), grid, dim3(C::NT), 0, stream, x, W, out, M, static_cast<int>(K),
-                     static_cast<int>(N));
+  if (gemm_buf_ok(M, K, N))
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, OutT, true>), grid, dim3(C::NT), 0, stream, x, W, out, M,
+                       static_cast<int>(K), static_cast<int>(N));
+  else
+    hipLaunchKernelGGL((gemm_bf16_kernel<C, OutT, false>), grid, dim3(C::NT), 0, stream, x, W, out, M,
+                       static_cast<int>(K), static_cast<int>(N));
   return hipGetLastError();
 }
 
@@ -330,8 +415,12 @@ static hipError_t launch_grouped_c(const uint16_t *x, int64_t Mx, const int32_t 
   const int64_t tiles = (P + C::BM - 1) / C::BM + E;
   const int64_t ncol = N / C::BN;
   const dim3 grid(static_cast<uint32_t>(8 * ((tiles + 7) / 8) * ncol));
-  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
-                     static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N), static_cast<int>(ncol));
+  if (gemm_buf_ok(Mx, K, N))
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C, true>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
+                       static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N), static_cast<int>(ncol));
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C, false>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
+                       static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N), static_cast<int>(ncol));
   return hipGetLastError();
 }
 
