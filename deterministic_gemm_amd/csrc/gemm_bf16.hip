@@ -26,6 +26,7 @@
 // one instruction spread over the LDS banks; writer and readers apply the same
 // swizzle.
 #include "lds_dma.h"
+#include "buf_dma.h"
 #include "launch.h"
 
 namespace drk {
@@ -123,28 +124,6 @@ __device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const
 // stages past the last; x units past K in a partial stage read the next row's
 // data, which no matrix step consumes.  Fewer registers than 64-bit
 // addresses, so deeper rings fit a wavefront's budget.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-constexpr uint32_t kGemmFarOff = 0xFFFFFFF0u;  // past every range
-
-__device__ __forceinline__ u32x4 gemm_rsrc(const void *base, int64_t nbytes) {
-  const uint64_t b = reinterpret_cast<uint64_t>(base);
-  const uint64_t n = nbytes <= 0 ? 0 : (nbytes >= kGemmFarOff ? kGemmFarOff : static_cast<uint64_t>(nbytes));
-  u32x4 r;
-  r[0] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
-  r[1] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));  // stride 0: a raw byte range
-  r[2] = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(n));
-  r[3] = 0x00020000u;
-  return r;
-}
-
-// Every active lane moves the 16 bytes at byte offset voff of the descriptor's
-// range (zeros past it) to LDS address lds_base + 16 * lane; inline assembly
-// for the reason given at dma16.
-__device__ __forceinline__ void dma16_buf(uint32_t voff, u32x4 rsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_base)
-               : "memory");
-}
-
 template <class C>
 __device__ __forceinline__ void gemm_voffs(const int32_t (&arow)[C::PER], int K, int N, int n0, int wave, int lane,
                                            uint32_t (&voff)[C::PER]) {
@@ -154,7 +133,7 @@ __device__ __forceinline__ void gemm_voffs(const int32_t (&arow)[C::PER], int K,
     if (p < C::AU) {
       const int r = p / C::UA, up = p % C::UA;
       const int u = up ^ C::swa(r);
-      voff[i] = arow[i] >= 0 ? static_cast<uint32_t>((static_cast<int64_t>(arow[i]) * K + 8 * u) * 2) : kGemmFarOff;
+      voff[i] = arow[i] >= 0 ? static_cast<uint32_t>((static_cast<int64_t>(arow[i]) * K + 8 * u) * 2) : kBufFarOff;
     } else {
       const int q = p - C::AU;
       const int kr = q / C::UB, up = q % C::UB;
@@ -171,8 +150,8 @@ __device__ __forceinline__ void gemm_issue_buf(const uint16_t *__restrict__ x, i
                                                char *stage) {
   const int64_t k0 = static_cast<int64_t>(st) * C::BK;
   const bool live = st < nst;
-  const u32x4 xr = gemm_rsrc(x + k0, live ? (Mx * K - k0) * 2 : 0);
-  const u32x4 wr = gemm_rsrc(W + k0 * N, live ? (K - k0) * static_cast<int64_t>(N) * 2 : 0);
+  const u32x4 xr = buf_rsrc(x + k0, live ? (Mx * K - k0) * 2 : 0);
+  const u32x4 wr = buf_rsrc(W + k0 * N, live ? (K - k0) * static_cast<int64_t>(N) * 2 : 0);
 #pragma unroll
   for (int i = 0; i < C::PER; ++i) {
     const uint32_t lds = __builtin_amdgcn_readfirstlane(
@@ -390,7 +369,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
 // Buffer descriptors address 32-bit byte ranges: operands under 4 GiB take
 // them, larger ones the 64-bit addresses.
 static bool gemm_buf_ok(int64_t rows, int64_t K, int64_t N) {
-  return rows * K * 2 < kGemmFarOff && K * N * 2 < kGemmFarOff;
+  return rows * K * 2 < kBufFarOff && K * N * 2 < kBufFarOff;
 }
 
 template <class C, class OutT = float>
