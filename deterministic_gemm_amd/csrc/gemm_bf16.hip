@@ -411,8 +411,9 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
   // 128 tiles (eight 32 x 64 wavefront tiles) by ~12% (configurations with
   // more stages in flight need more than the 256 registers a wavefront has
   // here).  Below that the weights dominate and 128 x 128 tiles stream them
-  // faster: 24 vs 48 us at 8 rows, 171 vs 194 us at 512 rows (864 MiB of
-  // weights), 223 vs 250 us at 16384 rows; even at 32768.
+  // faster: 22 vs 36 us at 8 rows, 169 vs 200 us at 512 rows (864 MiB of
+  // weights, 5.3 TB/s), 220 vs 236 us at 16384 rows; at 32768 the large tile
+  // wins (271 vs 289 us).
   if (N % 256 == 0 && P >= 128 * E)
     return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
   return launch_grouped_c<GemmCfg<128, 128, 4, 2, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
