@@ -111,3 +111,33 @@ def test_gate_dot_f32_and_ragged_k():
         note(f"gate dot bf16 x, f32 w K={K}")
         d, g = dr.gate_dot(dev_bf16_bits(xb), dev(wf))
         assert f32_equal_bits(d.cpu().numpy(), rd) and f32_equal_bits(g.cpu().numpy(), rg)
+
+
+def test_gemm_operands_of_4gib_and_more_take_the_64bit_path():
+    """x of 2^20 rows x 2048 (4 GiB, past a buffer descriptor's 32-bit range)
+    runs the transfers with 64-bit addresses; sampled rows, and the grouped
+    product reading rows of that x, must equal the same rows computed from a
+    small x (the buffer-descriptor path) bit for bit."""
+    dr = require_gpu()
+    M, K, N = 1 << 20, 2048, 128
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    note("gemm 4 GiB x: allocate")
+    x = torch.randn((M, K), device="cuda", generator=g).to(torch.bfloat16)
+    W = (torch.randn((K, N), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    note("gemm 4 GiB x: 64-bit path")
+    out = dr.gemm_bf16(x, W)
+    rows = torch.tensor([0, 1, 12345, M // 2, M - 2, M - 1], device="cuda")
+    note("gemm 4 GiB x: buffer path on the same rows")
+    small = dr.gemm_bf16(x[rows].contiguous(), W)
+    assert torch.equal(out[rows].view(torch.int32), small.view(torch.int32))
+    del out
+    E = 4
+    Wg = (torch.randn((E, K, N), device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    grows = torch.tensor([M - 1, 7, M // 3, 0, 999999, M - 5, 3, 12], dtype=torch.int32, device="cuda")
+    off = torch.tensor([0, 2, 5, 5, 8], dtype=torch.int32, device="cuda")
+    note("grouped gemm with 4 GiB x")
+    big = dr.grouped_gemm_bf16(x, Wg, off, grows)
+    note("grouped gemm with the gathered rows")
+    ref = dr.grouped_gemm_bf16(x[grows.long()].contiguous(), Wg, off)
+    assert torch.equal(big.view(torch.int32), ref.view(torch.int32))
