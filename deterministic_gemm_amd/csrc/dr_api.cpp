@@ -83,8 +83,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
                 "narrow variant needs fp32 x, K %% 4 == 0, E <= 512 and the logits output");
   if (variant == DR_VARIANT_TINY && !drk::tiny_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED, "tiny variant needs fp32 x, K %% 4 == 0, K <= 4096 and the logits output");
-  if (variant == DR_VARIANT_TINY && M > 4 * 65535)
-    return fail(DR_ERR_UNSUPPORTED, "tiny variant takes at most %d tokens", 4 * 65535);
+  if (variant == DR_VARIANT_TINY && M > drk::kTinyMaxRows)
+    return fail(DR_ERR_UNSUPPORTED, "tiny variant takes at most %lld tokens", (long long)drk::kTinyMaxRows);
   if (M == 0) return DR_OK;
 
   drk::RouteLaunch L;

@@ -49,6 +49,8 @@ bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
 hipError_t launch_route_tiny(const RouteLaunch &L);
 hipError_t launch_route_tiny_logits(const RouteLaunch &L);
 bool tiny_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
+// the most rows the vector-ALU family's grid takes (four tokens per row of workgroups)
+constexpr int64_t kTinyMaxRows = 4 * 65535;
 int64_t tiny_max_m(int64_t E, int64_t K);
 hipError_t launch_route_narrow(const RouteLaunch &L);
 hipError_t launch_route_narrow_logits(const RouteLaunch &L);

@@ -12,9 +12,10 @@
 // Disaggregated Inference", section "The anatomy of the missing numeric
 // contract").  The selection kernel then runs on the stored logits.
 //
-// One wavefront per workgroup: P = the next power of two >= nb block slots,
-// 64 / P experts, T tokens.  The workgroup's whole W slice (K rows of 64/P
-// experts, 64 KiB at most) and its tokens' x rows go to LDS in one burst of
+// A workgroup holds NW wavefronts, one token each, that share one W slice:
+// P = the next power of two >= nb block slots, 64 / P experts.  The slice (K
+// rows of 64/P experts, 64 KiB at most), its transfers dealt out to the NW
+// wavefronts, and each wavefront's x row go to LDS in one burst of
 // global_load_lds_dwordx4 transfers; each block's rows are followed by one
 // row of padding, so the P blocks read at one k land on distinct LDS banks.
 #include "route_common.h"
@@ -23,45 +24,45 @@
 
 namespace drk {
 
-// Batches this family takes: up to 48 tokens when a workgroup's W slice
-// leaves room for six tokens' x (K <= 2048) and E <= 512, else 32.  Measured at K=2048,
-// E=256, logits kernel alone: 10.1 us at M=32 (four tokens per workgroup),
-// 12.2 us at M=40..48 with six (four: 19.0; the narrow family: 14.7), 14.9 us
-// at M=64 with eight (narrow: 14.8).
-constexpr int64_t kTinyMaxM = 32, kTinyMaxM6 = 48;
-
-template <int P, int T>
+template <int P, int NW>
 struct TinyCfg {
   static_assert(P >= 1 && P <= 16 && (P & (P - 1)) == 0, "block slots");
+  static_assert(NW >= 1 && NW <= 8, "wavefronts");
   static constexpr int EPW = 64 / P;                 // experts per workgroup
   static constexpr int ROWB = EPW * 4;               // bytes of one W row slice
   static constexpr int WBLK = 256 * ROWB + ROWB;     // one block of rows plus a padding row
   static constexpr int XBLK = 1024 + 16;             // 256 values of one token's block plus padding
   static constexpr int WBYTES = P * WBLK;
-  static constexpr int XBYTES = T * P * XBLK;
+  static constexpr int XBYTES = NW * P * XBLK;       // one token per wavefront
   static constexpr int RPI = 1024 / ROWB;            // W rows per transfer instruction
   static_assert(WBYTES + XBYTES <= 160 * 1024, "LDS");
 };
 
-template <int P, int T>
-__global__ __launch_bounds__(64) void route_tiny_logits_kernel(const float *__restrict__ x,
-                                                               const float *__restrict__ W, int64_t M, int K,
-                                                               int E, int logit_bf16, void *__restrict__ logits) {
-  using C = TinyCfg<P, T>;
+// the most wavefronts a workgroup's LDS leaves room for
+template <int P>
+constexpr int kTinyMaxNW = P <= 8 ? 8 : 4;
+
+template <int P, int NW>
+__global__ __launch_bounds__(64 * NW) void route_tiny_logits_kernel(const float *__restrict__ x,
+                                                                    const float *__restrict__ W, int64_t M, int K,
+                                                                    int E, int logit_bf16, void *__restrict__ logits) {
+  using C = TinyCfg<P, NW>;
   __shared__ __attribute__((aligned(16))) char smem[C::WBYTES + C::XBYTES];
-  char *wl = smem, *xl = smem + C::WBYTES;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  char *wl = smem, *xl = smem + C::WBYTES + wave * (P * C::XBLK);
   const int ng = gridDim.x;
   const int g = (ng % 8 == 0) ? (blockIdx.x % 8) * (ng / 8) + blockIdx.x / 8 : blockIdx.x;  // XCD-contiguous groups
   const int e0 = g * C::EPW;
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * T;
+  const int64_t m = static_cast<int64_t>(blockIdx.y) * NW + wave;  // this wavefront's token
   const int nb = (K + 255) / 256;
 
-  // W slice: block b's rows k = 256 b .. 256 b + 255, ROWB bytes each.  At
-  // most 32 transfers stay outstanding (the wait counter holds 63).
+  // W slice: block b's rows k = 256 b .. 256 b + 255, ROWB bytes each, its
+  // transfer instructions dealt out to the NW wavefronts in turn.  At most
+  // 32 transfers stay outstanding (the wait counter holds 63).
   int issued = 0;
   for (int b = 0; b < nb; ++b)
     for (int i = 0; i < 256 / C::RPI; ++i) {
+      if ((b * (256 / C::RPI) + i) % NW != wave) continue;
       if (++issued > 32) wait_vmcnt<31>();
       const int r = i * C::RPI + lane / (C::ROWB / 16);  // row within the block
       const int u = lane % (C::ROWB / 16);               // 16-byte unit within the row
@@ -70,78 +71,64 @@ __global__ __launch_bounds__(64) void route_tiny_logits_kernel(const float *__re
       if (kk < K) src = W + static_cast<int64_t>(kk) * E + e0 + 4 * u;
       dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const float *>(wl + b * C::WBLK + i * 1024))));
     }
-  // x rows: token t, block b: 256 values in one instruction
-  for (int t = 0; t < T; ++t)
-    for (int b = 0; b < nb; ++b) {
-      if (++issued > 32) wait_vmcnt<31>();
-      const int kk = 256 * b + 4 * lane;
-      const void *src = &g_pad_pos;
-      if (m0 + t < M && kk < K) src = x + (m0 + t) * K + kk;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const float *>(xl + (t * P + b) * C::XBLK))));
-    }
+  // the token's x row: block b's 256 values in one instruction
+  for (int b = 0; b < nb; ++b) {
+    if (++issued > 32) wait_vmcnt<31>();
+    const int kk = 256 * b + 4 * lane;
+    const void *src = &g_pad_pos;
+    if (m < M && kk < K) src = x + m * K + kk;
+    dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const float *>(xl + b * C::XBLK))));
+  }
   compiler_fence();
   wait_vmcnt<0>();
-  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_s_barrier();  // the W slice came from every wavefront
   compiler_fence();
 
   const int b = lane / C::EPW, e = lane % C::EPW;
   const int klen = (b < nb) ? min(256, K - 256 * b) : 0;  // a multiple of 4
-  float acc[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) acc[t] = (b < nb) ? 0.0f : -0.0f;
+  float acc = (b < nb) ? 0.0f : -0.0f;
   const float *wrow = reinterpret_cast<const float *>(wl + b * C::WBLK) + e;
   const float *xrow = reinterpret_cast<const float *>(xl + b * C::XBLK);
   // unrolled so that later steps' LDS reads are in flight while a step's
   // fmafs wait on their operands
 #pragma unroll 8
   for (int k = 0; k < klen; k += 4) {
-    const float w0 = wrow[(k + 0) * C::EPW], w1 = wrow[(k + 1) * C::EPW];
-    const float w2 = wrow[(k + 2) * C::EPW], w3 = wrow[(k + 3) * C::EPW];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const float4 xv = *reinterpret_cast<const float4 *>(xrow + t * (P * C::XBLK / 4) + k);
-      acc[t] = __builtin_fmaf(xv.x, w0, acc[t]);
-      acc[t] = __builtin_fmaf(xv.y, w1, acc[t]);
-      acc[t] = __builtin_fmaf(xv.z, w2, acc[t]);
-      acc[t] = __builtin_fmaf(xv.w, w3, acc[t]);
-    }
+    const float4 xv = *reinterpret_cast<const float4 *>(xrow + k);
+    acc = __builtin_fmaf(xv.x, wrow[(k + 0) * C::EPW], acc);
+    acc = __builtin_fmaf(xv.y, wrow[(k + 1) * C::EPW], acc);
+    acc = __builtin_fmaf(xv.z, wrow[(k + 2) * C::EPW], acc);
+    acc = __builtin_fmaf(xv.w, wrow[(k + 3) * C::EPW], acc);
   }
   // the tree over the P block slots: level d adds lanes whose block index
   // differs in bit d, adjacent blocks first
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    float v = acc[t];
-#pragma unroll
-    for (int d = C::EPW; d < 64; d <<= 1) v = v + __shfl_xor(v, d, 64);
-    acc[t] = v;
-  }
-  if (b == 0) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-      const int64_t m = m0 + t;
-      if (m >= M) break;
-      if (logit_bf16) static_cast<uint16_t *>(logits)[m * E + e0 + e] = f32_to_bf16(acc[t]);
-      else static_cast<float *>(logits)[m * E + e0 + e] = acc[t];
-    }
+  for (int d = C::EPW; d < 64; d <<= 1) acc = acc + __shfl_xor(acc, d, 64);
+  if (b == 0 && m < M) {
+    if (logit_bf16) static_cast<uint16_t *>(logits)[m * E + e0 + e] = f32_to_bf16(acc);
+    else static_cast<float *>(logits)[m * E + e0 + e] = acc;
   }
 }
 
-template <int P, int T>
-static hipError_t launch_tiny_pt(const RouteLaunch &L) {
-  const dim3 grid(static_cast<uint32_t>(L.E / TinyCfg<P, T>::EPW), static_cast<uint32_t>((L.M + T - 1) / T));
-  hipLaunchKernelGGL((route_tiny_logits_kernel<P, T>), grid, dim3(64), 0, L.stream, L.xf, L.W, L.M,
+template <int P, int NW>
+static hipError_t launch_tiny_pw(const RouteLaunch &L) {
+  const dim3 grid(static_cast<uint32_t>(L.E / TinyCfg<P, NW>::EPW), static_cast<uint32_t>((L.M + NW - 1) / NW));
+  hipLaunchKernelGGL((route_tiny_logits_kernel<P, NW>), grid, dim3(64 * NW), 0, L.stream, L.xf, L.W, L.M,
                      static_cast<int>(L.K), static_cast<int>(L.E), L.logit_bf16, L.logits);
   return hipGetLastError();
 }
 
+// The LDS of one workgroup admits one per CU.  Four wavefronts while the
+// workgroups fit the CUs at once, else as many as LDS allows.  Measured at
+// K=2048, E=256, logits kernel alone: 6.0-6.4 us for M=1..32 with four
+// wavefronts (one wavefront per workgroup with four tokens each: 7.2-11.4),
+// 7.2-7.9 us for M=33..64 with eight; at K=4096: 6.4-8.3 us for M=1..16.
 template <int P>
 static hipError_t launch_tiny_p(const RouteLaunch &L) {
-  if (L.M <= 1) return launch_tiny_pt<P, 1>(L);
-  if (L.M <= 2) return launch_tiny_pt<P, 2>(L);
-  if constexpr (P <= 8) {
-    if (L.M > kTinyMaxM) return launch_tiny_pt<P, 6>(L);
+  const int64_t groups = L.E / TinyCfg<P, 4>::EPW;
+  if constexpr (kTinyMaxNW<P> > 4) {
+    if (groups * ((L.M + 3) / 4) > device_cus()) return launch_tiny_pw<P, kTinyMaxNW<P>>(L);
   }
-  return launch_tiny_pt<P, 4>(L);
+  return launch_tiny_pw<P, 4>(L);
 }
 
 bool tiny_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
@@ -163,6 +150,19 @@ hipError_t launch_route_tiny(const RouteLaunch &L) {
   return launch_route_select(L);
 }
 
-int64_t tiny_max_m(int64_t E, int64_t K) { return ((K + 255) / 256 <= 8 && E <= 512) ? kTinyMaxM6 : kTinyMaxM; }
+// Batches this family takes: while its workgroups, with as many wavefronts as
+// LDS allows, fit the CUs at once; past that a second round of workgroups
+// costs as much as the first, and the narrow family is faster.  Where the
+// narrow family does not take E, up to 4096 tokens: measured at E = 1024
+// against the row-wise family, the one left, 128 against 1917 us at M = 256
+// and 3167 against 5879 at M = 8192 (K = 2048); at K = 4096 6.7 against
+// 7.8 ms at M = 4096, but 13.4 against 11.7 at M = 8192.
+int64_t tiny_max_m(int64_t E, int64_t K) {
+  if (!narrow_supports(E, K, true, true)) return 4096;
+  int p = 1;
+  while (p < (K + 255) / 256) p <<= 1;
+  const int64_t nw = p <= 8 ? 8 : 4, groups = E * p / 64;
+  return groups > 0 ? nw * (device_cus() / groups) : 0;
+}
 
 }  // namespace drk

@@ -195,14 +195,18 @@ def test_auto_variant_is_a_function_of_shape(L):
     # exactly one switch, inside the m-scan range
     switches = sum(1 for a, b in zip(picks, picks[1:]) if a != b)
     assert switches == 1
-    assert dr.auto_variant(8192, 2048, 1024) == "rowwise"
-    # small batches that ask for the logits: the vector-ALU family up to 48
-    # tokens at K <= 2048 and E <= 512 (else 32), then narrow tiles (the
-    # switch lies inside the m-scan range)
-    assert [dr.auto_variant(M, 2048, 256) for M in (1, 19, 32, 33, 48, 49, 80)] == ["tiny"] * 5 + ["narrow"] * 2
-    assert [dr.auto_variant(M, 4096, 256) for M in (32, 33)] == ["tiny", "narrow"]
+    assert dr.auto_variant(8192, 2048, 1024, logits=False) == "rowwise"
+    # small batches that ask for the logits: the vector-ALU family while its
+    # workgroups fit the CUs at once (256 here: 64 tokens at K = 2048, E = 256;
+    # 16 at K = 4096; 128 at K = 1024), then narrow tiles (the switch lies
+    # inside the m-scan range); up to 4096 tokens where the narrow family does
+    # not take E
+    assert [dr.auto_variant(M, 2048, 256) for M in (1, 19, 32, 33, 64, 65, 80)] == ["tiny"] * 5 + ["narrow"] * 2
+    assert [dr.auto_variant(M, 4096, 256) for M in (16, 17)] == ["tiny", "narrow"]
+    assert [dr.auto_variant(M, 2048, 512) for M in (32, 33)] == ["tiny", "narrow"]
+    assert [dr.auto_variant(M, 1024, 256) for M in (128, 129)] == ["tiny", "narrow"]
     assert dr.auto_variant(19, 2048, 1024) == "tiny"
-    assert dr.auto_variant(40, 2048, 1024) == "rowwise"
+    assert [dr.auto_variant(M, 2048, 1024) for M in (4096, 4097)] == ["tiny", "rowwise"]
     assert dr.auto_variant(19, 8192, 256) == "narrow"   # K above the vector family's 4096
     # large batches that ask for the logits take the two-kernel family: at
     # 1024 < K <= 4096 above 2048 tokens for E = 256 and 1024 for E = 512
