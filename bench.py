@@ -147,6 +147,19 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
                       "frac_fp32_peak": round(2.0 * m * K * E / (ms * 1e-3) / 1e12 / PEAK_FP32_MATRIX_TFLOPS, 4)})
     suite["m_sweep_K2048_E256_k8"] = sweep
     log("m sweep done")
+    # bf16 activations (the sweep rows are bf16 values, so the cast is exact):
+    # the binding widens them to fp32 (dr_widen_bf16) and routes through the
+    # fp32 families; the register-staged bf16 family beside it
+    xbf = xd.to(torch.bfloat16)
+    bx = []
+    for m in (64, 8192):
+        xm = xbf[:m].contiguous()
+        ms, ms_e = timed(lambda: dr.route(xm, Wd, TOPK))
+        ms_t, _ = timed(lambda: dr.route(xm, Wd, TOPK, variant="tiled"))
+        bx.append({"M": m, "us": round(ms * 1e3, 2), "us_host_bound": round(ms_e * 1e3, 2),
+                   "tokens_per_s": round(m / (ms * 1e-3), 1), "us_bf16_tiled_family": round(ms_t * 1e3, 2)})
+    suite["bf16_x_widened_K2048_E256_k8"] = bx
+    log("bf16 activations done")
 
     calib = json.load(open(os.path.join(ROOT, "tests", "golden", "tie_calibration.json")))
     Wt = torch.from_numpy(wl.tie_weights(calib["pairs"])).to(dev)

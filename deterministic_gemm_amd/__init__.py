@@ -38,7 +38,7 @@ MARGIN_DTYPE = np.dtype(
 
 EXPORTED = (
     "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
-    "dr_route_bf16_gemm", "dr_gate_dot", "dr_gemm_bf16", "dr_grouped_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_contract",
+    "dr_route_bf16_gemm", "dr_gate_dot", "dr_gemm_bf16", "dr_grouped_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_widen_bf16", "dr_contract",
     "dr_status_string", "dr_last_error",
 )
 
@@ -89,6 +89,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     L.dr_moe_permute.restype = ctypes.c_int
     L.dr_moe_gather.argtypes = [P, ctypes.c_int, i64, i64, P, i64, P, P]
     L.dr_moe_gather.restype = ctypes.c_int
+    L.dr_widen_bf16.argtypes = [P, i64, P, P]
+    L.dr_widen_bf16.restype = ctypes.c_int
     L.dr_moe_combine.argtypes = [P, ctypes.c_int, i64, P, P, P, P, ctypes.c_int, P, i64, i32, i64, P, P]
     L.dr_moe_combine.restype = ctypes.c_int
     L.dr_contract.argtypes = [ctypes.POINTER(_Contract)]
@@ -145,6 +147,14 @@ def scratch_logits_used(M: int, K: int, E: int, x_dtype: str = "f32") -> bool:
     return auto_variant(M, K, E, x_dtype, logits=True) in ("tiny", "narrow", "split")
 
 
+def widen_bf16_used(M: int, K: int, E: int) -> bool:
+    """Whether route(...) with bf16 x and variant "auto" widens x to fp32
+    first (dr_widen_bf16): when the fp32 dispatch with a logits buffer picks
+    an LDS-staged family (tiny, narrow or split), which the bf16 families do
+    not match for speed.  The results are the same bits either way."""
+    return auto_variant(M, K, E, "f32", logits=True) in ("tiny", "narrow", "split")
+
+
 def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, logits: bool = True,
           weights: bool = True, margins: bool = True, variant: str = "auto", out=None,
           scratch_logits: bool = True):
@@ -171,9 +181,11 @@ def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, 
         lg_t = (torch.empty((M, E), dtype=torch.float32 if ldt == DR_F32 else torch.bfloat16, device=dev)
                 if logits else None)
         mg_t = torch.empty((M, 4), dtype=torch.int32, device=dev) if margins else None
+    v = VARIANTS[variant]
+    if x.dtype == torch.bfloat16 and v == 0 and widen_bf16_used(M, K, E):
+        x = widen_bf16(x)
     xd = DR_F32 if x.dtype == torch.float32 else DR_BF16
     flags = DR_ROUTE_RENORMALIZE if renormalize else 0
-    v = VARIANTS[variant]
     lg_pass = lg_t
     if (lg_t is None and v == 0 and scratch_logits
             and scratch_logits_used(M, K, E, "f32" if xd == DR_F32 else "bf16")):
@@ -267,6 +279,19 @@ def moe_permute(ids, E: int, out=None):
     st = L.dr_moe_permute(_ptr(ids), M, k, E, _ptr(offsets), _ptr(rows), _ptr(pos), _stream(dev))
     _check(st, "dr_moe_permute")
     return offsets, rows, pos
+
+
+def widen_bf16(x, out=None):
+    """dr_widen_bf16: a bfloat16 tensor widened exactly to float32 (same shape)."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.bfloat16,))
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
+    _dev_tensor(out, "out", (torch.float32,))
+    if out.shape != x.shape:
+        raise ValueError("out must have x's shape")
+    _check(L.dr_widen_bf16(_ptr(x), x.numel(), _ptr(out), _stream(x.device)), "dr_widen_bf16")
+    return out
 
 
 def moe_gather(x, rows, out=None):
@@ -381,3 +406,4 @@ dr_route_select = route_select
 dr_gate_dot = gate_dot
 dr_gemm_bf16 = gemm_bf16
 dr_contract = contract
+dr_widen_bf16 = widen_bf16

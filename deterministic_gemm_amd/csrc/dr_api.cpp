@@ -353,6 +353,15 @@ dr_status dr_moe_combine(const void *y, dr_dtype y_dtype, int64_t P, const float
                        "moe_combine launch");
 }
 
+dr_status dr_widen_bf16(const uint16_t *x, int64_t n, float *out, void *stream) {
+  g_last_error[0] = '\0';
+  if (n < 0) return fail(DR_ERR_INVALID, "n=%lld must be >= 0", (long long)n);
+  if (n > 0 && (!x || !out)) return fail(DR_ERR_INVALID, "x and out are required");
+  if (!aligned16(x) || !aligned16(out)) return fail(DR_ERR_INVALID, "pointers must be 16-byte aligned");
+  if (n == 0) return DR_OK;
+  return device_status(drk::launch_widen_bf16(x, n, out, static_cast<hipStream_t>(stream)), "widen launch");
+}
+
 void dr_contract(dr_contract_info *out) {
   if (!out) return;
   out->version = 1;

@@ -49,6 +49,7 @@ bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
 hipError_t launch_route_tiny(const RouteLaunch &L);
 hipError_t launch_route_tiny_logits(const RouteLaunch &L);
 bool tiny_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
+hipError_t launch_widen_bf16(const uint16_t *x, int64_t n, float *out, hipStream_t stream);
 // the most rows the vector-ALU family's grid takes (four tokens per row of workgroups)
 constexpr int64_t kTinyMaxRows = 4 * 65535;
 int64_t tiny_max_m(int64_t E, int64_t K);

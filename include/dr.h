@@ -133,6 +133,12 @@ typedef struct dr_contract_info {
  *            families passes a buffer anyway (the Python binding does).
  *   margins  [M] or NULL.
  *
+ * bf16 x runs the register-staged families only (tiled, row-wise: ~120 us
+ * at K = 2048, E = 256 for any M up to 8192 on MI355X).  Widening it first
+ * with dr_widen_bf16 and passing DR_F32 gives the same bits through the
+ * LDS-staged families: 16 us at M = 64 and 103 us at M = 8192, the widening
+ * included.  The Python binding does this by itself.
+ *
  * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32;
  * 0 <= M <= 2^22 tokens per call (larger M is DR_ERR_INVALID).
  * Other shapes return DR_ERR_UNSUPPORTED (no silent change of numeric path).
@@ -260,6 +266,18 @@ dr_status dr_route_bf16_gemm(const uint16_t *x, const uint16_t *W, int64_t M, in
  */
 dr_status dr_moe_permute(const int32_t *ids, int64_t M, int32_t k, int32_t E, int32_t *offsets,
                          int32_t *rows, int32_t *pos, void *stream);
+
+/*
+ * dr_widen_bf16 -- out[i] = x[i] widened exactly to fp32 for i in [0,n): the
+ * bf16 bits become the upper half of the fp32 pattern, the lower half zero
+ * (NaN payloads and signed zeros kept).  How bf16 activations reach the
+ * LDS-staged router families with unchanged results (dr_route, "x").
+ *   x [n] bf16 bits and out [n] fp32, device memory, 16-byte aligned, not
+ *   overlapping; both owned by the caller.  n == 0 is a no-op.
+ *   DR_ERR_INVALID for n < 0, missing or misaligned pointers.  One launch on
+ *   stream; errors of the launch itself are DR_ERR_DEVICE.
+ */
+dr_status dr_widen_bf16(const uint16_t *x, int64_t n, float *out, void *stream);
 
 /*
  * dr_moe_gather -- xp[p,:] = x[rows[p],:] for p in [0,P): activations in the

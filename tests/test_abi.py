@@ -232,3 +232,14 @@ def test_contract(L):
 def test_status_strings(L):
     for s in (0, 1, 2, 3):
         assert L.dr_status_string(s)
+
+
+def test_widen_bf16_validation(L):
+    assert L.dr_widen_bf16(None, -1, None, None) == INVALID
+    assert L.dr_widen_bf16(None, 8, A, None) == INVALID
+    assert L.dr_widen_bf16(A, 8, None, None) == INVALID
+    assert L.dr_widen_bf16(A + 2, 8, A, None) == INVALID  # misaligned x
+    assert L.dr_widen_bf16(A, 8, A + 4, None) == INVALID  # misaligned out
+    assert L.dr_widen_bf16(None, 0, None, None) == OK      # empty: nothing launched
+    assert not dr.widen_bf16_used(8192, 8192 * 4, 256)     # K above the fp32 families' limits
+    assert dr.widen_bf16_used(1, 2048, 256) and dr.widen_bf16_used(8192, 2048, 256)

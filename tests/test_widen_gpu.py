@@ -1,0 +1,73 @@
+"""bf16 activations: the exact widening to fp32 (dr_widen_bf16) and the
+binding's route through it, which must give the bits of the bf16 families and
+of the oracle ("Batch changed the model's mind", section "The fix: m-invariant
+twins": a row's result fixed by its own values; a bf16 value widened to fp32
+is the same number)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import assert_route_equal, dev, gpu_route_np, note, oracle_route, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+K, E, TOPK = 2048, 256, 8
+
+
+def _bits16(n, seed):
+    """Every class of bf16 pattern: normals of both signs, +-0, subnormals,
+    +-inf and NaNs with payloads."""
+    rng = np.random.default_rng(seed)
+    b = rng.integers(0, 1 << 16, size=n, dtype=np.uint32).astype(np.uint16)
+    special = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x7F81, 0x3F80], dtype=np.uint16)
+    b[: min(n, len(special))] = special[:n]
+    return b
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 4096 * 8 + 5, 3_000_001])
+def test_widen_is_exact(n):
+    dr = require_gpu()
+    b = _bits16(n, n)
+    note(f"widen n={n}")
+    xb = torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+    got = dr.widen_bf16(xb).cpu().numpy().view(np.uint32)
+    want = b.astype(np.uint32) << 16
+    assert np.array_equal(got, want)
+
+
+def test_widen_leaves_out_past_n_alone():
+    dr = require_gpu()
+    b = _bits16(13, 5)
+    xb = torch.from_numpy(b.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.full((16,), 7.0, device="cuda")
+    st = dr.load_library().dr_widen_bf16(xb.data_ptr(), 13, out.data_ptr(), None)
+    assert st == dr.DR_OK
+    o = out.cpu().numpy()
+    assert np.array_equal(o[:13].view(np.uint32), b.astype(np.uint32) << 16)
+    assert np.all(o[13:] == 7.0)
+
+
+@pytest.fixture(scope="module")
+def data():
+    W = wl.router_weights(K, E)
+    xf = wl.sweep_x(8192, K)  # bf16-valued fp32 rows
+    return W, xf
+
+
+@pytest.mark.parametrize("M", [1, 19, 64, 65, 1024, 8192])
+def test_bf16_route_equals_fp32_route_and_bf16_families(data, M):
+    dr = require_gpu()
+    W, xf = data
+    Wd = dev(W)
+    xb = dev(xf[:M]).to(torch.bfloat16)
+    assert np.array_equal(xb.float().cpu().numpy(), xf[:M])  # the rows are bf16 values
+    note(f"bf16 x M={M}: auto widens={dr.widen_bf16_used(M, K, E)}")
+    got = gpu_route_np(dr, xb, Wd, TOPK)
+    want = gpu_route_np(dr, dev(xf[:M]), Wd, TOPK)
+    assert_route_equal(got, want, what=f"bf16 vs fp32 x, M={M}")
+    if M <= 1024:
+        note(f"bf16 x M={M}: against the register-staged family")
+        assert_route_equal(got, gpu_route_np(dr, xb, Wd, TOPK, variant="tiled"), what=f"tiled, M={M}")
+    if M <= 65:
+        assert_route_equal(got, oracle_route(xf[:M], W, TOPK), what=f"oracle, M={M}")
