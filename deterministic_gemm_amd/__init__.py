@@ -150,9 +150,11 @@ def scratch_logits_used(M: int, K: int, E: int, x_dtype: str = "f32") -> bool:
 def widen_bf16_used(M: int, K: int, E: int) -> bool:
     """Whether route(...) with bf16 x and variant "auto" widens x to fp32
     first (dr_widen_bf16): when the fp32 dispatch with a logits buffer picks
-    an LDS-staged family (tiny, narrow or split), which the bf16 families do
-    not match for speed.  The results are the same bits either way."""
-    return auto_variant(M, K, E, "f32", logits=True) in ("tiny", "narrow", "split")
+    an LDS-staged family (tiny, narrow or split) and the bf16 dispatch does
+    not (the vector-ALU family reads bf16 itself).  The results are the same
+    bits either way."""
+    fast = ("tiny", "narrow", "split")
+    return auto_variant(M, K, E, "f32", logits=True) in fast and auto_variant(M, K, E, "bf16", logits=True) not in fast
 
 
 def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, logits: bool = True,

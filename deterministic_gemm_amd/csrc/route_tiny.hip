@@ -42,8 +42,10 @@ struct TinyCfg {
 template <int P>
 constexpr int kTinyMaxNW = P <= 8 ? 8 : 4;
 
-template <int P, int NW>
-__global__ __launch_bounds__(64 * NW) void route_tiny_logits_kernel(const float *__restrict__ x,
+// XB: x holds bf16 bits (K % 8 == 0), staged as they are and widened
+// exactly when read; else fp32 (K % 4 == 0).
+template <int P, int NW, bool XB>
+__global__ __launch_bounds__(64 * NW) void route_tiny_logits_kernel(const void *__restrict__ xv,
                                                                     const float *__restrict__ W, int64_t M, int K,
                                                                     int E, int logit_bf16, void *__restrict__ logits) {
   using C = TinyCfg<P, NW>;
@@ -71,12 +73,16 @@ __global__ __launch_bounds__(64 * NW) void route_tiny_logits_kernel(const float 
       if (kk < K) src = W + static_cast<int64_t>(kk) * E + e0 + 4 * u;
       dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const float *>(wl + b * C::WBLK + i * 1024))));
     }
-  // the token's x row: block b's 256 values in one instruction
+  // the token's x row: block b's 256 values in one instruction (bf16: the
+  // first 32 lanes; the others fill the block's unused upper half)
   for (int b = 0; b < nb; ++b) {
     if (++issued > 32) wait_vmcnt<31>();
-    const int kk = 256 * b + 4 * lane;
+    const int kk = 256 * b + (XB ? 8 : 4) * lane;
     const void *src = &g_pad_pos;
-    if (m < M && kk < K) src = x + m * K + kk;
+    if (m < M && kk < K && (!XB || lane < 32)) {
+      if constexpr (XB) src = static_cast<const uint16_t *>(xv) + m * K + kk;
+      else src = static_cast<const float *>(xv) + m * K + kk;
+    }
     dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(reinterpret_cast<const float *>(xl + b * C::XBLK))));
   }
   compiler_fence();
@@ -88,16 +94,22 @@ __global__ __launch_bounds__(64 * NW) void route_tiny_logits_kernel(const float 
   const int klen = (b < nb) ? min(256, K - 256 * b) : 0;  // a multiple of 4
   float acc = (b < nb) ? 0.0f : -0.0f;
   const float *wrow = reinterpret_cast<const float *>(wl + b * C::WBLK) + e;
-  const float *xrow = reinterpret_cast<const float *>(xl + b * C::XBLK);
+  const char *xrow = xl + b * C::XBLK;
   // unrolled so that later steps' LDS reads are in flight while a step's
   // fmafs wait on their operands
 #pragma unroll 8
   for (int k = 0; k < klen; k += 4) {
-    const float4 xv = *reinterpret_cast<const float4 *>(xrow + k);
-    acc = __builtin_fmaf(xv.x, wrow[(k + 0) * C::EPW], acc);
-    acc = __builtin_fmaf(xv.y, wrow[(k + 1) * C::EPW], acc);
-    acc = __builtin_fmaf(xv.z, wrow[(k + 2) * C::EPW], acc);
-    acc = __builtin_fmaf(xv.w, wrow[(k + 3) * C::EPW], acc);
+    float4 xk;
+    if constexpr (XB) {
+      const uint2 u = *reinterpret_cast<const uint2 *>(xrow + 2 * k);  // four bf16, little-endian pairs
+      xk = make_float4(u2f(u.x << 16), u2f(u.x & 0xFFFF0000u), u2f(u.y << 16), u2f(u.y & 0xFFFF0000u));
+    } else {
+      xk = *reinterpret_cast<const float4 *>(xrow + 4 * k);
+    }
+    acc = __builtin_fmaf(xk.x, wrow[(k + 0) * C::EPW], acc);
+    acc = __builtin_fmaf(xk.y, wrow[(k + 1) * C::EPW], acc);
+    acc = __builtin_fmaf(xk.z, wrow[(k + 2) * C::EPW], acc);
+    acc = __builtin_fmaf(xk.w, wrow[(k + 3) * C::EPW], acc);
   }
   // the tree over the P block slots: level d adds lanes whose block index
   // differs in bit d, adjacent blocks first
@@ -112,8 +124,14 @@ __global__ __launch_bounds__(64 * NW) void route_tiny_logits_kernel(const float 
 template <int P, int NW>
 static hipError_t launch_tiny_pw(const RouteLaunch &L) {
   const dim3 grid(static_cast<uint32_t>(L.E / TinyCfg<P, NW>::EPW), static_cast<uint32_t>((L.M + NW - 1) / NW));
-  hipLaunchKernelGGL((route_tiny_logits_kernel<P, NW>), grid, dim3(64 * NW), 0, L.stream, L.xf, L.W, L.M,
-                     static_cast<int>(L.K), static_cast<int>(L.E), L.logit_bf16, L.logits);
+  if (L.xf)
+    hipLaunchKernelGGL((route_tiny_logits_kernel<P, NW, false>), grid, dim3(64 * NW), 0, L.stream,
+                       static_cast<const void *>(L.xf), L.W, L.M, static_cast<int>(L.K), static_cast<int>(L.E),
+                       L.logit_bf16, L.logits);
+  else
+    hipLaunchKernelGGL((route_tiny_logits_kernel<P, NW, true>), grid, dim3(64 * NW), 0, L.stream,
+                       static_cast<const void *>(L.xb), L.W, L.M, static_cast<int>(L.K), static_cast<int>(L.E),
+                       L.logit_bf16, L.logits);
   return hipGetLastError();
 }
 
@@ -132,7 +150,7 @@ static hipError_t launch_tiny_p(const RouteLaunch &L) {
 }
 
 bool tiny_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
-  return x_f32 && has_logits && K % 4 == 0 && K <= 4096 && E % 64 == 0 && E <= 1024;
+  return has_logits && K % (x_f32 ? 4 : 8) == 0 && K <= 4096 && E % 64 == 0 && E <= 1024;
 }
 
 hipError_t launch_route_tiny_logits(const RouteLaunch &L) {

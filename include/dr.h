@@ -76,8 +76,9 @@ typedef DR_ENUM(dr_variant) {
                              logits output */
   DR_VARIANT_TINY = 5     /* a few tokens: each lane runs (expert, K-block) chains on the vector
                              ALUs with the workgroup's W slice in LDS, the blocks combine across
-                             lanes, then the selection kernel; needs fp32 x, K % 4 == 0,
-                             K <= 4096 and the logits output */
+                             lanes, then the selection kernel; needs K % 4 == 0 (fp32 x)
+                             or K % 8 == 0 (bf16 x, widened when read), K <= 4096
+                             and the logits output */
 } dr_variant;
 
 /* Divide the k selected weights by their sum (left to right in rank order). */
@@ -133,11 +134,12 @@ typedef struct dr_contract_info {
  *            families passes a buffer anyway (the Python binding does).
  *   margins  [M] or NULL.
  *
- * bf16 x runs the register-staged families only (tiled, row-wise: ~120 us
- * at K = 2048, E = 256 for any M up to 8192 on MI355X).  Widening it first
- * with dr_widen_bf16 and passing DR_F32 gives the same bits through the
- * LDS-staged families: 16 us at M = 64 and 103 us at M = 8192, the widening
- * included.  The Python binding does this by itself.
+ * bf16 x takes the vector-ALU family for small batches (as fp32 x does,
+ * K % 8 == 0) and otherwise the register-staged families (tiled, row-wise:
+ * ~120 us at K = 2048, E = 256 for any M up to 8192 on MI355X).  Above the
+ * small batches, widening it first with dr_widen_bf16 and passing DR_F32
+ * gives the same bits through the LDS-staged families (113 us at M = 8192,
+ * the widening included).  The Python binding does this by itself.
  *
  * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32;
  * 0 <= M <= 2^22 tokens per call (larger M is DR_ERR_INVALID).

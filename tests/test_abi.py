@@ -242,4 +242,7 @@ def test_widen_bf16_validation(L):
     assert L.dr_widen_bf16(A, 8, A + 4, None) == INVALID  # misaligned out
     assert L.dr_widen_bf16(None, 0, None, None) == OK      # empty: nothing launched
     assert not dr.widen_bf16_used(8192, 8192 * 4, 256)     # K above the fp32 families' limits
-    assert dr.widen_bf16_used(1, 2048, 256) and dr.widen_bf16_used(8192, 2048, 256)
+    # small batches: the vector-ALU family reads bf16 x itself (K % 8 == 0)
+    assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (1, 64, 65)] == ["tiny", "tiny", "tiled"]
+    assert dr.auto_variant(1, 2044, 256, "bf16") != "tiny" and dr.auto_variant(1, 2044, 256) == "tiny"
+    assert [dr.widen_bf16_used(M, 2048, 256) for M in (1, 64, 65, 8192)] == [False, False, True, True]

@@ -71,3 +71,19 @@ def test_bf16_route_equals_fp32_route_and_bf16_families(data, M):
         assert_route_equal(got, gpu_route_np(dr, xb, Wd, TOPK, variant="tiled"), what=f"tiled, M={M}")
     if M <= 65:
         assert_route_equal(got, oracle_route(xf[:M], W, TOPK), what=f"oracle, M={M}")
+
+
+@pytest.mark.parametrize("Kx", [8, 264, 1000, 2048, 4096])
+def test_tiny_reads_bf16_directly(Kx):
+    """The vector-ALU family staging bf16 x as it is (widening when read),
+    forced at batches that take four and eight wavefronts per workgroup and
+    several rounds, against the oracle on the widened rows."""
+    dr = require_gpu()
+    rng = np.random.default_rng(Kx)
+    W = (rng.standard_normal((Kx, 256)) * 0.05).astype(np.float32)
+    for M in (1, 37, 200):
+        xb = torch.from_numpy(rng.standard_normal((M, Kx)).astype(np.float32)).to(torch.bfloat16)
+        x = xb.float().numpy()
+        note(f"tiny bf16 x K={Kx} M={M}")
+        got = gpu_route_np(dr, xb.cuda(), dev(W), 6, variant="tiny")
+        assert_route_equal(got, oracle_route(x, W, 6), what=f"tiny bf16 K={Kx} M={M}")
