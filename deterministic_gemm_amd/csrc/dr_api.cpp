@@ -77,7 +77,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
     return fail(DR_ERR_UNSUPPORTED, "tiled variant does not support E=%lld", (long long)E);
   if (variant == DR_VARIANT_SPLIT && !drk::split_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
-                "split variant needs fp32 x, K %% 4 == 0, E in {256, 512} and the logits output");
+                "split variant needs E in {256, 512}, the logits output, and fp32 x with K %% 4 == 0 or bf16 x "
+                "with K %% 8 == 0 and K <= 4096");
   if (variant == DR_VARIANT_NARROW && !drk::narrow_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
                 "narrow variant needs fp32 x, K %% 4 == 0, E <= 512 and the logits output");

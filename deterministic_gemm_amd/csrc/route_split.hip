@@ -31,10 +31,15 @@ namespace drk {
 // 2^ceil(log2 G) leaves, part q taking groups [qP/2, (q+1)P/2)), each part on
 // its own half of every stage; the two part values are added at the end,
 // which is the tree's top level, so the logits are the same bits.
-template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_, int KP_ = 1, bool LATE_ = false>
+// XB: x holds bf16 bits (K % 8 == 0), staged as they are, 8 values per
+// 16-byte unit, and widened exactly when read; else fp32, 4 per unit.
+template <int E_, int ET_, int AT_, int BT_, int WT_, int KC_, int S_, int KP_ = 1, bool LATE_ = false,
+          bool XB_ = false>
 struct SplitCfg {
   static constexpr int E = E_, ET = ET_, AT = AT_, BT = BT_, WT = WT_, KC = KC_, S = S_, KP = KP_;
   static constexpr bool LATE = LATE_;  // refill the freed stage after the chunk's matrix steps
+  static constexpr bool XB = XB_;
+  static constexpr int XV = XB ? 8 : 4;       // x values per 16-byte unit
   static constexpr int EW = 16 * BT;          // experts per wavefront
   static constexpr int NWE = ET / EW;         // wavefronts across the expert tile
   static constexpr int NWP = NWE * WT;        // wavefronts per part
@@ -43,16 +48,16 @@ struct SplitCfg {
   static constexpr int TW = 16 * AT;          // tokens per wavefront
   static constexpr int TT = WT * TW;          // tokens per workgroup
   static constexpr int NET = E / ET;          // expert tiles
-  static constexpr int HU = KC / 4;           // 16-byte x units per (slot, token) row
+  static constexpr int HU = KC / XV;          // 16-byte x units per (slot, token) row
   static constexpr int SW = KC * ET + 16;     // W slot stride (floats), +16 staggers banks
   static constexpr int WST = 4 * SW;          // W floats per stage and part
-  static constexpr int XST = 4 * TT * KC;     // x floats per stage and part
+  static constexpr int XST = 4 * TT * HU * 4;  // x floats (4-byte words) per stage and part
   static constexpr int PST = WST + XST;       // floats per stage and part
   static constexpr int STG = KP * PST;        // floats per stage
   static constexpr int LGP = ET + 4;          // logit tile pitch (floats)
   static constexpr int WI = 4 * KC * ET / 256;  // W transfers (64 lanes x 16 B) per chunk
   static constexpr int WIW = WI / NWP;          // ... per wavefront of the part
-  static constexpr int XU = TT * KC;            // x 16-byte units per chunk
+  static constexpr int XU = 4 * TT * HU;        // x 16-byte units per chunk
   static constexpr int XI = XU / 64;            // x transfers per chunk
   static constexpr int XIW = XI / NWP;          // ... per wavefront of the part
   static constexpr int PER = WIW + XIW;         // transfers per chunk per wavefront
@@ -63,7 +68,7 @@ struct SplitCfg {
   static_assert(KP == 1 || KP == 2, "parts");
   static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
   static_assert(PER * (S - 1) <= 63, "vmcnt range");
-  static_assert(KC % 4 == 0 && 256 % KC == 0 && (S == 3 || S == 4), "chunking");
+  static_assert(KC % XV == 0 && 256 % KC == 0 && (S == 3 || S == 4), "chunking");
   static_assert(TT * LGP + (KP - 1) * NWP * AT * BT * 4 * 64 <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");
   static_assert(S * STG * 4 <= 160 * 1024, "LDS");
@@ -73,7 +78,7 @@ struct SplitCfg {
 // Transfers of chunk ci into `stage`; the same scheme as the fused kernel's
 // dma_issue (route_tiled.hip), with W columns e0 .. e0+ET-1 only.
 template <class C>
-__device__ __forceinline__ void split_issue(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+__device__ __forceinline__ void split_issue(const void *__restrict__ xv, const float *__restrict__ W, int64_t M,
                                             int K, int64_t m0, int e0, int nb, int nchunks, int span, int wave,
                                             int lane, int ci, float *stage) {
   constexpr int E = C::E, ET = C::ET, KC = C::KC, TT = C::TT, HU = C::HU;
@@ -104,7 +109,10 @@ __device__ __forceinline__ void split_issue(const float *__restrict__ xf, const 
       dma16(src, lds);
     }
   }
-  const float *xrow0 = xf + m0 * K;
+  // x as stored: fp32 or bf16 bits, XS bytes a value
+  constexpr int XS = C::XB ? 2 : 4;
+  const char *xb = static_cast<const char *>(xv);
+  const char *xrow0 = xb + m0 * K * XS;
 #pragma unroll
   for (int i = 0; i < C::XIW; ++i) {
     const int u = (wave * C::XIW + i) * 64 + lane;  // x unit within the chunk
@@ -113,14 +121,14 @@ __device__ __forceinline__ void split_issue(const float *__restrict__ xf, const 
     const int tok = rem / HU, hp = rem % HU;
     const int h = hp ^ C::swz(tok);
     const int blk = 4 * g + s;
-    const int kg = blk * 256 + kk0 + 4 * h;
+    const int kg = blk * 256 + kk0 + C::XV * h;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + C::WST + (wave * C::XIW + i) * 64 * 4));
     if (full_k && full_m) {
-      dma16_s(xrow0, static_cast<uint32_t>((tok * K + kg) * 4), lds);
+      dma16_s(reinterpret_cast<const float *>(xrow0), static_cast<uint32_t>((tok * K + kg) * XS), lds);
     } else {
       const int64_t m = m0 + tok;
       const void *src = &g_pad_pos;
-      if (live && blk < nb && kg < K && m < M) src = xf + m * K + kg;
+      if (live && blk < nb && kg < K && m < M) src = xb + (m * K + kg) * XS;
       dma16(src, lds);
     }
   }
@@ -130,7 +138,7 @@ __device__ __forceinline__ void split_issue(const float *__restrict__ xf, const 
 // the previous chunk, then 4 slots x KC chain steps on the matrix cores; at
 // the end of a group of four K-blocks, fold the group's partials.
 template <class C, int MAXL>
-__device__ __forceinline__ void split_step(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+__device__ __forceinline__ void split_step(const void *__restrict__ xf, const float *__restrict__ W, int64_t M,
                                            int K, int64_t m0, int e0, int nb, int nchunks, int span, int wave,
                                            int lane, int ci, const float *cur, float *refill,
                                            f32x16 (&acc)[C::AT][C::BT], f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
@@ -168,7 +176,14 @@ __device__ __forceinline__ void split_step(const float *__restrict__ xf, const f
 #pragma unroll
     for (int a = 0; a < AT; ++a) {
       const int tok = tb + a * 16 + r_l;
-      av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+      if constexpr (C::XB) {
+        // unit c4 / 2 of the row holds 8 values; this step's 4 are its half c4 % 2
+        const uint2 u = *reinterpret_cast<const uint2 *>(
+            xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4 + (c4 & 1) * 2);
+        av[a] = make_float4(u2f(u.x << 16), u2f(u.x & 0xFFFF0000u), u2f(u.y << 16), u2f(u.y & 0xFFFF0000u));
+      } else {
+        av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+      }
     }
     float bw[BT][4];
 #pragma unroll
@@ -215,7 +230,7 @@ __device__ __forceinline__ void split_step(const float *__restrict__ xf, const f
 // indices eight apart: they land on the same XCD and share its L2, and x is
 // fetched from HBM once.  Blocks past the last token tile exit at once.
 template <class C, int MAXL>
-__global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const float *__restrict__ xf,
+__global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *__restrict__ xf,
                                                                    const float *__restrict__ W, int64_t M, int K,
                                                                    void *logits, int logit_bf16) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, STG = C::STG;
@@ -410,7 +425,8 @@ static hipError_t launch_logits_cm(const RouteLaunch &L) {
   const int64_t ntt = (L.M + C::TT - 1) / C::TT;
   const int64_t nblk = (ntt + 7) / 8 * 8 * C::NET;
   hipLaunchKernelGGL((route_split_logits_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0,
-                     L.stream, L.xf, L.W, L.M, static_cast<int>(L.K), L.logits, L.logit_bf16);
+                     L.stream, C::XB ? static_cast<const void *>(L.xb) : static_cast<const void *>(L.xf), L.W, L.M,
+                     static_cast<int>(L.K), L.logits, L.logit_bf16);
   return hipGetLastError();
 }
 
@@ -451,7 +467,10 @@ static hipError_t launch_select_e(const RouteLaunch &L) {
 }
 
 bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
-  return (E == 256 || E == 512) && K >= 1 && K <= 16384 && (K % 4) == 0 && x_f32 && has_logits;
+  // bf16 x: the configurations of K <= 4096 (their x transfers divide
+  // evenly over the wavefronts at 8 values per unit)
+  return (E == 256 || E == 512) && K >= 1 && K <= (x_f32 ? 16384 : 4096) && (K % (x_f32 ? 4 : 8)) == 0 &&
+         has_logits;
 }
 
 bool select_supports(int64_t E) { return E == 64 || E == 128 || E == 256 || E == 512 || E == 1024; }
@@ -467,10 +486,18 @@ hipError_t launch_route_logits(const RouteLaunch &L) {
     // of 16 steps need too many registers for the deeper counter stacks of
     // K > 4096
     case 256:
+      if (!L.xf) {
+        if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
+        return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
+      }
       if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true>>(L);
       if (L.K > 4096) return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4, 1, true>>(L);
       return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
     case 512:
+      if (!L.xf) {
+        if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
+        return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
+      }
       if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true>>(L);
       if (L.K > 4096) return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4, 1, true>>(L);
       return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);

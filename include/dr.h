@@ -68,8 +68,9 @@ typedef DR_ENUM(dr_variant) {
   DR_VARIANT_ROWWISE = 1, /* few tokens per workgroup, vector FMA (small M) */
   DR_VARIANT_TILED = 2,   /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
   DR_VARIANT_SPLIT = 3,   /* (token, expert) tiles on matrix cores writing the logits, then a
-                             selection kernel reading them back; needs fp32 x, K % 4 == 0,
-                             E in {256, 512} and the logits output */
+                             selection kernel reading them back; needs E in {256, 512}, the
+                             logits output, and fp32 x with K % 4 == 0 or bf16 x (staged as
+                             it is, widened when read) with K % 8 == 0 and K <= 4096 */
   DR_VARIANT_NARROW = 4,  /* small batches: 16-token x 16-expert tiles whose wavefronts split
                              the K groups along the canonical tree, writing the logits, then
                              the selection kernel; needs fp32 x, K % 4 == 0, E <= 512 and the
@@ -134,12 +135,12 @@ typedef struct dr_contract_info {
  *            families passes a buffer anyway (the Python binding does).
  *   margins  [M] or NULL.
  *
- * bf16 x takes the vector-ALU family for small batches (as fp32 x does,
- * K % 8 == 0) and otherwise the register-staged families (tiled, row-wise:
- * ~120 us at K = 2048, E = 256 for any M up to 8192 on MI355X).  Above the
- * small batches, widening it first with dr_widen_bf16 and passing DR_F32
- * gives the same bits through the LDS-staged families (113 us at M = 8192,
- * the widening included).  The Python binding does this by itself.
+ * bf16 x (K % 8 == 0, K <= 4096) takes the vector-ALU family for small
+ * batches and the two-kernel family for large ones, as fp32 x does; in
+ * between, and at other K, the register-staged families (tiled, row-wise:
+ * ~120 us at K = 2048, E = 256 for any M up to 8192 on MI355X).  There,
+ * widening it first with dr_widen_bf16 and passing DR_F32 gives the same
+ * bits through the narrow tiles; the Python binding does this by itself.
  *
  * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32;
  * 0 <= M <= 2^22 tokens per call (larger M is DR_ERR_INVALID).

@@ -78,7 +78,8 @@ def test_route_variant_rejects(L):
     # the split family writes the logits and reads them back: it needs that
     # output, fp32 x in whole 16-byte pieces and E in {256, 512}
     assert _route(L, lg=0, variant=3) == UNSUPPORTED
-    assert _route(L, xd=1, variant=3) == UNSUPPORTED
+    assert _route(L, xd=1, K=8192, variant=3) == UNSUPPORTED  # bf16 x: K <= 4096 and K % 8 == 0
+    assert _route(L, xd=1, K=2044, variant=3) == UNSUPPORTED
     assert _route(L, K=2046, variant=3) == UNSUPPORTED
     assert _route(L, E=128, k=8, variant=3) == UNSUPPORTED
     assert _route(L, M=0, variant=3) == OK
@@ -219,7 +220,8 @@ def test_auto_variant_is_a_function_of_shape(L):
     assert [dr.auto_variant(M, 8192, 256) for M in (1280, 1281)] == ["narrow", "split"]
     assert [dr.auto_variant(M, 1024, 256) for M in (1280, 1281)] == ["narrow", "split"]
     assert dr.auto_variant(8192, 2048, 256, logits=False) == "tiled"
-    assert dr.auto_variant(8192, 2048, 256, x_dtype="bf16") == "tiled"
+    assert dr.auto_variant(8192, 2048, 256, x_dtype="bf16") == "split"  # bf16 x staged as it is
+    assert dr.auto_variant(8192, 8192, 256, x_dtype="bf16") == "tiled"
     assert dr.auto_variant(8192, 2046, 256) == "tiled"
 
 
@@ -245,4 +247,10 @@ def test_widen_bf16_validation(L):
     # small batches: the vector-ALU family reads bf16 x itself (K % 8 == 0)
     assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (1, 64, 65)] == ["tiny", "tiny", "tiled"]
     assert dr.auto_variant(1, 2044, 256, "bf16") != "tiny" and dr.auto_variant(1, 2044, 256) == "tiny"
-    assert [dr.widen_bf16_used(M, 2048, 256) for M in (1, 64, 65, 8192)] == [False, False, True, True]
+    # large batches: the two-kernel family stages bf16 x itself (K % 8 == 0,
+    # K <= 4096); between the two the binding widens bf16 x for narrow tiles
+    assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (2048, 2049, 8192)] == ["tiled", "split", "split"]
+    assert dr.auto_variant(8192, 8192, 256, "bf16") != "split" and dr.auto_variant(8192, 8192, 256) == "split"
+    assert dr.auto_variant(8192, 2044, 256, "bf16") != "split"
+    assert [dr.widen_bf16_used(M, 2048, 256) for M in (1, 64, 65, 2048, 2049, 8192)] == [False, False, True, True,
+                                                                                        False, False]

@@ -87,3 +87,22 @@ def test_tiny_reads_bf16_directly(Kx):
         note(f"tiny bf16 x K={Kx} M={M}")
         got = gpu_route_np(dr, xb.cuda(), dev(W), 6, variant="tiny")
         assert_route_equal(got, oracle_route(x, W, 6), what=f"tiny bf16 K={Kx} M={M}")
+
+
+@pytest.mark.parametrize("Kx,Ex,kx", [(8, 256, 8), (264, 256, 8), (1000, 512, 10), (2048, 256, 8), (2056, 256, 8),
+                                      (4096, 512, 10)])
+def test_split_reads_bf16_directly(Kx, Ex, kx):
+    """The two-kernel family staging bf16 x as it is (8 values per 16-byte
+    unit, widened when read), in its one-part and two-part configurations,
+    with ragged token tiles and K tails, against the oracle."""
+    dr = require_gpu()
+    rng = np.random.default_rng(Kx + Ex)
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    for M in (70, 300, 2100):
+        xb = torch.from_numpy(rng.standard_normal((M, Kx)).astype(np.float32)).to(torch.bfloat16)
+        x = xb.float().numpy()
+        note(f"split bf16 x K={Kx} E={Ex} M={M}")
+        got = gpu_route_np(dr, xb.cuda(), dev(W), kx, variant="split")
+        assert_route_equal(got, oracle_route(x, W, kx), what=f"split bf16 K={Kx} E={Ex} M={M}")
+        got_bf = gpu_route_np(dr, xb.cuda(), dev(W), kx, variant="split", logit_dtype="bf16")
+        assert_route_equal(got_bf, oracle_route(x, W, kx, logits_bf16=True), what=f"split bf16 logits K={Kx} M={M}")
