@@ -81,7 +81,7 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
                 "with K %% 8 == 0 and K <= 4096");
   if (variant == DR_VARIANT_NARROW && !drk::narrow_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
-                "narrow variant needs fp32 x, K %% 4 == 0, E <= 512 and the logits output");
+                "narrow variant needs E <= 512, the logits output, and K %% 4 == 0 (fp32 x) or K %% 8 == 0 (bf16 x)");
   if (variant == DR_VARIANT_TINY && !drk::tiny_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED, "tiny variant needs K %% 4 == 0 (fp32 x) or K %% 8 == 0 (bf16 x), K <= 4096 and the logits output");
   if (variant == DR_VARIANT_TINY && M > drk::kTinyMaxRows)

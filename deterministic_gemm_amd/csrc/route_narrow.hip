@@ -26,26 +26,30 @@
 
 namespace drk {
 
-template <int E_, int AT_, int BT_, int KG_, int KC_, int S_>
+// XB: x holds bf16 bits (K % 8 == 0), staged as they are, 8 values per
+// 16-byte unit, and widened exactly when read; else fp32, 4 per unit.
+template <int E_, int AT_, int BT_, int KG_, int KC_, int S_, bool XB_ = false>
 struct NarrowCfg {
   static constexpr int E = E_, AT = AT_, BT = BT_, KG = KG_, KC = KC_, S = S_;
+  static constexpr bool XB = XB_;
+  static constexpr int XV = XB ? 8 : 4;       // x values per 16-byte unit
   static constexpr int TT = 16 * AT, ET = 16 * BT;  // tokens, experts per workgroup
   static constexpr int NT = 64 * KG;
   static constexpr int NET = E / ET;
-  static constexpr int HU = KC / 4;           // 16-byte x units per (slot, token) row
+  static constexpr int HU = KC / XV;          // 16-byte x units per (slot, token) row
   static constexpr int SW = KC * ET + 16;     // W slot stride (floats), +16 staggers banks
   static constexpr int WST = 4 * SW;
-  static constexpr int XST = 4 * TT * KC;
+  static constexpr int XST = 4 * TT * HU * 4;  // x floats (4-byte words) per stage
   static constexpr int STG = WST + XST;       // floats per stage
   static constexpr int WU = KC * ET / 4;      // W units per slot
   static constexpr int WI = 4 * WU / 64;      // W transfers per chunk
-  static constexpr int XI = TT * KC / 64;     // x transfers per chunk
+  static constexpr int XI = 4 * TT * HU / 64;  // x transfers per chunk
   static constexpr int PER = WI + XI;
   static constexpr int CPG = 256 / KC;
   static constexpr int NQ = AT * BT * 4;       // group partials per lane
-  static_assert(WU % 64 == 0 && WI >= 1 && XI >= 1 && XI * 64 == TT * KC, "whole transfers");
+  static_assert(WU % 64 == 0 && WI >= 1 && XI >= 1 && XI * 64 == 4 * TT * HU, "whole transfers");
   static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
-  static_assert(KC % 4 == 0 && 256 % KC == 0, "chunking");
+  static_assert(KC % XV == 0 && 256 % KC == 0, "chunking");
   static_assert(KG == 1 || KG == 2 || KG == 4, "parts");
   static_assert((KG * S * STG + (KG - 1) * 64 * NQ) * 4 <= 160 * 1024, "LDS");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
@@ -55,7 +59,7 @@ struct NarrowCfg {
 // group) into `stage`; past the wave's last chunk, padding transfers keep the
 // count fixed.
 template <class C>
-__device__ __forceinline__ void narrow_issue(const float *__restrict__ xf, const float *__restrict__ W, int64_t M,
+__device__ __forceinline__ void narrow_issue(const void *__restrict__ xv, const float *__restrict__ W, int64_t M,
                                              int K, int64_t m0, int e0, int nb, int g0, int nch, int lane, int ci,
                                              float *stage) {
   constexpr int E = C::E, ET = C::ET, KC = C::KC, TT = C::TT, HU = C::HU;
@@ -83,17 +87,17 @@ __device__ __forceinline__ void narrow_issue(const float *__restrict__ xf, const
     const int tok = rem / HU, hp = rem % HU;
     const int h = hp ^ C::swz(tok);
     const int blk = 4 * g + s;
-    const int kg = blk * 256 + kk0 + 4 * h;
+    const int kg = blk * 256 + kk0 + C::XV * h;
     const uint32_t lds = __builtin_amdgcn_readfirstlane(lds_addr(stage + C::WST + i * 64 * 4));
     const int64_t m = m0 + tok;
     const void *src = &g_pad_pos;
-    if (live && blk < nb && kg < K && m < M) src = xf + m * K + kg;
+    if (live && blk < nb && kg < K && m < M) src = static_cast<const char *>(xv) + (m * K + kg) * (C::XB ? 2 : 4);
     dma16(src, lds);
   }
 }
 
 template <class C, int MAXL>
-__global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const float *__restrict__ xf,
+__global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const void *__restrict__ xf,
                                                                     const float *__restrict__ W, int64_t M, int K,
                                                                     void *logits, int logit_bf16) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, KC = C::KC, HU = C::HU;
@@ -144,13 +148,23 @@ __global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const float 
     narrow_issue<C>(xf, W, M, K, m0, e0, nb, g0, nch, lane, ci + S - 1, my + ((ci + S - 1) % S) * C::STG);
     const float *cur = my + (ci % S) * C::STG;
     const float *xs = cur + C::WST;
+    [[maybe_unused]] uint4 ux[AT];  // bf16 x: one 16-byte unit feeds two steps
 #pragma unroll
     for (int c4 = 0; c4 < KC / 4; ++c4) {
       float4 av[AT];
 #pragma unroll
       for (int a = 0; a < AT; ++a) {
         const int tok = a * 16 + r_l;
-        av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+        if constexpr (C::XB) {
+          // unit c4 / 2 of the row holds 8 values, read whole at even steps;
+          // this step's 4 are its half c4 % 2
+          if ((c4 & 1) == 0)
+            ux[a] = *reinterpret_cast<const uint4 *>(xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
+          const uint32_t lo = (c4 & 1) ? ux[a].z : ux[a].x, hi = (c4 & 1) ? ux[a].w : ux[a].y;
+          av[a] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
+        } else {
+          av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+        }
       }
       float bw[BT][4];
 #pragma unroll
@@ -231,7 +245,8 @@ template <class C, int MAXL>
 static hipError_t launch_narrow_cm(const RouteLaunch &L) {
   const int64_t nblk = (L.M + C::TT - 1) / C::TT * C::NET;
   hipLaunchKernelGGL((route_narrow_logits_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0,
-                     L.stream, L.xf, L.W, L.M, static_cast<int>(L.K), L.logits, L.logit_bf16);
+                     L.stream, C::XB ? static_cast<const void *>(L.xb) : static_cast<const void *>(L.xf), L.W, L.M,
+                     static_cast<int>(L.K), L.logits, L.logit_bf16);
   return hipGetLastError();
 }
 
@@ -262,20 +277,20 @@ static hipError_t launch_narrow_c(const RouteLaunch &L) {
 // 24 us (16 x 16 tiles: 30), 2048 38 us (the split kernels: 44); K = 4096, E =
 // 512: M = 240 22 us (four parts with four stages: 31), 512 40 us (59), 1024
 // 65 us (115).  More groups keep one part per group and four stages.
-template <int E>
+template <int E, bool XB>
 static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
-  if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4>>(L);
-  if (G > 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4>>(L);
+  if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4, XB>>(L);
+  if (G > 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4, XB>>(L);
   const int64_t slots = 2 * static_cast<int64_t>(device_cus());
   const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
   if (wgs(16, 16) <= slots) {
-    if (G == 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2>>(L);
-    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4>>(L);
+    if (G == 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2, XB>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4, XB>>(L);
   }
-  if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, 16, 3>>(L);
-  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, 8, 4>>(L);
+  if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, 16, 3, XB>>(L);
+  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, 8, 4, XB>>(L);
 }
 
 // The largest batch the narrow family takes before the split kernels: at
@@ -291,16 +306,16 @@ int64_t narrow_max_m(int64_t E, int64_t K) {
 }
 
 bool narrow_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
-  return (E == 64 || E == 128 || E == 256 || E == 512) && K >= 1 && K <= 16384 && (K % 4) == 0 && x_f32 &&
+  return (E == 64 || E == 128 || E == 256 || E == 512) && K >= 1 && K <= 16384 && (K % (x_f32 ? 4 : 8)) == 0 &&
          has_logits;
 }
 
 hipError_t launch_route_narrow_logits(const RouteLaunch &L) {
   switch (L.E) {
-    case 64: return launch_narrow_e<64>(L);
-    case 128: return launch_narrow_e<128>(L);
-    case 256: return launch_narrow_e<256>(L);
-    case 512: return launch_narrow_e<512>(L);
+    case 64: return L.xf ? launch_narrow_e<64, false>(L) : launch_narrow_e<64, true>(L);
+    case 128: return L.xf ? launch_narrow_e<128, false>(L) : launch_narrow_e<128, true>(L);
+    case 256: return L.xf ? launch_narrow_e<256, false>(L) : launch_narrow_e<256, true>(L);
+    case 512: return L.xf ? launch_narrow_e<512, false>(L) : launch_narrow_e<512, true>(L);
     default: return hipErrorInvalidValue;
   }
 }

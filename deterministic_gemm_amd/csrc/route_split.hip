@@ -170,6 +170,7 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
   if constexpr (!C::LATE) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
 
   const float *xs = cur + C::WST;
+  [[maybe_unused]] uint4 ux[AT];  // bf16 x: one 16-byte unit feeds two steps
 #pragma unroll
   for (int c4 = 0; c4 < KC / 4; ++c4) {
     float4 av[AT];
@@ -177,10 +178,12 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
     for (int a = 0; a < AT; ++a) {
       const int tok = tb + a * 16 + r_l;
       if constexpr (C::XB) {
-        // unit c4 / 2 of the row holds 8 values; this step's 4 are its half c4 % 2
-        const uint2 u = *reinterpret_cast<const uint2 *>(
-            xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4 + (c4 & 1) * 2);
-        av[a] = make_float4(u2f(u.x << 16), u2f(u.x & 0xFFFF0000u), u2f(u.y << 16), u2f(u.y & 0xFFFF0000u));
+        // unit c4 / 2 of the row holds 8 values, read whole at even steps;
+        // this step's 4 are its half c4 % 2
+        if ((c4 & 1) == 0)
+          ux[a] = *reinterpret_cast<const uint4 *>(xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
+        const uint32_t lo = (c4 & 1) ? ux[a].z : ux[a].x, hi = (c4 & 1) ? ux[a].w : ux[a].y;
+        av[a] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
       } else {
         av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
       }

@@ -73,8 +73,8 @@ typedef DR_ENUM(dr_variant) {
                              it is, widened when read) with K % 8 == 0 and K <= 4096 */
   DR_VARIANT_NARROW = 4,  /* small batches: 16-token x 16-expert tiles whose wavefronts split
                              the K groups along the canonical tree, writing the logits, then
-                             the selection kernel; needs fp32 x, K % 4 == 0, E <= 512 and the
-                             logits output */
+                             the selection kernel; needs E <= 512, the logits output, and
+                             K % 4 == 0 (fp32 x) or K % 8 == 0 (bf16 x, staged as it is) */
   DR_VARIANT_TINY = 5     /* a few tokens: each lane runs (expert, K-block) chains on the vector
                              ALUs with the workgroup's W slice in LDS, the blocks combine across
                              lanes, then the selection kernel; needs K % 4 == 0 (fp32 x)
@@ -135,12 +135,12 @@ typedef struct dr_contract_info {
  *            families passes a buffer anyway (the Python binding does).
  *   margins  [M] or NULL.
  *
- * bf16 x (K % 8 == 0, K <= 4096) takes the vector-ALU family for small
- * batches and the two-kernel family for large ones, as fp32 x does; in
- * between, and at other K, the register-staged families (tiled, row-wise:
- * ~120 us at K = 2048, E = 256 for any M up to 8192 on MI355X).  There,
- * widening it first with dr_widen_bf16 and passing DR_F32 gives the same
- * bits through the narrow tiles; the Python binding does this by itself.
+ * bf16 x with K % 8 == 0 takes the families fp32 x does (the two-kernel
+ * family up to K = 4096), staged as it is and widened when read.  Elsewhere
+ * it takes the register-staged families (tiled, row-wise: ~120 us at K =
+ * 2048, E = 256 for any M up to 8192 on MI355X); there, widening it first
+ * with dr_widen_bf16 and passing DR_F32 gives the same bits through the
+ * faster families, and the Python binding does this by itself.
  *
  * Supported: E in {64, 128, 256, 512, 1024}; 1 <= K <= 16384; k <= 32;
  * 0 <= M <= 2^22 tokens per call (larger M is DR_ERR_INVALID).

@@ -85,7 +85,7 @@ def test_route_variant_rejects(L):
     assert _route(L, M=0, variant=3) == OK
     # the narrow family has the same needs, with any E up to 512
     assert _route(L, lg=0, variant=4) == UNSUPPORTED
-    assert _route(L, xd=1, variant=4) == UNSUPPORTED
+    assert _route(L, xd=1, K=2044, variant=4) == UNSUPPORTED  # bf16 x: K % 8 == 0
     assert _route(L, E=1024, k=8, variant=4) == UNSUPPORTED
 
 
@@ -245,12 +245,13 @@ def test_widen_bf16_validation(L):
     assert L.dr_widen_bf16(None, 0, None, None) == OK      # empty: nothing launched
     assert not dr.widen_bf16_used(8192, 8192 * 4, 256)     # K above the fp32 families' limits
     # small batches: the vector-ALU family reads bf16 x itself (K % 8 == 0)
-    assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (1, 64, 65)] == ["tiny", "tiny", "tiled"]
+    assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (1, 64, 65)] == ["tiny", "tiny", "narrow"]
     assert dr.auto_variant(1, 2044, 256, "bf16") != "tiny" and dr.auto_variant(1, 2044, 256) == "tiny"
-    # large batches: the two-kernel family stages bf16 x itself (K % 8 == 0,
-    # K <= 4096); between the two the binding widens bf16 x for narrow tiles
-    assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (2048, 2049, 8192)] == ["tiled", "split", "split"]
+    # the narrow tiles and the two-kernel family stage bf16 x themselves
+    # (K % 8 == 0; the two-kernel family K <= 4096); the binding widens bf16
+    # x only where they do not
+    assert [dr.auto_variant(M, 2048, 256, "bf16") for M in (2048, 2049, 8192)] == ["narrow", "split", "split"]
     assert dr.auto_variant(8192, 8192, 256, "bf16") != "split" and dr.auto_variant(8192, 8192, 256) == "split"
     assert dr.auto_variant(8192, 2044, 256, "bf16") != "split"
-    assert [dr.widen_bf16_used(M, 2048, 256) for M in (1, 64, 65, 2048, 2049, 8192)] == [False, False, True, True,
-                                                                                        False, False]
+    assert not any(dr.widen_bf16_used(M, 2048, 256) for M in (1, 64, 65, 2048, 2049, 8192))
+    assert dr.widen_bf16_used(8192, 8192, 256) and not dr.widen_bf16_used(1024, 8192, 256)

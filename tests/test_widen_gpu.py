@@ -106,3 +106,20 @@ def test_split_reads_bf16_directly(Kx, Ex, kx):
         assert_route_equal(got, oracle_route(x, W, kx), what=f"split bf16 K={Kx} E={Ex} M={M}")
         got_bf = gpu_route_np(dr, xb.cuda(), dev(W), kx, variant="split", logit_dtype="bf16")
         assert_route_equal(got_bf, oracle_route(x, W, kx, logits_bf16=True), what=f"split bf16 logits K={Kx} M={M}")
+
+
+@pytest.mark.parametrize("Kx,Ex,kx,Ms", [(264, 256, 8, (5, 70)), (1000, 64, 4, (33,)), (2048, 256, 8, (70, 600, 2000)),
+                                         (4096, 512, 10, (19, 240)), (5000, 256, 8, (40,))])
+def test_narrow_reads_bf16_directly(Kx, Ex, kx, Ms):
+    """The narrow tiles staging bf16 x as they are, in every tile and part
+    configuration (one to four K-group parts; 16 x 16, 32 x 16 and 32 x 32
+    tiles; chunks of 16 and 8 steps), against the oracle."""
+    dr = require_gpu()
+    rng = np.random.default_rng(Kx * 3 + Ex)
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    for M in Ms:
+        xb = torch.from_numpy(rng.standard_normal((M, Kx)).astype(np.float32)).to(torch.bfloat16)
+        x = xb.float().numpy()
+        note(f"narrow bf16 x K={Kx} E={Ex} M={M}")
+        got = gpu_route_np(dr, xb.cuda(), dev(W), kx, variant="narrow")
+        assert_route_equal(got, oracle_route(x, W, kx), what=f"narrow bf16 K={Kx} E={Ex} M={M}")
