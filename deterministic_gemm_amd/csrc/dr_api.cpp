@@ -77,7 +77,7 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
     return fail(DR_ERR_UNSUPPORTED, "tiled variant does not support E=%lld", (long long)E);
   if (variant == DR_VARIANT_SPLIT && !drk::split_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
-                "split variant needs E in {256, 512}, the logits output, and fp32 x with K %% 4 == 0 or bf16 x "
+                "split variant needs E in {256, 512, 1024}, the logits output, and fp32 x with K %% 4 == 0 or bf16 x "
                 "with K %% 8 == 0 and K <= 4096");
   if (variant == DR_VARIANT_NARROW && !drk::narrow_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
@@ -135,7 +135,11 @@ int device_cus() {
 extern "C" {
 
 dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits) {
-  const int64_t narrow_max = drk::narrow_max_m(E, K);
+  // where the narrow family does not take E, the two-kernel family follows
+  // the vector-ALU family directly (or takes every batch, past its K)
+  const int64_t narrow_max = drk::narrow_supports(E, K, true, true) ? drk::narrow_max_m(E, K)
+                             : drk::tiny_supports(E, K, true, true)  ? drk::tiny_max_m(E, K)
+                                                                     : 0;
   if (M > narrow_max && drk::split_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_SPLIT;
   if (M <= drk::tiny_max_m(E, K) && drk::tiny_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_TINY;
   if (M <= narrow_max && drk::narrow_supports(E, K, x_dtype == DR_F32, with_logits != 0)) return DR_VARIANT_NARROW;

@@ -472,7 +472,7 @@ static hipError_t launch_select_e(const RouteLaunch &L) {
 bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits) {
   // bf16 x: the configurations of K <= 4096 (their x transfers divide
   // evenly over the wavefronts at 8 values per unit)
-  return (E == 256 || E == 512) && K >= 1 && K <= (x_f32 ? 16384 : 4096) && (K % (x_f32 ? 4 : 8)) == 0 &&
+  return (E == 256 || E == 512 || E == 1024) && K >= 1 && K <= (x_f32 ? 16384 : 4096) && (K % (x_f32 ? 4 : 8)) == 0 &&
          has_logits;
 }
 
@@ -504,6 +504,14 @@ hipError_t launch_route_logits(const RouteLaunch &L) {
       if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true>>(L);
       if (L.K > 4096) return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4, 1, true>>(L);
       return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
+    case 1024:
+      if (!L.xf) {
+        if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
+        return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
+      }
+      if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true>>(L);
+      if (L.K > 4096) return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 8, 4, 1, true>>(L);
+      return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
     default: return hipErrorInvalidValue;
   }
 }

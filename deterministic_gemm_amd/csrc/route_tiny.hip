@@ -171,12 +171,14 @@ hipError_t launch_route_tiny(const RouteLaunch &L) {
 // Batches this family takes: while its workgroups, with as many wavefronts as
 // LDS allows, fit the CUs at once; past that a second round of workgroups
 // costs as much as the first, and the narrow family is faster.  Where the
-// narrow family does not take E, up to 4096 tokens: measured at E = 1024
-// against the row-wise family, the one left, 128 against 1917 us at M = 256
-// and 3167 against 5879 at M = 8192 (K = 2048); at K = 4096 6.7 against
-// 7.8 ms at M = 4096, but 13.4 against 11.7 at M = 8192.
+// narrow family does not take E but the two-kernel family does (E = 1024),
+// up to 64 tokens at K <= 2048 and 32 above: measured at E = 1024 (full
+// route), 42 against 59 us at M = 64 and 68 against 59 at M = 128 (K =
+// 2048); 73 against 101 at M = 32 and 125 against 99 at M = 64 (K = 4096).
+// Where neither does, up to 4096 tokens against the row-wise family, the one
+// left (E = 1024, K = 2048: 128 against 1917 us at M = 256).
 int64_t tiny_max_m(int64_t E, int64_t K) {
-  if (!narrow_supports(E, K, true, true)) return 4096;
+  if (!narrow_supports(E, K, true, true)) return split_supports(E, K, true, true) ? (K <= 2048 ? 64 : 32) : 4096;
   int p = 1;
   while (p < (K + 255) / 256) p <<= 1;
   const int64_t nw = p <= 8 ? 8 : 4, groups = E * p / 64;

@@ -68,7 +68,7 @@ typedef DR_ENUM(dr_variant) {
   DR_VARIANT_ROWWISE = 1, /* few tokens per workgroup, vector FMA (small M) */
   DR_VARIANT_TILED = 2,   /* token tiles on fp32 matrix cores, one K=1 MFMA step per fmaf */
   DR_VARIANT_SPLIT = 3,   /* (token, expert) tiles on matrix cores writing the logits, then a
-                             selection kernel reading them back; needs E in {256, 512}, the
+                             selection kernel reading them back; needs E in {256, 512, 1024}, the
                              logits output, and fp32 x with K % 4 == 0 or bf16 x (staged as
                              it is, widened when read) with K % 8 == 0 and K <= 4096 */
   DR_VARIANT_NARROW = 4,  /* small batches: 16-token x 16-expert tiles whose wavefronts split

@@ -207,7 +207,10 @@ def test_auto_variant_is_a_function_of_shape(L):
     assert [dr.auto_variant(M, 2048, 512) for M in (32, 33)] == ["tiny", "narrow"]
     assert [dr.auto_variant(M, 1024, 256) for M in (128, 129)] == ["tiny", "narrow"]
     assert dr.auto_variant(19, 2048, 1024) == "tiny"
-    assert [dr.auto_variant(M, 2048, 1024) for M in (4096, 4097)] == ["tiny", "rowwise"]
+    # E = 1024: the two-kernel family right after the vector-ALU family
+    assert [dr.auto_variant(M, 2048, 1024) for M in (64, 65, 8192)] == ["tiny", "split", "split"]
+    assert [dr.auto_variant(M, 4096, 1024) for M in (32, 33)] == ["tiny", "split"]
+    assert [dr.auto_variant(M, 8192, 1024) for M in (1, 8192)] == ["split", "split"]
     assert dr.auto_variant(19, 8192, 256) == "narrow"   # K above the vector family's 4096
     # large batches that ask for the logits take the two-kernel family: at
     # 1024 < K <= 4096 above 2048 tokens for E = 256 and 1024 for E = 512

@@ -192,7 +192,7 @@ def test_every_supported_e(dr, Ex, kx):
     for variant in ("auto", "rowwise", "tiled", "split", "narrow", "tiny"):
         if variant in ("tiled", "narrow") and Ex == 1024:
             continue
-        if variant == "split" and Ex not in (256, 512):
+        if variant == "split" and Ex not in (256, 512, 1024):
             continue
         note(f"E={Ex} k={kx} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
@@ -259,3 +259,18 @@ def test_rows_at_any_offset(dr, router_w, sweep):
             rows = slice(shift, shift + 50)
             assert_route_equal(tuple(g[rows] for g in got), tuple(r[1000:1050] for r in ref),
                                what=f"shift={shift} {variant}")
+
+
+@pytest.mark.parametrize("Kx,M", [(2048, 2100), (4096, 600), (264, 1500)])
+def test_split_at_1024_experts(dr, Kx, M):
+    """The two-kernel family at E = 1024 (eight 128-expert tiles, or sixteen
+    64-expert tiles in two parts), fp32 and bf16 x, against the oracle."""
+    rng = np.random.default_rng(Kx + M)
+    W = (rng.standard_normal((Kx, 1024)) * 0.05).astype(np.float32)
+    xb = torch.from_numpy(rng.standard_normal((M, Kx)).astype(np.float32)).to(torch.bfloat16)
+    x = xb.float().numpy()
+    ref = oracle_route(x, W, 8)
+    for xd in (dev(x), xb.cuda()):
+        note(f"split E=1024 K={Kx} M={M} x {xd.dtype}")
+        got = gpu_route_np(dr, xd, dev(W), 8, variant="split")
+        assert_route_equal(got, ref, what=f"split E=1024 K={Kx} M={M} {xd.dtype}")
