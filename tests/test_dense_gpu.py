@@ -31,10 +31,11 @@ def test_gemm_rows_invariant_across_m_and_close_to_exact(dense):
     note("gemm M=4096")
     full = dr.gemm_bf16(xd, Wd).cpu().numpy()
     # the sweep sizes plus others so that, on a 256-CU device, every tile
-    # configuration runs: 32 x 32 (M <= 128), 64 x 64 (200, 256), 64 x 128
-    # (512), 128 x 128 (1000, 1024), 256 x 128 (2048), 256 x 256 (3000, 4096),
-    # several with a ragged last tile
-    for M in sorted(set(wl.DENSE_MS) | {200, 256, 1000, 1024, 2048, 3000}):
+    # configuration N = 4096 reaches runs: 32 x 32 (M <= 128), 64 x 64 (200,
+    # 256), 64 x 64 with two stages (300, 512), 128 x 128 (1000, 1024),
+    # 256 x 128 (2048), 256 x 256 (3000, 4096), several with a ragged last
+    # tile (64 x 128 runs where M > N: the bf16 router's logits GEMM)
+    for M in sorted(set(wl.DENSE_MS) | {200, 256, 300, 1000, 1024, 2048, 3000}):
         note(f"gemm M={M}")
         out = dr.gemm_bf16(xd[:M].contiguous(), Wd).cpu().numpy()
         assert f32_equal_bits(out, full[:M]), f"M={M} rows differ from the M=4096 run"
