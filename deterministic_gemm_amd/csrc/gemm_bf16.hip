@@ -439,7 +439,7 @@ static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *ou
   if (M <= 128 || tiles(32, 32) <= 2 * cus)
     return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>, OutT>(x, W, out, M, K, N, stream);
   if (tiles(64, 64) <= cus) return launch_gemm_c<GemmCfg<64, 64, 2, 2, 128, 3>, OutT>(x, W, out, M, K, N, stream);
-  // two 64 KiB stages, so two workgroups share a CU and twice the tiles run
+  // two 32 KiB stages (64 KiB), so two workgroups share a CU and twice the tiles run
   // in one round; worth it while W, not x, is most of the traffic (M <= N):
   // 30.7 against 37.5 us at M = 512, K = N = 4096, but 30.0 against 23.7 at
   // M = 8192, K = 2048, N = 256, where each x row is read by more tiles

@@ -60,20 +60,31 @@ def test_gemm_row_offsets(dense):
 
 
 def test_gemm_small_shapes_close_to_exact():
+    """Within the stated 1e-2 absolute of the exact product.  The inputs are
+    bf16, so every product is exact in fp32 and the only error is the fp32
+    accumulation's: at most about K * 2^-24 * sum_k |x_k w_k|, which for these
+    N(0,1) operands (K <= 224, sum |x w| <= ~200) is below 3e-3 even as a
+    worst case, and typically ~1e-5."""
     dr = require_gpu()
     rng = np.random.default_rng(3)
     # partial K stages and ragged M tiles in every tile configuration (on a
-    # 256-CU device: 32 x 32 for the first six, then 64 x 64, 64 x 128,
-    # 128 x 128, 256 x 128 and twice 256 x 256)
-    for (M, K, N) in ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
-                      (1500, 160, 256), (200, 160, 4096), (450, 96, 4096), (900, 224, 4096), (1800, 96, 4096),
-                      (2100, 96, 4096), (4100, 160, 4096)):
+    # 256-CU device: 32 x 32 for the first six, then 64 x 64, 64 x 64 with
+    # two stages, 128 x 128, 256 x 128, twice 256 x 256, and 64 x 128, which
+    # runs only where M > N: a ragged 48-row last tile and a partial K stage)
+    shapes = ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
+              (1500, 160, 256), (200, 160, 4096), (450, 96, 4096), (900, 224, 4096), (1800, 96, 4096),
+              (2100, 96, 4096), (4100, 160, 4096), (6000, 96, 256))
+    worst = 0.0
+    for (M, K, N) in shapes:
         xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
         Wb = wl.to_bf16_bits(rng.standard_normal((K, N)).astype(np.float32))
         note(f"gemm small {M}x{K}x{N}")
         out = dr.gemm_bf16(dev_bf16_bits(xb), dev_bf16_bits(Wb)).cpu().numpy()
         ref = oracle.gemm_bf16_ref(xb, Wb)
-        assert np.abs(out - ref).max() <= TOL * max(1.0, np.abs(ref).max() / 10)
+        err = float(np.abs(out.astype(np.float64) - ref.astype(np.float64)).max())
+        worst = max(worst, err)
+        assert err <= TOL, (M, K, N, err)
+    print(f"small shapes: max |delta| vs exact {worst:.3e} over {len(shapes)} shapes")
 
 
 def test_gate_dot_bit_exact_and_m_invariant(dense):
