@@ -26,10 +26,9 @@ __device__ __forceinline__ u32x4 buf_rsrc(const void *base, int64_t nbytes) {
 
 // Every active lane moves the 16 bytes at byte offset voff of the descriptor's
 // range (zeros past it) to LDS address lds_base + 16 * lane; inline assembly
-// for the reason given at dma16.
+// for the reason given at dma16, with the LDS base as an m0 operand likewise.
 __device__ __forceinline__ void dma16_buf(uint32_t voff, u32x4 rsrc, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "s"(lds_base)
-               : "memory");
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds_base) : "memory");
 }
 
 }  // namespace drk

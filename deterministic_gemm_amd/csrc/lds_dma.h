@@ -30,16 +30,18 @@ __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory")
 // to LDS address lds_base + 16 * lane.  Written as inline assembly so that
 // the compiler's wait-count pass does not treat it as an LDS write to be
 // drained before every LDS read; the kernel orders these transfers itself
-// (wait_vmcnt + barrier).  m0 is used only here.
+// (wait_vmcnt + barrier).  The LDS base goes in as an m0 operand ("{m0}"), so
+// the compiler writes m0 itself and knows the statement reads it: no value
+// of its own is ever kept in m0 across the transfer.
 __device__ __forceinline__ void dma16(const void *src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds_base) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
 }
 
 // The same transfer addressed as a 64-bit SGPR base plus a 32-bit per-lane
 // byte offset: half the per-lane address operand, which measurably reduces the
 // time each transfer takes from the matrix cores' issue.
 __device__ __forceinline__ void dma16_s(const float *base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_base) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const float *p) {
