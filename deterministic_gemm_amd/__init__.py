@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libdr.so")
 
 DR_OK, DR_ERR_INVALID, DR_ERR_UNSUPPORTED, DR_ERR_DEVICE = 0, 1, 2, 3
 DR_F32, DR_BF16 = 0, 1
-VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3, "narrow": 4, "tiny": 5}
+VARIANTS = {"auto": 0, "rowwise": 1, "tiled": 2, "split": 3, "narrow": 4, "tiny": 5, "fused": 6}
 VARIANT_NAMES = {v: k for k, v in VARIANTS.items()}
 DR_ROUTE_RENORMALIZE = 1
 
@@ -128,6 +128,31 @@ def _dev_tensor(t, name, dtypes):
     return t
 
 
+def _out_tensor(t, name, dtype, shape, device):
+    """Checks a caller-supplied output (or extra input) tensor against exactly
+    what the C call will write through its pointer: a torch tensor on
+    `device`, of `dtype`, contiguous, of `shape`.  Raises TypeError or
+    ValueError; the kernels would otherwise write past a smaller
+    allocation."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _same_device(t, name, device):
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} must be on {device} (the device of the first operand), got {t.device}")
+    return t
+
+
 def contract() -> dict:
     c = _Contract()
     load_library().dr_contract(ctypes.byref(c))
@@ -174,9 +199,18 @@ def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, 
     M, K = x.shape
     E = W.shape[1]
     dev = x.device
+    _same_device(W, "W", dev)
     ldt = {"f32": DR_F32, "bf16": DR_BF16}[logit_dtype]
+    ldtype = torch.float32 if ldt == DR_F32 else torch.bfloat16
     if out is not None:
         ids_t, w_t, lg_t, mg_t = out
+        _out_tensor(ids_t, "ids", torch.int32, (M, k), dev)
+        if w_t is not None:
+            _out_tensor(w_t, "weights", torch.float32, (M, k), dev)
+        if lg_t is not None:
+            _out_tensor(lg_t, "logits", ldtype, (M, E), dev)
+        if mg_t is not None:
+            _out_tensor(mg_t, "margins", torch.int32, (M, 4), dev)
     else:
         ids_t = torch.empty((M, k), dtype=torch.int32, device=dev)
         w_t = torch.empty((M, k), dtype=torch.float32, device=dev) if weights else None
@@ -216,9 +250,12 @@ def route_logits(x, W, *, logit_dtype: str = "f32", out=None):
         raise ValueError("x must be [M,K] and W [K,E]")
     M, K = x.shape
     E = W.shape[1]
+    _same_device(W, "W", x.device)
     ldt = {"f32": DR_F32, "bf16": DR_BF16}[logit_dtype]
+    ldtype = torch.float32 if ldt == DR_F32 else torch.bfloat16
     if out is None:
-        out = torch.empty((M, E), dtype=torch.float32 if ldt == DR_F32 else torch.bfloat16, device=x.device)
+        out = torch.empty((M, E), dtype=ldtype, device=x.device)
+    _out_tensor(out, "out", ldtype, (M, E), x.device)
     st = L.dr_route_logits(_ptr(x), _ptr(W), M, K, E, ldt, _ptr(out), _stream(x.device))
     _check(st, "dr_route_logits")
     return out
@@ -237,6 +274,11 @@ def route_select(logits, k: int, *, renormalize: bool = False, weights: bool = T
     dev = logits.device
     if out is not None:
         ids_t, w_t, mg_t = out
+        _out_tensor(ids_t, "ids", torch.int32, (M, k), dev)
+        if w_t is not None:
+            _out_tensor(w_t, "weights", torch.float32, (M, k), dev)
+        if mg_t is not None:
+            _out_tensor(mg_t, "margins", torch.int32, (M, 4), dev)
     else:
         ids_t = torch.empty((M, k), dtype=torch.int32, device=dev)
         w_t = torch.empty((M, k), dtype=torch.float32, device=dev) if weights else None
@@ -253,9 +295,12 @@ def gate_dot(x, w, *, dot: bool = True, gate: bool = True):
     L = load_library()
     _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
     _dev_tensor(w, "w", (torch.float32, torch.bfloat16))
+    if x.dim() != 2:
+        raise ValueError("x must be [M,K]")
     M, K = x.shape
     if w.shape != (K,):
         raise ValueError("w must be [K]")
+    _same_device(w, "w", x.device)
     d = torch.empty((M,), dtype=torch.float32, device=x.device) if dot else None
     g = torch.empty((M,), dtype=torch.float32, device=x.device) if gate else None
     st = L.dr_gate_dot(_ptr(x), DR_F32 if x.dtype == torch.float32 else DR_BF16, _ptr(w),
@@ -274,6 +319,9 @@ def moe_permute(ids, E: int, out=None):
     dev = ids.device
     if out is not None:
         offsets, rows, pos = out
+        _out_tensor(offsets, "offsets", torch.int32, (E + 1,), dev)
+        _out_tensor(rows, "rows", torch.int32, (M * k,), dev)
+        _out_tensor(pos, "pos", torch.int32, (M, k), dev)
     else:
         offsets = torch.empty((E + 1,), dtype=torch.int32, device=dev)
         rows = torch.empty((M * k,), dtype=torch.int32, device=dev)
@@ -289,9 +337,7 @@ def widen_bf16(x, out=None):
     _dev_tensor(x, "x", (torch.bfloat16,))
     if out is None:
         out = torch.empty(x.shape, dtype=torch.float32, device=x.device)
-    _dev_tensor(out, "out", (torch.float32,))
-    if out.shape != x.shape:
-        raise ValueError("out must have x's shape")
+    _out_tensor(out, "out", torch.float32, x.shape, x.device)
     _check(L.dr_widen_bf16(_ptr(x), x.numel(), _ptr(out), _stream(x.device)), "dr_widen_bf16")
     return out
 
@@ -301,9 +347,13 @@ def moe_gather(x, rows, out=None):
     L = load_library()
     _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
     _dev_tensor(rows, "rows", (torch.int32,))
+    if x.dim() != 2 or rows.dim() != 1:
+        raise ValueError("x must be [M,D] and rows [P]")
+    _same_device(rows, "rows", x.device)
     M, D = x.shape
     P = rows.numel()
     xp = out if out is not None else torch.empty((P, D), dtype=x.dtype, device=x.device)
+    _out_tensor(xp, "out", x.dtype, (P, D), x.device)
     st = L.dr_moe_gather(_ptr(x), DR_F32 if x.dtype == torch.float32 else DR_BF16, M, D, _ptr(rows), P,
                          _ptr(xp), _stream(x.device))
     _check(st, "dr_moe_gather")
@@ -318,14 +368,24 @@ def moe_combine(y, weights, ids, pos, shared=None, gate=None, out=None):
     _dev_tensor(weights, "weights", (torch.float32,))
     _dev_tensor(ids, "ids", (torch.int32,))
     _dev_tensor(pos, "pos", (torch.int32,))
+    if y.dim() != 2 or ids.dim() != 2:
+        raise ValueError("y must be [P,D] and ids [M,k]")
     P, D = y.shape
     M, k = ids.shape
+    dev = y.device
+    _out_tensor(weights, "weights", torch.float32, (M, k), dev)
+    _out_tensor(ids, "ids", torch.int32, (M, k), dev)
+    _out_tensor(pos, "pos", torch.int32, (M, k), dev)
     sdt = DR_F32
     if shared is not None:
         _dev_tensor(shared, "shared", (torch.float32, torch.bfloat16))
-        _dev_tensor(gate, "gate", (torch.float32,))
+        _out_tensor(shared, "shared", shared.dtype, (M, D), dev)
+        if gate is None:
+            raise ValueError("gate is required with shared")
+        _out_tensor(gate, "gate", torch.float32, (M,), dev)
         sdt = DR_F32 if shared.dtype == torch.float32 else DR_BF16
-    o = out if out is not None else torch.empty((M, D), dtype=torch.float32, device=y.device)
+    o = out if out is not None else torch.empty((M, D), dtype=torch.float32, device=dev)
+    _out_tensor(o, "out", torch.float32, (M, D), dev)
     st = L.dr_moe_combine(_ptr(y), DR_F32 if y.dtype == torch.float32 else DR_BF16, P, _ptr(weights), _ptr(ids),
                           _ptr(pos), _ptr(shared), sdt, _ptr(gate) if shared is not None else None, M, k, D,
                           _ptr(o), _stream(y.device))
@@ -340,11 +400,14 @@ def route_bf16_gemm(x, W, k: int, *, renormalize: bool = False, weights: bool = 
     L = load_library()
     _dev_tensor(x, "x", (torch.bfloat16,))
     _dev_tensor(W, "W", (torch.bfloat16,))
+    if x.dim() != 2 or W.dim() != 2:
+        raise ValueError("x must be [M,K] and W [K,E]")
     M, K = x.shape
     K2, E = W.shape
     if K != K2:
         raise ValueError("inner sizes differ")
     dev = x.device
+    _same_device(W, "W", dev)
     ids_t = torch.empty((M, k), dtype=torch.int32, device=dev)
     w_t = torch.empty((M, k), dtype=torch.float32, device=dev) if weights else None
     lg_t = torch.empty((M, E), dtype=torch.bfloat16, device=dev)
@@ -362,18 +425,24 @@ def grouped_gemm_bf16(x, W, offsets, rows=None, out=None):
     _dev_tensor(x, "x", (torch.bfloat16,))
     _dev_tensor(W, "W", (torch.bfloat16,))
     _dev_tensor(offsets, "offsets", (torch.int32,))
+    if x.dim() != 2 or W.dim() != 3:
+        raise ValueError("x must be [Mx,K] and W [E,K,N]")
     Mx, K = x.shape
     E, K2, N = W.shape
     if K != K2:
         raise ValueError("inner sizes differ")
-    if offsets.numel() != E + 1:
-        raise ValueError("offsets must have E+1 entries")
+    _same_device(W, "W", x.device)
+    _out_tensor(offsets, "offsets", torch.int32, (E + 1,), x.device)
     if rows is not None:
         _dev_tensor(rows, "rows", (torch.int32,))
+        if rows.dim() != 1:
+            raise ValueError("rows must be [P]")
+        _same_device(rows, "rows", x.device)
         P = rows.numel()
     else:
         P = Mx
     o = out if out is not None else torch.empty((P, N), dtype=torch.float32, device=x.device)
+    _out_tensor(o, "out", torch.float32, (P, N), x.device)
     st = L.dr_grouped_gemm_bf16(_ptr(x), Mx, _ptr(rows), _ptr(W), _ptr(offsets), E, P, K, N, _ptr(o),
                                 _stream(x.device))
     _check(st, "dr_grouped_gemm_bf16")
@@ -385,12 +454,16 @@ def gemm_bf16(x, W, out=None):
     L = load_library()
     _dev_tensor(x, "x", (torch.bfloat16,))
     _dev_tensor(W, "W", (torch.bfloat16,))
+    if x.dim() != 2 or W.dim() != 2:
+        raise ValueError("x must be [M,K] and W [K,N]")
     M, K = x.shape
     K2, N = W.shape
     if K != K2:
         raise ValueError("inner sizes differ")
+    _same_device(W, "W", x.device)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    _out_tensor(out, "out", torch.float32, (M, N), x.device)
     st = L.dr_gemm_bf16(_ptr(x), _ptr(W), _ptr(out), M, K, N, _stream(x.device))
     _check(st, "dr_gemm_bf16")
     return out

@@ -74,6 +74,7 @@ def test_route_rejects(L, kw, status):
 
 def test_route_variant_rejects(L):
     assert _route(L, variant=9) == INVALID
+    assert _route(L, variant=7) == INVALID
     assert _route(L, E=1024, k=8, variant=2) == UNSUPPORTED  # the tiled family stops at E=512
     # the split family writes the logits and reads them back: it needs that
     # output, fp32 x in whole 16-byte pieces and E in {256, 512}
@@ -87,6 +88,11 @@ def test_route_variant_rejects(L):
     assert _route(L, lg=0, variant=4) == UNSUPPORTED
     assert _route(L, xd=1, K=2044, variant=4) == UNSUPPORTED  # bf16 x: K % 8 == 0
     assert _route(L, E=1024, k=8, variant=4) == UNSUPPORTED
+    # the one-launch family: E = 256 only; the logits output is optional
+    assert _route(L, E=512, k=8, variant=6) == UNSUPPORTED
+    assert _route(L, K=2046, variant=6) == UNSUPPORTED
+    assert _route(L, xd=1, K=8192, variant=6) == UNSUPPORTED
+    assert _route(L, M=0, lg=0, variant=6) == OK
 
 
 def test_halves_reject(L):
@@ -258,3 +264,36 @@ def test_widen_bf16_validation(L):
     assert dr.auto_variant(8192, 2044, 256, "bf16") != "split"
     assert not any(dr.widen_bf16_used(M, 2048, 256) for M in (1, 64, 65, 2048, 2049, 8192))
     assert dr.widen_bf16_used(8192, 8192, 256) and not dr.widen_bf16_used(1024, 8192, 256)
+
+
+def test_binding_validates_out_tensors():
+    """The binding checks every caller-supplied output (and extra input)
+    tensor against what the C call writes through its pointer -- dtype,
+    shape, device, contiguity -- before any call; a mismatch raises instead of
+    letting a kernel write past a smaller allocation.  The checks run on
+    host tensors here (no GPU needed); the entry points themselves refuse
+    host tensors first."""
+    import torch
+
+    cpu = torch.device("cpu")
+    ok = torch.empty((4, 8), dtype=torch.int32)
+    assert dr._out_tensor(ok, "ids", torch.int32, (4, 8), cpu) is ok
+    bad = [
+        (torch.empty((4, 7), dtype=torch.int32), ValueError),           # too few columns
+        (torch.empty((3, 8), dtype=torch.int32), ValueError),           # too few rows
+        (torch.empty((4, 8), dtype=torch.int64), TypeError),            # wrong dtype
+        (torch.empty((8, 4), dtype=torch.int32).t(), ValueError),       # not contiguous
+        (torch.empty((4, 8), dtype=torch.int32, device="meta"), ValueError),  # another device
+        (ok.numpy(), TypeError),                                        # not a tensor
+    ]
+    for t, exc in bad:
+        with pytest.raises(exc):
+            dr._out_tensor(t, "ids", torch.int32, (4, 8), cpu)
+    with pytest.raises(ValueError):
+        dr._same_device(torch.empty(3, device="meta"), "W", cpu)
+    # every entry point refuses host operands before touching its outputs
+    x = torch.zeros((4, 64))
+    with pytest.raises(TypeError):
+        dr.route(x, torch.zeros((64, 256)), 8, out=(ok, None, None, None))
+    with pytest.raises(TypeError):
+        dr.gemm_bf16(x.to(torch.bfloat16), torch.zeros((64, 128), dtype=torch.bfloat16))
