@@ -301,6 +301,71 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
     return suite, checks
 
 
+PROFILE_WORKLOADS = ("route", "route_fused", "route_split", "dense_M4096", "dense_M65", "grouped")
+
+
+def profile_workload(name: str, steps: int, warmup: int, copy_calibration: bool = False):
+    """Runs one workload alone, `warmup` untimed then `steps` timed calls on
+    resident inputs, and prints its average time per call: the program that
+    rocprofv3 kernel-trace and counter runs wrap, so that their dispatches are
+    this workload's only.  route: dr_route at the headline workload (the
+    family AUTO picks); route_fused / route_split: that call with the family
+    forced; dense_M4096 / dense_M65: dr_gemm_bf16 at K = N = 4096; grouped:
+    the grouped expert GEMM at 65536 rows x 2048 x 1024, E = 256."""
+    import numpy as np
+    import torch
+
+    import deterministic_gemm_amd as dr
+    import workloads as wl
+
+    dr.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    if copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
+    if name.startswith("route"):
+        xd = torch.from_numpy(wl.sweep_x(M, K)).to(dev)
+        Wd = torch.from_numpy(wl.router_weights(K, E)).to(dev)
+        variant = {"route": "auto", "route_fused": "fused", "route_split": "split"}[name]
+        out = (torch.empty((M, TOPK), dtype=torch.int32, device=dev),
+               torch.empty((M, TOPK), dtype=torch.float32, device=dev),
+               torch.empty((M, E), dtype=torch.float32, device=dev),
+               torch.empty((M, 4), dtype=torch.int32, device=dev))
+        fn = lambda: dr.route(xd, Wd, TOPK, out=out, variant=variant)  # noqa: E731
+        work = {"M": M, "K": K, "E": E, "k": TOPK, "flop": 2.0 * M * K * E}
+    elif name.startswith("dense"):
+        m = {"dense_M4096": 4096, "dense_M65": 65}[name]
+        xb = torch.from_numpy(wl.dense_x_bits(m).view(np.int16)).view(torch.bfloat16).to(dev)
+        Wb = torch.from_numpy(wl.dense_w_bits().view(np.int16)).view(torch.bfloat16).to(dev)
+        ob = torch.empty((m, wl.DENSE_N), dtype=torch.float32, device=dev)
+        fn = lambda: dr.gemm_bf16(xb, Wb, out=ob)  # noqa: E731
+        work = {"M": m, "K": wl.DENSE_K, "N": wl.DENSE_N, "flop": 2.0 * m * wl.DENSE_K * wl.DENSE_N}
+    elif name == "grouped":
+        Ng = 1024
+        xd = torch.from_numpy(wl.sweep_x(M, K)).to(dev)
+        Wd = torch.from_numpy(wl.router_weights(K, E)).to(dev)
+        ids_r = dr.route(xd, Wd, TOPK, weights=False, logits=False, margins=False)[0]
+        off_r, rows_r, _ = dr.moe_permute(ids_r, E)
+        xb_r = xd.to(torch.bfloat16)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(wl.SEED_MOE + 4)
+        Wg = (torch.randn((E, K, Ng), device=dev, generator=gen) * float(wl.W_STD)).to(torch.bfloat16)
+        og = torch.empty((M * TOPK, Ng), dtype=torch.float32, device=dev)
+        fn = lambda: dr.grouped_gemm_bf16(xb_r, Wg, off_r, rows_r, out=og)  # noqa: E731
+        work = {"P": M * TOPK, "K": K, "N": Ng, "E": E, "flop": 2.0 * M * TOPK * K * Ng}
+    else:
+        raise SystemExit(f"unknown workload {name}; one of {PROFILE_WORKLOADS}")
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ms = _time(fn, stream, torch, steps=steps, warmup=0)
+    print(json.dumps({"profile": name, "steps": steps, "warmup": warmup, "us_per_call": round(ms * 1e3, 2),
+                      **work}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,7 +378,12 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one 256 MiB device-to-device copy, the known-size reference for "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--profile", choices=PROFILE_WORKLOADS,
+                    help="run only this workload (--warmup untimed, then --steps timed calls) for rocprofv3")
     args = ap.parse_args()
+    if args.profile:
+        profile_workload(args.profile, args.steps, args.warmup, args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (rows are independent, "
               "so data-parallel sharding exchanges nothing and per-GPU throughput is the figure)",

@@ -62,7 +62,8 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   if (logit_dtype != DR_F32 && logit_dtype != DR_BF16) return fail(DR_ERR_INVALID, "bad logit_dtype");
   if (flags & ~DR_ROUTE_RENORMALIZE) return fail(DR_ERR_INVALID, "unknown flags 0x%x", flags);
   if (variant != DR_VARIANT_AUTO && variant != DR_VARIANT_ROWWISE && variant != DR_VARIANT_TILED &&
-      variant != DR_VARIANT_SPLIT && variant != DR_VARIANT_NARROW && variant != DR_VARIANT_TINY)
+      variant != DR_VARIANT_SPLIT && variant != DR_VARIANT_NARROW && variant != DR_VARIANT_TINY &&
+      variant != DR_VARIANT_FUSED)
     return fail(DR_ERR_INVALID, "bad variant");
   if (M > 0 && (!x || !W || !ids)) return fail(DR_ERR_INVALID, "x, W and ids are required");
   if (!aligned16(x) || !aligned16(W) || !aligned16(ids) || !aligned16(weights) || !aligned16(logits) ||
@@ -79,6 +80,9 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
     return fail(DR_ERR_UNSUPPORTED,
                 "split variant needs E in {256, 512, 1024}, the logits output, and fp32 x with K %% 4 == 0 or bf16 x "
                 "with K %% 8 == 0 and K <= 4096");
+  if (variant == DR_VARIANT_FUSED && !drk::fused_supports(E, K, x_dtype == DR_F32))
+    return fail(DR_ERR_UNSUPPORTED,
+                "fused variant needs E = 256 and fp32 x with K %% 4 == 0 or bf16 x with K %% 8 == 0 and K <= 4096");
   if (variant == DR_VARIANT_NARROW && !drk::narrow_supports(E, K, x_dtype == DR_F32, logits != nullptr))
     return fail(DR_ERR_UNSUPPORTED,
                 "narrow variant needs E <= 512, the logits output, and K %% 4 == 0 (fp32 x) or K %% 8 == 0 (bf16 x)");
@@ -104,6 +108,7 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
   L.margins = margins;
   L.stream = static_cast<hipStream_t>(stream);
   const hipError_t e = variant == DR_VARIANT_SPLIT    ? drk::launch_route_split(L)
+                       : variant == DR_VARIANT_FUSED  ? drk::launch_route_fused(L)
                        : variant == DR_VARIANT_NARROW ? drk::launch_route_narrow(L)
                        : variant == DR_VARIANT_TINY   ? drk::launch_route_tiny(L)
                        : variant == DR_VARIANT_TILED  ? drk::launch_route_tiled(L)

@@ -45,6 +45,8 @@ hipError_t launch_route_rowwise(const RouteLaunch &L);
 hipError_t launch_route_tiled(const RouteLaunch &L);
 bool tiled_supports(int64_t E, int64_t K);
 hipError_t launch_route_split(const RouteLaunch &L);
+hipError_t launch_route_fused(const RouteLaunch &L);
+bool fused_supports(int64_t E, int64_t K, bool x_f32);
 bool split_supports(int64_t E, int64_t K, bool x_f32, bool has_logits);
 hipError_t launch_route_tiny(const RouteLaunch &L);
 hipError_t launch_route_tiny_logits(const RouteLaunch &L);

@@ -58,16 +58,22 @@ struct SplitCfg {
   static constexpr int WI = 4 * KC * ET / 256;  // W transfers (64 lanes x 16 B) per chunk
   static constexpr int WIW = WI / NWP;          // ... per wavefront of the part
   static constexpr int XU = 4 * TT * HU;        // x 16-byte units per chunk
-  static constexpr int XI = XU / 64;            // x transfers per chunk
-  static constexpr int XIW = XI / NWP;          // ... per wavefront of the part
-  static constexpr int PER = WIW + XIW;         // transfers per chunk per wavefront
+  static constexpr int XI = XU / 64;            // x transfers per chunk ...
+  static constexpr int XW = XI < NWP ? XI : NWP;  // ... issued by the part's first XW wavefronts
+  static constexpr int XIW = XI / XW;           // ... XIW each
+  static constexpr int PER_X = WIW + XIW;       // transfers per chunk, x-issuing wavefronts
+  static constexpr int PER_W = WIW;             // transfers per chunk, the others
   static constexpr int CPG = 256 / KC;          // chunks per group of four K-blocks
+  // One expert tile covering all E: a workgroup holds whole tokens and runs
+  // the selection itself (one launch)
+  static constexpr bool FUSED = ET == E;
   static_assert(NWE * EW == ET, "whole wavefront expert tiles");
   static_assert(WIW * NWP == WI && WIW >= 1, "W transfers split evenly");
-  static_assert(XI * 64 == XU && XIW * NWP == XI && XIW >= 1, "x transfers split evenly");
+  static_assert(XI * 64 == XU && XIW * XW == XI && XIW >= 1, "x transfers split evenly");
   static_assert(KP == 1 || KP == 2, "parts");
+  static_assert(!FUSED || (KP == 1 && TT % (4 * NW) == 0 && ET + 4 >= 68), "fused: whole tokens per wavefront row");
   static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
-  static_assert(PER * (S - 1) <= 63, "vmcnt range");
+  static_assert(PER_X * (S - 1) <= 63, "vmcnt range");
   static_assert(KC % XV == 0 && 256 % KC == 0 && (S == 3 || S == 4), "chunking");
   static_assert(TT * LGP + (KP - 1) * NWP * AT * BT * 4 * 64 <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");
@@ -113,6 +119,7 @@ __device__ __forceinline__ void split_issue(const void *__restrict__ xv, const f
   constexpr int XS = C::XB ? 2 : 4;
   const char *xb = static_cast<const char *>(xv);
   const char *xrow0 = xb + m0 * K * XS;
+  if (wave >= C::XW) return;
 #pragma unroll
   for (int i = 0; i < C::XIW; ++i) {
     const int u = (wave * C::XIW + i) * 64 + lane;  // x unit within the chunk
@@ -164,7 +171,10 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
         }
   }
   compiler_fence();
-  wait_vmcnt<C::PER * (S - 2)>();
+  if (wp < C::XW)
+    wait_vmcnt<C::PER_X * (S - 2)>();
+  else
+    wait_vmcnt<C::PER_W * (S - 2)>();
   __builtin_amdgcn_s_barrier();
   compiler_fence();
   if constexpr (!C::LATE) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
@@ -235,7 +245,7 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
 template <class C, int MAXL>
 __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *__restrict__ xf,
                                                                    const float *__restrict__ W, int64_t M, int K,
-                                                                   void *logits, int logit_bf16) {
+                                                                   EpilogueArgs ea) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, STG = C::STG;
   __shared__ __attribute__((aligned(16))) float smem[S * STG];
 
@@ -317,8 +327,14 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *_
         }
   }
   __syncthreads();
-  if (!logit_bf16) {
-    float *out = static_cast<float *>(logits);
+  if constexpr (C::FUSED) {
+    // whole tokens: each row of 16 lanes selects one token from its LDS row
+    // (and stores its logits when asked)
+    for (int i = 4 * wave; i < TT; i += 4 * C::NW) route_tokens_row16<C::E>(lg + i * C::LGP, C::LGP, m0 + i, M, ea);
+    return;
+  }
+  if (!ea.logit_bf16) {
+    float *out = static_cast<float *>(ea.logits);
     for (int u = t; u < TT * ET / 4; u += C::NT) {
       const int tok = u / (ET / 4), c4 = u % (ET / 4);
       const int64_t m = m0 + tok;
@@ -327,7 +343,7 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *_
             *reinterpret_cast<const float4 *>(lg + tok * C::LGP + 4 * c4);
     }
   } else {
-    uint16_t *out = static_cast<uint16_t *>(logits);
+    uint16_t *out = static_cast<uint16_t *>(ea.logits);
     for (int u = t; u < TT * ET / 8; u += C::NT) {
       const int tok = u / (ET / 8), c8 = u % (ET / 8);
       const int64_t m = m0 + tok;
@@ -427,9 +443,10 @@ template <class C, int MAXL>
 static hipError_t launch_logits_cm(const RouteLaunch &L) {
   const int64_t ntt = (L.M + C::TT - 1) / C::TT;
   const int64_t nblk = (ntt + 7) / 8 * 8 * C::NET;
+  EpilogueArgs ea{L.k, L.logit_bf16, L.flags, L.ids, L.weights, L.logits, L.margins};
   hipLaunchKernelGGL((route_split_logits_kernel<C, MAXL>), dim3(static_cast<uint32_t>(nblk)), dim3(C::NT), 0,
                      L.stream, C::XB ? static_cast<const void *>(L.xb) : static_cast<const void *>(L.xf), L.W, L.M,
-                     static_cast<int>(L.K), L.logits, L.logit_bf16);
+                     static_cast<int>(L.K), ea);
   return hipGetLastError();
 }
 
@@ -526,6 +543,28 @@ hipError_t launch_route_select(const RouteLaunch &L) {
     case 1024: return launch_select_e<1024>(L);
     default: return hipErrorInvalidValue;
   }
+}
+
+#ifdef DR_SWEEP
+#include <cstdlib>
+#endif
+
+bool fused_supports(int64_t E, int64_t K, bool x_f32) {
+  return E == 256 && K >= 1 && K <= (x_f32 ? 16384 : 4096) && (K % (x_f32 ? 4 : 8)) == 0;
+}
+
+hipError_t launch_route_fused(const RouteLaunch &L) {
+  if (L.E != 256) return hipErrorInvalidValue;
+#ifdef DR_SWEEP
+  const char *cv = getenv("DR_FUSED_CFG");
+  const int cfg = cv ? atoi(cv) : 0;
+  if (L.xf) {
+    if (cfg == 1) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, false>>(L);
+    if (cfg == 2) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 3, 1, true>>(L);
+  }
+#endif
+  if (!L.xf) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true, true>>(L);
+  return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true>>(L);
 }
 
 hipError_t launch_route_split(const RouteLaunch &L) {

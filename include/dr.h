@@ -27,7 +27,11 @@
  *    after returning), row-major and contiguous, 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *    asynchronous on that stream and never synchronise the device.
- *  - The library allocates no device memory and uses no atomics.
+ *  - The library allocates no device memory.  No value is accumulated by an
+ *    atomic anywhere: the routing, GEMM and combine kernels use no atomics,
+ *    and dr_moe_permute counts integers (expert histograms, presence bits)
+ *    with LDS atomic add / or, whose results do not depend on the order in
+ *    which the lanes arrive.
  *  - Arguments are validated before any launch; on a non-OK status no kernel
  *    was launched and outputs are untouched.  DR_ERR_DEVICE means a launch
  *    failed; dr_last_error() then holds the HIP error text.
@@ -75,11 +79,16 @@ typedef DR_ENUM(dr_variant) {
                              the K groups along the canonical tree, writing the logits, then
                              the selection kernel; needs E <= 512, the logits output, and
                              K % 4 == 0 (fp32 x) or K % 8 == 0 (bf16 x, staged as it is) */
-  DR_VARIANT_TINY = 5     /* a few tokens: each lane runs (expert, K-block) chains on the vector
+  DR_VARIANT_TINY = 5,    /* a few tokens: each lane runs (expert, K-block) chains on the vector
                              ALUs with the workgroup's W slice in LDS, the blocks combine across
                              lanes, then the selection kernel; needs K % 4 == 0 (fp32 x)
                              or K % 8 == 0 (bf16 x, widened when read), K <= 4096
                              and the logits output */
+  DR_VARIANT_FUSED = 6    /* one launch: 32-token x all-E tiles on matrix cores, the split
+                             family's pipeline, then the selection inside the same workgroup;
+                             the logits output is optional; needs E = 256 and fp32 x with
+                             K % 4 == 0 or bf16 x (staged as it is) with K % 8 == 0 and
+                             K <= 4096 */
 } dr_variant;
 
 /* Divide the k selected weights by their sum (left to right in rank order). */
@@ -156,8 +165,11 @@ dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int6
                            float *weights, void *logits, dr_margin *margins, uint32_t flags,
                            dr_variant variant, void *stream);
 
-/* The family AUTO picks: a pure function of the call's shape (M, K, E), the
- * x dtype and whether the logits output is requested. */
+/* The family AUTO picks: a function of the call's shape (M, K, E), the x
+ * dtype, whether the logits output is requested, and the current device's
+ * compute-unit count (which sets how many workgroups run at once, so where
+ * one family stops filling the chip).  It never depends on the data, and
+ * every family it can pick computes the same bits. */
 dr_variant dr_route_auto_variant(int64_t M, int64_t K, int64_t E, dr_dtype x_dtype, int with_logits);
 
 /*

@@ -38,7 +38,7 @@ def mscan_ref(router_w):
     return oracle_route(fx, router_w, TOPK)
 
 
-@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled", "split", "narrow", "tiny"])
+@pytest.mark.parametrize("variant", ["auto", "rowwise", "tiled", "split", "narrow", "tiny", "fused"])
 def test_mscan_fixed_rows_bit_identical(dr, router_w, mscan_ref, variant):
     """Every M in 19..80, the fixed request placed first and last, ascending
     then descending: the fixed rows equal the oracle's solo run bit for bit."""
@@ -97,11 +97,11 @@ def test_sweep_every_m_matches_oracle(dr, router_w, sweep):
         assert_route_equal(got, tuple(r[:M] for r in ref), what=f"M={M}")
 
 
-@pytest.mark.parametrize("variant", ["rowwise", "tiled", "split", "narrow", "tiny"])
+@pytest.mark.parametrize("variant", ["rowwise", "tiled", "split", "narrow", "tiny", "fused"])
 def test_sweep_forced_variants(dr, router_w, sweep, variant):
     x, ref = sweep
     Wd = dev(router_w)
-    for M in (1, 65, 1024):
+    for M in (1, 65, 1024) + ((8192,) if variant in ("split", "fused") else ()):
         note(f"sweep forced {variant} M={M}")
         got = gpu_route_np(dr, dev(x[:M]), Wd, TOPK, variant=variant)
         assert_route_equal(got, tuple(r[:M] for r in ref), what=f"{variant} M={M}")
@@ -133,7 +133,7 @@ def test_bf16_input_storage_is_bit_identical(dr, router_w, sweep):
     Wd = dev(router_w)
     M = 300
     xb = dev(x[:M]).to(torch.bfloat16)  # exact: x is bf16-valued
-    for variant in ("rowwise", "tiled"):
+    for variant in ("rowwise", "tiled", "fused"):
         note(f"bf16 storage {variant}")
         got = gpu_route_np(dr, xb, Wd, TOPK, variant=variant)
         assert_route_equal(got, tuple(r[:M] for r in ref), what=f"bf16 x {variant}")
@@ -176,7 +176,7 @@ def test_ragged_k_split(dr, Kx):
     W = (rng.standard_normal((Kx, 256)) * 0.05).astype(np.float32)
     x = rng.standard_normal((70, Kx)).astype(np.float32)
     ref = oracle_route(x, W, 6)
-    for variant in ("split", "narrow", "tiled") + (("tiny",) if Kx <= 4096 else ()):
+    for variant in ("split", "narrow", "tiled", "fused") + (("tiny",) if Kx <= 4096 else ()):
         note(f"ragged K={Kx} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), 6, variant=variant)
         assert_route_equal(got, ref, what=f"K={Kx} {variant}")
@@ -189,10 +189,12 @@ def test_every_supported_e(dr, Ex, kx):
     W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
     x = rng.standard_normal((77, Kx)).astype(np.float32)
     ref = oracle_route(x, W, kx)
-    for variant in ("auto", "rowwise", "tiled", "split", "narrow", "tiny"):
+    for variant in ("auto", "rowwise", "tiled", "split", "narrow", "tiny", "fused"):
         if variant in ("tiled", "narrow") and Ex == 1024:
             continue
         if variant == "split" and Ex not in (256, 512, 1024):
+            continue
+        if variant == "fused" and Ex != 256:
             continue
         note(f"E={Ex} k={kx} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
@@ -206,7 +208,7 @@ def test_modes(dr, router_w, sweep, mode):
     kw = {"logit_dtype": "bf16"} if mode == "bf16_logits" else {"renormalize": True}
     ref = oracle_route(x[:M], router_w, TOPK, logits_bf16=(mode == "bf16_logits"),
                        renormalize=(mode == "renormalize"))
-    for variant in ("rowwise", "tiled", "split", "narrow", "tiny"):
+    for variant in ("rowwise", "tiled", "split", "narrow", "tiny", "fused"):
         note(f"mode {mode} {variant}")
         got = gpu_route_np(dr, dev(x[:M]), dev(router_w), TOPK, variant=variant, **kw)
         assert_route_equal(got, ref, what=f"{mode} {variant}")
@@ -230,7 +232,7 @@ def test_special_values(dr, Ex):
     W[:, 9] = -0.0
     W[:, 10] = W[:, 11]                        # exact ties
     ref = oracle_route(x, W, kx)
-    for variant in ("rowwise", "tiled", "narrow", "tiny") + (("split",) if Ex == 256 else ()):
+    for variant in ("rowwise", "tiled", "narrow", "tiny") + (("split", "fused") if Ex == 256 else ()):
         note(f"special values E={Ex} {variant}")
         got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant)
         assert_route_equal(got, ref, what=f"special {variant}")
@@ -261,16 +263,18 @@ def test_rows_at_any_offset(dr, router_w, sweep):
                                what=f"shift={shift} {variant}")
 
 
-@pytest.mark.parametrize("Kx,M", [(2048, 2100), (4096, 600), (264, 1500)])
+@pytest.mark.parametrize("Kx,M", [(2048, 2100), (4096, 600), (264, 1500), (8192, 300), (16384, 100)])
 def test_split_at_1024_experts(dr, Kx, M):
     """The two-kernel family at E = 1024 (eight 128-expert tiles, or sixteen
-    64-expert tiles in two parts), fp32 and bf16 x, against the oracle."""
+    64-expert tiles in two parts), fp32 and bf16 x, against the oracle.  Above
+    K = 4096 (fp32 x only) the 8-step-chunk configuration runs, with counter
+    stacks of depth 4 (K = 8192) and 5 (K = 16384)."""
     rng = np.random.default_rng(Kx + M)
     W = (rng.standard_normal((Kx, 1024)) * 0.05).astype(np.float32)
     xb = torch.from_numpy(rng.standard_normal((M, Kx)).astype(np.float32)).to(torch.bfloat16)
     x = xb.float().numpy()
     ref = oracle_route(x, W, 8)
-    for xd in (dev(x), xb.cuda()):
+    for xd in ((dev(x), xb.cuda()) if Kx <= 4096 else (dev(x),)):
         note(f"split E=1024 K={Kx} M={M} x {xd.dtype}")
         got = gpu_route_np(dr, xd, dev(W), 8, variant="split")
         assert_route_equal(got, ref, what=f"split E=1024 K={Kx} M={M} {xd.dtype}")
