@@ -37,7 +37,7 @@ MARGIN_DTYPE = np.dtype(
 )
 
 EXPORTED = (
-    "dr_route", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
+    "dr_route", "dr_route_noalloc", "dr_route_variant", "dr_route_auto_variant", "dr_route_logits", "dr_route_select",
     "dr_route_bf16_gemm", "dr_gate_dot", "dr_gemm_bf16", "dr_grouped_gemm_bf16", "dr_moe_permute", "dr_moe_gather", "dr_moe_combine", "dr_widen_bf16", "dr_contract",
     "dr_status_string", "dr_last_error",
 )
@@ -68,6 +68,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P, i64, i32, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32
     L.dr_route.argtypes = [P, ctypes.c_int, P, i64, i64, i64, i32, ctypes.c_int, P, P, P, P, u32, P]
     L.dr_route.restype = ctypes.c_int
+    L.dr_route_noalloc.argtypes = [P, ctypes.c_int, P, i64, i64, i64, i32, ctypes.c_int, P, P, P, P, u32, P]
+    L.dr_route_noalloc.restype = ctypes.c_int
     L.dr_route_variant.argtypes = [P, ctypes.c_int, P, i64, i64, i64, i32, ctypes.c_int, P, P, P, P, u32,
                                    ctypes.c_int, P]
     L.dr_route_variant.restype = ctypes.c_int
@@ -234,6 +236,38 @@ def route(x, W, k: int, *, logit_dtype: str = "f32", renormalize: bool = False, 
                                 _ptr(mg_t), flags, v, _stream(dev))
     _check(st, "dr_route")
     return ids_t, w_t, lg_t, mg_t
+
+
+def route_noalloc(x, W, k: int, out, *, logit_dtype: str = "f32", renormalize: bool = False):
+    """dr_route_noalloc: dr_route that allocates nothing, for callers that
+    cannot (graph capture, serving loops).  `out` = (ids [M,k] int32,
+    weights [M,k] float32 or None, logits [M,E] or None, margins [M,4] int32
+    or None), all preallocated; nothing is allocated here either.  With
+    logits None the two-launch families keep their logits in the library's
+    static 16 MiB device buffer (M*E*4 bytes at most).  Returns out."""
+    L = load_library()
+    _dev_tensor(x, "x", (torch.float32, torch.bfloat16))
+    _dev_tensor(W, "W", (torch.float32,))
+    if x.dim() != 2 or W.dim() != 2 or x.shape[1] != W.shape[0]:
+        raise ValueError("x must be [M,K] and W [K,E]")
+    M, K = x.shape
+    E = W.shape[1]
+    dev = x.device
+    _same_device(W, "W", dev)
+    ldt = {"f32": DR_F32, "bf16": DR_BF16}[logit_dtype]
+    ids_t, w_t, lg_t, mg_t = out
+    _out_tensor(ids_t, "ids", torch.int32, (M, k), dev)
+    if w_t is not None:
+        _out_tensor(w_t, "weights", torch.float32, (M, k), dev)
+    if lg_t is not None:
+        _out_tensor(lg_t, "logits", torch.float32 if ldt == DR_F32 else torch.bfloat16, (M, E), dev)
+    if mg_t is not None:
+        _out_tensor(mg_t, "margins", torch.int32, (M, 4), dev)
+    xd = DR_F32 if x.dtype == torch.float32 else DR_BF16
+    st = L.dr_route_noalloc(_ptr(x), xd, _ptr(W), M, K, E, k, ldt, _ptr(ids_t), _ptr(w_t), _ptr(lg_t), _ptr(mg_t),
+                            DR_ROUTE_RENORMALIZE if renormalize else 0, _stream(dev))
+    _check(st, "dr_route_noalloc")
+    return out
 
 
 def route_variant(x, W, k: int, variant: str, **kw):
@@ -475,6 +509,7 @@ def margins_to_numpy(mg: torch.Tensor) -> np.ndarray:
 
 
 dr_route = route
+dr_route_noalloc = route_noalloc
 dr_route_variant = route_variant
 dr_route_logits = route_logits
 dr_route_select = route_select

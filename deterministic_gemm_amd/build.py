@@ -17,7 +17,7 @@ OBJDIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["dr_api.cpp", "route_rowwise.hip", "route_tiled.hip", "route_split.hip", "route_narrow.hip", "route_tiny.hip",
-           "gate_dot.hip", "gemm_bf16.hip", "moe.hip", "widen.hip"]
+           "gate_dot.hip", "gemm_bf16.hip", "moe.hip", "widen.hip", "route_noalloc.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

@@ -49,10 +49,12 @@ constexpr int64_t kTiledMinM = 48;
 // above it they use 64 x 64 or 64 x 128 tiles.  Without the logits output the
 // fused kernels run.
 
+// noalloc: dr_route_noalloc, which keeps the logits of a two-launch family in
+// the library's static device buffer when the caller passes no logits buffer.
 dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
                      int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
                      void *logits, dr_margin *margins, uint32_t flags, dr_variant variant,
-                     void *stream) {
+                     void *stream, bool noalloc = false) {
   g_last_error[0] = '\0';
   if (M < 0 || M > kMaxM) return fail(DR_ERR_INVALID, "M=%lld out of range", (long long)M);
   if (K < 1) return fail(DR_ERR_INVALID, "K=%lld must be >= 1", (long long)K);
@@ -73,6 +75,25 @@ dr_status route_impl(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
     return fail(DR_ERR_UNSUPPORTED, "E=%lld: supported E are 64, 128, 256, 512, 1024", (long long)E);
   if (K > kMaxK) return fail(DR_ERR_UNSUPPORTED, "K=%lld above %lld", (long long)K, (long long)kMaxK);
   if (k > kMaxTopK) return fail(DR_ERR_UNSUPPORTED, "k=%d above %d", k, kMaxTopK);
+  if (noalloc && !logits) {
+    // the family AUTO picks given a logits buffer; the two-launch ones keep
+    // the logits between their launches in the static buffer
+    const dr_variant v = dr_route_auto_variant(M, K, E, x_dtype, 1);
+    if (v == DR_VARIANT_TINY || v == DR_VARIANT_NARROW || v == DR_VARIANT_SPLIT) {
+      const int64_t bytes = M * E * (logit_dtype == DR_BF16 ? 2 : 4);
+      if (bytes > drk::kNoallocScratchBytes)
+        return fail(DR_ERR_UNSUPPORTED,
+                    "dr_route_noalloc: the logits of M=%lld x E=%lld (%lld bytes) exceed its %lld-byte device "
+                    "buffer; pass a logits buffer or split the batch",
+                    (long long)M, (long long)E, (long long)bytes, (long long)drk::kNoallocScratchBytes);
+      if (M == 0) return DR_OK;
+      void *buf = nullptr;
+      const dr_status s = device_status(drk::noalloc_scratch(&buf), "dr_route_noalloc: device buffer lookup");
+      if (s != DR_OK) return s;
+      logits = buf;
+      variant = v;
+    }
+  }
   if (variant == DR_VARIANT_AUTO) variant = dr_route_auto_variant(M, K, E, x_dtype, logits != nullptr);
   if (variant == DR_VARIANT_TILED && !drk::tiled_supports(E, K))
     return fail(DR_ERR_UNSUPPORTED, "tiled variant does not support E=%lld", (long long)E);
@@ -157,6 +178,13 @@ dr_status dr_route(const void *x, dr_dtype x_dtype, const float *W, int64_t M, i
                    void *logits, dr_margin *margins, uint32_t flags, void *stream) {
   return route_impl(x, x_dtype, W, M, K, E, k, logit_dtype, ids, weights, logits, margins, flags,
                     DR_VARIANT_AUTO, stream);
+}
+
+dr_status dr_route_noalloc(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
+                           int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
+                           void *logits, dr_margin *margins, uint32_t flags, void *stream) {
+  return route_impl(x, x_dtype, W, M, K, E, k, logit_dtype, ids, weights, logits, margins, flags,
+                    DR_VARIANT_AUTO, stream, true);
 }
 
 dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int64_t M,

@@ -37,6 +37,12 @@ hipError_t launch_moe_combine(const void *y, int y_bf16, int64_t P, const float 
                               const int32_t *pos, const void *shared, int shared_bf16, const float *gate,
                               int64_t M, int k, int64_t D, float *out, hipStream_t stream);
 
+// dr_route_noalloc: the size of the library's static device buffer (the
+// logits of 16384 tokens x 256 experts in fp32), and its address on the
+// current device (looked up on the first call per device).
+constexpr int64_t kNoallocScratchBytes = int64_t(16) << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 // Compute units of the current device (256 if the query fails).
 int64_t narrow_max_m(int64_t E, int64_t K);
 int device_cus();

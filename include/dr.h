@@ -159,6 +159,26 @@ dr_status dr_route(const void *x, dr_dtype x_dtype, const float *W, int64_t M, i
                    int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
                    void *logits, dr_margin *margins, uint32_t flags, void *stream);
 
+/*
+ * dr_route_noalloc -- dr_route for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, same bits as dr_route, and the same family
+ * choice as dr_route given a logits buffer.  When logits is NULL and that
+ * family runs in two launches (tiny, narrow, split), the logits pass between
+ * the launches through the library's one static device buffer of 16 MiB
+ * (the fp32 logits of 16384 tokens x 256 experts) instead of a caller
+ * buffer, so the call neither allocates nor needs a logits buffer; a batch
+ * whose logits (M*E*4 bytes, M*E*2 with DR_BF16 logits) exceed it returns
+ * DR_ERR_UNSUPPORTED with the sizes in dr_last_error().  With a logits buffer
+ * it is dr_route.  Each GPU holds its own copy of the buffer until the process
+ * ends (its address is looked up on the first call per device, with that
+ * device current); calls on one GPU share it, so calls that overlap on one
+ * GPU (two streams, two threads) race.
+ */
+dr_status dr_route_noalloc(const void *x, dr_dtype x_dtype, const float *W, int64_t M, int64_t K,
+                           int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids, float *weights,
+                           void *logits, dr_margin *margins, uint32_t flags, void *stream);
+
 /* dr_route with the kernel family forced.  Same bits as dr_route. */
 dr_status dr_route_variant(const void *x, dr_dtype x_dtype, const float *W, int64_t M,
                            int64_t K, int64_t E, int32_t k, dr_dtype logit_dtype, int32_t *ids,

@@ -297,3 +297,20 @@ def test_binding_validates_out_tensors():
         dr.route(x, torch.zeros((64, 256)), 8, out=(ok, None, None, None))
     with pytest.raises(TypeError):
         dr.gemm_bf16(x.to(torch.bfloat16), torch.zeros((64, 128), dtype=torch.bfloat16))
+
+
+def test_noalloc_refuses_batches_past_its_buffer(L):
+    """dr_route_noalloc checks the size of the logits it would keep in its
+    static device buffer before touching the device: 16384 x 256 fp32
+    logits fit, one token more does not (bf16 logits take half)."""
+    P = ctypes.c_void_p
+
+    def call(M, E=256, ld=0, lg=None, x=A):
+        return L.dr_route_noalloc(P(x) if x else None, 0, P(A), M, 2048, E, 8, ld, P(A), None, lg, None, 0, None)
+
+    assert call(16385) == UNSUPPORTED
+    assert "exceed" in L.dr_last_error().decode()
+    assert call(16385 * 2, ld=1) == UNSUPPORTED
+    assert call(8193, E=512) == UNSUPPORTED
+    assert call(0, x=0) == OK                      # empty batch: nothing launched, no device touched
+    assert call(1, x=0) == INVALID                 # the usual argument checks come first
