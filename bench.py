@@ -9,11 +9,13 @@ size dr_route runs two kernels: the logits GEMM, then the selection.
 
 Printed: one JSON line with the throughput; the roofline of the dominant
 kernel -- the logits GEMM's fp32 matrix-core FLOPs over that kernel's
-average launch duration, timed with HIP events on the stream it runs on, in
-a second timed loop that launches it alone through dr_route_logits -- with
-HBM traffic from the committed rocprofv3 counter summary when it still
-matches the kernel sources; an M-invariance and oracle check on sampled
-rows; and the CPU oracle timed on the same workload as a baseline.
+average launch duration, timed with HIP events on the stream it runs on
+over a second loop of back-to-back launches of that kernel alone (through
+dr_route_logits, the same kernel as inside dr_route) -- with HBM traffic from the
+committed rocprofv3 counter summary when it still matches the kernel
+sources; an M-invariance and oracle check on sampled rows; and the CPU
+oracle timed on the same workload as a baseline, on every core of the
+process's affinity mask (within the CPU share OMP_NUM_THREADS states).
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -225,10 +227,26 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
         for Wl, xl in layers:
             dr.route(xl, Wl, TOPK, weights=False, logits=False, margins=False, out=(ids_out, None, None, None))
     ms = _time(stack, stream, torch, steps=3, warmup=1)
+    # every request's ids at every layer against its solo run, bit for bit
+    # (the pages' serve gate: each stream alone and batched), counted
+    offs = np.cumsum([0] + lengths)
+    cats = {"identical": 0, "order_only": 0, "set_differs": 0}
+    for Wl, xl in layers:
+        ids_b = dr.route(xl, Wl, TOPK, weights=False, logits=False, margins=False)[0].cpu().numpy()
+        for r in range(len(lengths)):
+            ids_s = dr.route(xl[offs[r]:offs[r + 1]].contiguous(), Wl, TOPK, weights=False, logits=False,
+                             margins=False)[0].cpu().numpy()
+            same = np.all(ids_s == ids_b[offs[r]:offs[r + 1]], axis=1)
+            same_set = np.all(np.sort(ids_s, 1) == np.sort(ids_b[offs[r]:offs[r + 1]], 1), axis=1)
+            cats["identical"] += int(same.sum())
+            cats["order_only"] += int((same_set & ~same).sum())
+            cats["set_differs"] += int((~same_set).sum())
     suite["stack_40_layers_M16384_ids_only"] = {
         "variant": dr.auto_variant(Ms, K, E, logits=dr.scratch_logits_used(Ms, K, E)), "ms_end_to_end": round(ms, 3),
         "tokens_per_s": round(Ms * wl.STACK_LAYERS / (ms * 1e-3), 1),
-        "note": "tokens x layers per second over 40 back-to-back dr_route calls, ids only"}
+        "note": "tokens x layers per second over 40 back-to-back dr_route calls, ids only",
+        "solo_vs_batched": {"token_layer_decisions": Ms * wl.STACK_LAYERS, **cats,
+                            "pass": cats["identical"] == Ms * wl.STACK_LAYERS}}
     del layers, ids_out
     log("40-layer stack done")
 
@@ -450,9 +468,11 @@ def main():
     ms_step = ms_total / args.steps
     tokens_per_s = M / (ms_step * 1e-3)
 
-    # the dominant kernel alone: the logits GEMM launched by itself, the same
-    # number of times, on the same stream (its launches run back to back, so
-    # the bracketing events time the kernels)
+    # the dominant kernel alone: the logits GEMM launched back to back through
+    # dr_route_logits (the same kernel, configuration and bits as inside
+    # dr_route), `steps` launches on the stream they run on, bracketed by HIP
+    # events; back-to-back launches leave no gaps, so the events time the
+    # kernels themselves
     variant = dr.auto_variant(M, K, E)
     lg_only = out[2]
     if variant == "split":
@@ -515,7 +535,9 @@ def main():
                    "kernel": variant},
         "roofline": roofline,
         "roofline_kernel": {"name": dominant, "us_per_launch": round(ms_kernel * 1e3, 2),
-                            "flop_per_launch": flops},
+                            "flop_per_launch": flops,
+                            "timed": f"{args.steps} back-to-back launches after {args.warmup} untimed, "
+                                     "bracketed by HIP events"},
         "settle": {"steps": settle_blocks * 20,
                    "note": "untimed steps before the warm-up, until two blocks of 20 agree within 1%"},
         "m_invariance": inv,
@@ -533,7 +555,11 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
 
-        nthreads = min(16, oracle.default_threads())
+        # every core in the process's affinity mask, within the CPU share the
+        # host gives a one-GPU job when it states one (OMP_NUM_THREADS)
+        affinity = oracle.default_threads()
+        share = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+        nthreads = min(affinity, share) if share > 0 else affinity
         sample = M  # the whole batch: about 9 CPU-seconds of fmaf work
         t0 = time.perf_counter()
         rids, rw, rlg, rmg = oracle.route(x[:sample], W, TOPK, nthreads=nthreads)
@@ -545,7 +571,8 @@ def main():
                       np.array_equal(rmg.view(np.uint8), mg_full[:sample].view(np.uint8)))
         result["cpu_baseline"] = {"value": round(sample / dt, 1), "unit": "tokens/s", "cores": nthreads,
                                   "kind": "oracle",
-                                  "sample": f"all {sample} tokens of the workload, one oracle call, wall clock"}
+                                  "sample": f"all {sample} tokens of the workload, one oracle call, wall clock",
+                                  "affinity_cores": affinity, "cpu_share": share or None}
         result["oracle_parity"] = parity
         result["oracle_ulps_hist_equal"] = _ulps_hist(np, rmg["ulps"]) == result["margins"]["ulps_hist"]
         if "ties" in checks:
