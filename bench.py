@@ -319,7 +319,8 @@ def measure_suite(dr, wl, torch, np, xd, Wd, stream):
     return suite, checks
 
 
-PROFILE_WORKLOADS = ("route", "route_fused", "route_split", "dense_M4096", "dense_M65", "grouped")
+PROFILE_WORKLOADS = ("route", "route_fused", "route_split", "route_bf16x", "dense_M4096", "dense_M65", "dense_M1",
+                     "grouped")
 
 
 def profile_workload(name: str, steps: int, warmup: int, copy_calibration: bool = False):
@@ -328,7 +329,8 @@ def profile_workload(name: str, steps: int, warmup: int, copy_calibration: bool 
     rocprofv3 kernel-trace and counter runs wrap, so that their dispatches are
     this workload's only.  route: dr_route at the headline workload (the
     family AUTO picks); route_fused / route_split: that call with the family
-    forced; dense_M4096 / dense_M65: dr_gemm_bf16 at K = N = 4096; grouped:
+    forced; route_bf16x: with x stored as bf16; dense_M4096 / dense_M65 /
+    dense_M1: dr_gemm_bf16 at K = N = 4096; grouped:
     the grouped expert GEMM at 65536 rows x 2048 x 1024, E = 256."""
     import numpy as np
     import torch
@@ -347,7 +349,9 @@ def profile_workload(name: str, steps: int, warmup: int, copy_calibration: bool 
     if name.startswith("route"):
         xd = torch.from_numpy(wl.sweep_x(M, K)).to(dev)
         Wd = torch.from_numpy(wl.router_weights(K, E)).to(dev)
-        variant = {"route": "auto", "route_fused": "fused", "route_split": "split"}[name]
+        variant = {"route": "auto", "route_fused": "fused", "route_split": "split", "route_bf16x": "auto"}[name]
+        if name == "route_bf16x":  # the same bf16 values stored as bf16 (staged as they are)
+            xd = xd.to(torch.bfloat16)
         out = (torch.empty((M, TOPK), dtype=torch.int32, device=dev),
                torch.empty((M, TOPK), dtype=torch.float32, device=dev),
                torch.empty((M, E), dtype=torch.float32, device=dev),
@@ -355,7 +359,7 @@ def profile_workload(name: str, steps: int, warmup: int, copy_calibration: bool 
         fn = lambda: dr.route(xd, Wd, TOPK, out=out, variant=variant)  # noqa: E731
         work = {"M": M, "K": K, "E": E, "k": TOPK, "flop": 2.0 * M * K * E}
     elif name.startswith("dense"):
-        m = {"dense_M4096": 4096, "dense_M65": 65}[name]
+        m = {"dense_M4096": 4096, "dense_M65": 65, "dense_M1": 1}[name]
         xb = torch.from_numpy(wl.dense_x_bits(m).view(np.int16)).view(torch.bfloat16).to(dev)
         Wb = torch.from_numpy(wl.dense_w_bits().view(np.int16)).view(torch.bfloat16).to(dev)
         ob = torch.empty((m, wl.DENSE_N), dtype=torch.float32, device=dev)

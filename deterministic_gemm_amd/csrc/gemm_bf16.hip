@@ -277,19 +277,33 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
     }
 }
 
+// Workgroups go to the eight XCDs in turn (linear index L to XCD L % 8).
+// With gy > 0 the tile grid is cut into gy x (8 / gy) rectangles and XCD j
+// takes rectangle j: its L2 then reads x for the rectangle's row tiles and W
+// for its column tiles only (at 16 x 16 tiles, 24 of 64 MiB instead of all of
+// x and an eighth of W).  Otherwise, with a multiple of eight column tiles,
+// XCD j takes the j-th contiguous eighth of them with every row tile, so
+// neighbouring tiles that share 128-byte lines of W read them through one L2.
 template <class C, class OutT, bool BUF>
 __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__restrict__ x,
                                                          const uint16_t *__restrict__ W,
                                                          OutT *__restrict__ out, int64_t M, int K,
-                                                         int N) {
+                                                         int N, int gy) {
   __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
-  const int64_t m0 = static_cast<int64_t>(blockIdx.y) * C::BM;
-  // Workgroups go to the eight XCDs in turn.  With a multiple of eight column
-  // tiles, XCD j takes the j-th contiguous eighth of them, so neighbouring
-  // tiles that share 128-byte lines of W read them through one L2.
-  const int nx = gridDim.x;
-  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
-  gemm_tile<C, OutT, false, BUF>(x, nullptr, M, W, out, m0, M, K, N, bx * C::BN, smem);
+  const int nx = gridDim.x, ny = gridDim.y;
+  int bx, by;
+  if (gy > 0) {
+    const int L = blockIdx.x + blockIdx.y * nx;
+    const int xcd = L % 8, slot = L / 8;
+    const int gx = 8 / gy, rb = ny / gy, cb = nx / gx;  // tiles per rectangle: rb x cb
+    by = (xcd / gx) * rb + slot / cb;
+    bx = (xcd % gx) * cb + slot % cb;
+  } else {
+    by = blockIdx.y;
+    bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
+  }
+  gemm_tile<C, OutT, false, BUF>(x, nullptr, M, W, out, static_cast<int64_t>(by) * C::BM, M, K, N, bx * C::BN,
+                                 smem);
 }
 
 // Grouped (per-expert) product: expert e owns output rows [offsets[e],
@@ -366,22 +380,136 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
                                  (slot % ncol) * C::BN, smem);
 }
 
+// Skinny batches (M <= 16): every row of the batch in one workgroup, against
+// a 16-column strip of W.  With few rows the product is bound by streaming W
+// (32 MiB at K = N = 4096) from HBM; 16-column strips put a workgroup on every
+// CU (256 at N = 4096) and a ring of eight 16 KiB stages keeps 56 KiB of W in
+// flight per CU.  Four wavefronts share the transfers; wavefront w runs the
+// 16-row fragment w (the configuration allows up to NW of them).  Each output is still reduced by the dense
+// kernel's instruction sequence -- one v_mfma_f32_16x16x32_bf16 per 32-wide K
+// step, k ascending, one accumulator from zero, the same operand placement in
+// the lanes (the same stage layout, swizzles and reads, through gemm_kstep) --
+// so rows are bit-identical to every other tile configuration.
+template <int MR_, int BK_, int S_, int NW_>
+struct SkinnyCfg {
+  static constexpr int BM = MR_, BN = 16, BK = BK_, S = S_, NW = NW_, NT = 64 * NW;
+  static constexpr int TM = 16, TN = 16, FM = 1, FN = 1;  // one 16x16 fragment per computing wavefront
+  static constexpr int FMT = MR_ / 16;                    // computing wavefronts
+  static constexpr int UA = BK / 8, UB = 2;
+  static constexpr int AU = BM * UA, BU = BK * UB;
+  static constexpr int ABYTES = AU * 16, STAGE = (AU + BU) * 16;
+  static constexpr int PER = (AU + BU) / 64 / NW;
+  static_assert(MR_ % 16 == 0 && FMT <= NW, "a wavefront per row fragment");
+  static_assert(BK % 32 == 0 && (UA == 16 || UA == 32), "K steps per stage");
+  static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
+  static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
+  static_assert(S * STAGE <= 160 * 1024, "LDS");
+  __host__ __device__ static constexpr int swa(int r) { return r % 16; }
+  __host__ __device__ static constexpr int swb(int k) { return (k / 8) % 2; }
+};
+
+template <class C, class OutT>
+__global__ __launch_bounds__(C::NT) void gemm_skinny_kernel(const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ W,
+                                                           OutT *__restrict__ out, int64_t M, int K, int N) {
+  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
+  // XCD j takes the j-th contiguous eighth of the strips (as in the dense
+  // kernel), so the four strips of a 128-byte line of W share one L2
+  const int nx = gridDim.x;
+  const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int n0 = bx * C::BN;
+  constexpr int S = C::S;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int ta = lane & 15, tj = ta >> 2, tq = ta & 3;
+  const int nst = (K + C::BK - 1) / C::BK;
+  const bool computes = wave < C::FMT && static_cast<int64_t>(wave) * 16 < M;
+
+  f32x4 acc[1][1];
+  acc[0][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  int32_t arow[C::PER];
+  gemm_arows<C>(nullptr, M, 0, M, wave, lane, arow);
+  uint32_t voff[C::PER];
+  gemm_voffs<C>(arow, K, N, n0, wave, lane, voff);
+  const auto issue = [&](int st) {
+    gemm_issue_buf<C>(x, M, W, K, N, voff, st, nst, wave, smem + (st % S) * C::STAGE);
+  };
+#pragma unroll
+  for (int i = 0; i < S - 1; ++i) issue(i);
+  for (int st = 0; st < nst; ++st) {
+    compiler_fence();
+    wait_vmcnt<C::PER * (S - 2)>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    issue(st + S - 1);
+    const char *As = smem + (st % S) * C::STAGE;
+    const char *Bs = As + C::ABYTES;
+    const int nsub = (K - st * C::BK) < C::BK ? (K - st * C::BK) / 32 : C::BK / 32;
+    if (computes) {
+#pragma unroll
+      for (int kk = 0; kk < C::BK / 32; ++kk)
+        if (kk < nsub) gemm_kstep<C>(As, Bs, kk, wave, 0, r16, g4, tj, tq, acc);
+    }
+  }
+  compiler_fence();
+  wait_vmcnt<0>();
+  if (!computes) return;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t m = wave * 16 + g4 * 4 + q;
+    if (m >= M) continue;
+    if constexpr (sizeof(OutT) == 2) out[m * N + n0 + r16] = gemm_f32_to_bf16(acc[0][0][q]);
+    else out[m * N + n0 + r16] = acc[0][0][q];
+  }
+}
+
 // Buffer descriptors address 32-bit byte ranges: operands under 4 GiB take
 // them, larger ones the 64-bit addresses.
 static bool gemm_buf_ok(int64_t rows, int64_t K, int64_t N) {
   return rows * K * 2 < kBufFarOff && K * N * 2 < kBufFarOff;
 }
 
+// Rectangles per column of the XCD map (gemm_bf16_kernel): the gy in {1, 2,
+// 4, 8} that divides the tile grid into eight equal rectangles with the fewest
+// operand bytes per rectangle (rows x BM + columns x BN, both times K), or 0
+// (the column-eighths map) when no such cut exists or the grid has fewer than
+// two tiles per XCD.
+static int gemm_xcd_rows(int64_t nx, int64_t ny, int bm, int bn) {
+  if (nx * ny < 16) return 0;
+  int best = 0;
+  int64_t best_cost = 0;
+  for (int gy = 1; gy <= 8; gy *= 2) {
+    const int gx = 8 / gy;
+    if (ny % gy != 0 || nx % gx != 0) continue;
+    const int64_t cost = (ny / gy) * bm + (nx / gx) * bn;
+    if (best == 0 || cost < best_cost) {
+      best = gy;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 template <class C, class OutT = float>
 static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K,
                                 int64_t N, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(N / C::BN), static_cast<uint32_t>((M + C::BM - 1) / C::BM));
+  const int64_t nx = N / C::BN, ny = (M + C::BM - 1) / C::BM;
+  const dim3 grid(static_cast<uint32_t>(nx), static_cast<uint32_t>(ny));
+  const int gy = gemm_xcd_rows(nx, ny, C::BM, C::BN);
   if (gemm_buf_ok(M, K, N))
     hipLaunchKernelGGL((gemm_bf16_kernel<C, OutT, true>), grid, dim3(C::NT), 0, stream, x, W, out, M,
-                       static_cast<int>(K), static_cast<int>(N));
+                       static_cast<int>(K), static_cast<int>(N), gy);
   else
     hipLaunchKernelGGL((gemm_bf16_kernel<C, OutT, false>), grid, dim3(C::NT), 0, stream, x, W, out, M,
-                       static_cast<int>(K), static_cast<int>(N));
+                       static_cast<int>(K), static_cast<int>(N), gy);
+  return hipGetLastError();
+}
+
+template <class C, class OutT>
+static hipError_t launch_skinny_c(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
+                                  hipStream_t stream) {
+  hipLaunchKernelGGL((gemm_skinny_kernel<C, OutT>), dim3(static_cast<uint32_t>(N / C::BN)), dim3(C::NT), 0, stream,
+                     x, W, out, M, static_cast<int>(K), static_cast<int>(N));
   return hipGetLastError();
 }
 
@@ -431,11 +559,22 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
 // = 4096, N = 256..14336): within ~1 us or 2% everywhere; e.g. K = N = 4096:
 // M = 256 38 us, 512 43, 1024 56, 2048 90, 3072 124, 4096 142; K = 2048, N =
 // 256: M = 1024 13 us, 8192 25.
+// Measured at K = N = 4096 (graph replay): 13.2 us at M = 1 and 14.3 at M =
+// 16 against 14.5-15 for 32 x 32 tiles; with 32, 64 or 80 rows per strip it
+// lost (16.1-16.5 us at M = 19-32, 19-20.7 at M = 33-80, against 15.0 and
+// 18.3-18.5): the bytes in flight are not what caps these batches.
+constexpr int64_t kSkinnyMaxM = 16;
+
 template <class OutT>
 static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
                                   hipStream_t stream) {
   const int64_t cus = device_cus();
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * (N / bn); };
+  // skinny batches: all rows in one workgroup per 16-column strip, while the
+  // strips cover at least half the CUs and the operands fit buffer
+  // descriptors
+  if (M <= kSkinnyMaxM && N / 16 >= cus / 2 && gemm_buf_ok(M, K, N))
+    return launch_skinny_c<SkinnyCfg<16, 256, 8, 4>, OutT>(x, W, out, M, K, N, stream);
   if (M <= 128 || tiles(32, 32) <= 2 * cus)
     return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>, OutT>(x, W, out, M, K, N, stream);
   if (tiles(64, 64) <= cus) return launch_gemm_c<GemmCfg<64, 64, 2, 2, 128, 3>, OutT>(x, W, out, M, K, N, stream);

@@ -545,24 +545,12 @@ hipError_t launch_route_select(const RouteLaunch &L) {
   }
 }
 
-#ifdef DR_SWEEP
-#include <cstdlib>
-#endif
-
 bool fused_supports(int64_t E, int64_t K, bool x_f32) {
   return E == 256 && K >= 1 && K <= (x_f32 ? 16384 : 4096) && (K % (x_f32 ? 4 : 8)) == 0;
 }
 
 hipError_t launch_route_fused(const RouteLaunch &L) {
   if (L.E != 256) return hipErrorInvalidValue;
-#ifdef DR_SWEEP
-  const char *cv = getenv("DR_FUSED_CFG");
-  const int cfg = cv ? atoi(cv) : 0;
-  if (L.xf) {
-    if (cfg == 1) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, false>>(L);
-    if (cfg == 2) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 3, 1, true>>(L);
-  }
-#endif
   if (!L.xf) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true, true>>(L);
   return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true>>(L);
 }

@@ -31,11 +31,12 @@ def test_gemm_rows_invariant_across_m_and_close_to_exact(dense):
     note("gemm M=4096")
     full = dr.gemm_bf16(xd, Wd).cpu().numpy()
     # the sweep sizes plus others so that, on a 256-CU device, every tile
-    # configuration N = 4096 reaches runs: 32 x 32 (M <= 128), 64 x 64 (200,
+    # configuration N = 4096 reaches runs: the skinny 16-column strips (M =
+    # 1, 16), 32 x 32 (17 <= M <= 128), 64 x 64 (200,
     # 256), 64 x 64 with two stages (300, 512), 128 x 128 (1000, 1024),
     # 256 x 128 (2048), 256 x 256 (3000, 4096), several with a ragged last
     # tile (64 x 128 runs where M > N: the bf16 router's logits GEMM)
-    for M in sorted(set(wl.DENSE_MS) | {200, 256, 300, 1000, 1024, 2048, 3000}):
+    for M in sorted(set(wl.DENSE_MS) | {1, 16, 17, 33, 64, 80, 81, 200, 256, 300, 1000, 1024, 2048, 3000}):
         note(f"gemm M={M}")
         out = dr.gemm_bf16(xd[:M].contiguous(), Wd).cpu().numpy()
         assert f32_equal_bits(out, full[:M]), f"M={M} rows differ from the M=4096 run"
@@ -70,10 +71,13 @@ def test_gemm_small_shapes_close_to_exact():
     # partial K stages and ragged M tiles in every tile configuration (on a
     # 256-CU device: 32 x 32 for the first six, then 64 x 64, 64 x 64 with
     # two stages, 128 x 128, 256 x 128, twice 256 x 256, and 64 x 128, which
-    # runs only where M > N: a ragged 48-row last tile and a partial K stage)
+    # runs only where M > N: a ragged 48-row last tile and a partial K stage;
+    # then the skinny strips (M <= 16) with a partial last K stage, and 32 x 32
+    # tiles at N = 4096)
     shapes = ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
               (1500, 160, 256), (200, 160, 4096), (450, 96, 4096), (900, 224, 4096), (1800, 96, 4096),
-              (2100, 96, 4096), (4100, 160, 4096), (6000, 96, 256))
+              (2100, 96, 4096), (4100, 160, 4096), (6000, 96, 256),
+              (3, 96, 4096), (16, 288, 2048), (40, 224, 4096), (70, 160, 4096))
     worst = 0.0
     for (M, K, N) in shapes:
         xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
