@@ -25,11 +25,25 @@
 // 16-byte units of each LDS row are XOR-swizzled by row so that the reads of
 // one instruction spread over the LDS banks; writer and readers apply the same
 // swizzle.
+#include <type_traits>
+#include <utility>
+
 #include "lds_dma.h"
 #include "buf_dma.h"
 #include "launch.h"
 
 namespace drk {
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, each i a constant
+// expression inside f.
+template <class F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -202,6 +216,69 @@ __device__ __forceinline__ void gemm_kstep(const char *As, const char *Bs, int k
       acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
 }
 
+// One whole stage (BK / 32 K steps) of a wavefront's tile, with the operand
+// reads running ahead of the matrix steps: the x fragment of step t + AD (a
+// step is one K step of one 16-row fragment) and the W fragments of the next
+// K step are read from LDS while the matrix steps of step t run, into a ring
+// of AD + 1 x fragments and two sets of W fragments, each read issued between
+// two matrix steps.  The same instructions and operands per output as
+// gemm_kstep, in the same order per accumulator, so the bits are the same.
+template <class C>
+__device__ __forceinline__ void gemm_stage_pipelined(const char *As, const char *Bs, int wm, int wn, int r16, int g4,
+                                                     int tj, int tq, f32x4 (&acc)[C::FM][C::FN]) {
+  constexpr int FM = C::FM, FN = C::FN, KK = C::BK / 32, T = KK * FM;
+  constexpr int BSTEP = FM > 1 ? FM / 2 : 0;  // the step of each K step that reads the next W fragments
+  constexpr int AD = 2;  // x fragments read ahead
+  bf16x8 af[AD + 1], bfv[2][FN];
+  const auto read_a = [&](int t, bf16x8 &dst) {
+    const int kk = t / FM, i = t % FM;
+    const int r = wm * C::TM + i * 16 + r16;
+    const int u = (kk * 4 + g4) ^ C::swa(r);
+    dst = *reinterpret_cast<const bf16x8 *>(As + (r * C::UA + u) * 16);
+  };
+  const auto read_b = [&](int kk, bf16x8 (&dst)[FN]) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = wn * C::TN + j * 16 + 4 * tq;
+      i16x4 h[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int kr = kk * 32 + 8 * g4 + 4 * c + tj;
+        const int u = (col / 8) ^ C::swb(kr);
+        const char *a = Bs + (kr * C::UB + u) * 16 + (col % 8) * 2;
+        h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
+      }
+      const i16x4 lo = h[0], hi = h[1];
+      dst[j] = __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){
+                                              lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+    }
+  };
+  read_b(0, bfv[0]);
+  static_for<AD>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    if constexpr (t < T) read_a(t, af[t]);
+  });
+  static_for<T>([&](auto tc) {
+    constexpr int t = decltype(tc)::value;
+    constexpr int kk = t / FM, i = t % FM;
+    constexpr bool ra = t + AD < T, rb = i == BSTEP && kk + 1 < KK;
+    constexpr int nr = (ra ? 1 : 0) + (rb ? 2 * FN : 0);  // LDS reads issued in this step
+    if constexpr (ra) read_a(t + AD, af[(t + AD) % (AD + 1)]);
+    if constexpr (rb) read_b(kk + 1, bfv[(kk + 1) % 2]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[t % (AD + 1)], bfv[kk % 2][j], acc[i][j], 0, 0, 0);
+    // one read after each matrix step, the rest after the step's last one
+    constexpr int inter = nr < FN ? nr : FN;
+    static_for<inter>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    });
+    if constexpr (FN > inter) __builtin_amdgcn_sched_group_barrier(0x008, FN - inter, 0);
+    if constexpr (nr > inter) __builtin_amdgcn_sched_group_barrier(0x100, nr - inter, 0);
+  });
+}
+
 // One output tile: rows [m0, min(m0 + BM, mend)) and columns [n0, n0 + BN) of
 // out = x[rows] . W, every output reduced by the same instruction sequence;
 // stored as fp32, or rounded to bf16 (OutT = uint16_t).  With SKIP, a
@@ -252,10 +329,21 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
     const char *As = smem + (st % S) * C::STAGE;
     const char *Bs = As + C::ABYTES;
     const int nsub = (K - st * C::BK) < C::BK ? (K - st * C::BK) / 32 : C::BK / 32;
+    if (!SKIP || wlive) {
+      // wavefront tiles of up to 8 fragments: the larger ones (64 x 64 and
+      // 128 x 64) measured slower pipelined (86 against 77 us at M = 2048,
+      // K = N = 4096) or ran out of registers
+      bool done = false;
+      if constexpr (C::FM * C::FN <= 8) {
+        if (nsub == C::BK / 32) {
+          gemm_stage_pipelined<C>(As, Bs, wm, wn, r16, g4, tj, tq, acc);
+          done = true;
+        }
+      }
+      if (!done) {
 #pragma unroll
-    for (int kk = 0; kk < C::BK / 32; ++kk) {
-      if (kk < nsub) {
-        if (!SKIP || wlive) gemm_kstep<C>(As, Bs, kk, wm, wn, r16, g4, tj, tq, acc);
+        for (int kk = 0; kk < C::BK / 32; ++kk)
+          if (kk < nsub) gemm_kstep<C>(As, Bs, kk, wm, wn, r16, g4, tj, tq, acc);
       }
     }
   }
