@@ -147,39 +147,59 @@ __global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const void *
     compiler_fence();
     narrow_issue<C>(xf, W, M, K, m0, e0, nb, g0, nch, lane, ci + S - 1, my + ((ci + S - 1) % S) * C::STG);
     const float *cur = my + (ci % S) * C::STG;
+    // operands of step group c4 + 1 read while the matrix steps of c4 run,
+    // one read between each of the first matrix steps (as in split_step,
+    // route_split.hip)
     const float *xs = cur + C::WST;
-    [[maybe_unused]] uint4 ux[AT];  // bf16 x: one 16-byte unit feeds two steps
-#pragma unroll
-    for (int c4 = 0; c4 < KC / 4; ++c4) {
-      float4 av[AT];
+    float4 av[2][AT];
+    float bw[2][BT][4];
+    [[maybe_unused]] uint4 ux[2][AT];  // bf16 x: one 16-byte unit feeds two step groups
+    const auto read_ops = [&](int c4, int r) {
 #pragma unroll
       for (int a = 0; a < AT; ++a) {
         const int tok = a * 16 + r_l;
         if constexpr (C::XB) {
-          // unit c4 / 2 of the row holds 8 values, read whole at even steps;
-          // this step's 4 are its half c4 % 2
           if ((c4 & 1) == 0)
-            ux[a] = *reinterpret_cast<const uint4 *>(xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
-          const uint32_t lo = (c4 & 1) ? ux[a].z : ux[a].x, hi = (c4 & 1) ? ux[a].w : ux[a].y;
-          av[a] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
+            ux[(c4 >> 1) & 1][a] =
+                *reinterpret_cast<const uint4 *>(xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
         } else {
-          av[a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+          av[r][a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
         }
       }
-      float bw[BT][4];
 #pragma unroll
       for (int b = 0; b < BT; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bw[b][q] = cur[s_l * C::SW + (4 * c4 + q) * ET + b * 16 + r_l];
+        for (int q = 0; q < 4; ++q) bw[r][b][q] = cur[s_l * C::SW + (4 * c4 + q) * ET + b * 16 + r_l];
+    };
+    read_ops(0, 0);
+#pragma unroll
+    for (int c4 = 0; c4 < KC / 4; ++c4) {
+      const int r = c4 & 1;
+      if (c4 + 1 < KC / 4) read_ops(c4 + 1, r ^ 1);
+      if constexpr (C::XB) {
+#pragma unroll
+        for (int a = 0; a < AT; ++a) {
+          const uint4 u = ux[(c4 >> 1) & 1][a];
+          const uint32_t lo = (c4 & 1) ? u.z : u.x, hi = (c4 & 1) ? u.w : u.y;
+          av[r][a] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
+        }
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int a = 0; a < AT; ++a)
 #pragma unroll
           for (int b = 0; b < BT; ++b) {
-            const float aval = (q == 0) ? av[a].x : (q == 1) ? av[a].y : (q == 2) ? av[a].z : av[a].w;
-            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[b][q], acc[a][b], 0, 0, 0);
+            const float aval = (q == 0) ? av[r][a].x : (q == 1) ? av[r][a].y : (q == 2) ? av[r][a].z : av[r][a].w;
+            acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[r][b][q], acc[a][b], 0, 0, 0);
           }
+      constexpr int NR = AT + 2 * BT, NM = 4 * AT * BT;
+#pragma unroll
+      for (int i = 0; i < (NR < NM ? NR : NM); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      if constexpr (NM > NR) __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
     }
     if (cg == C::CPG - 1) {
       // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
