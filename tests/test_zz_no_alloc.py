@@ -59,3 +59,45 @@ def test_noalloc_equals_dr_route_on_two_calls_second_smaller():
                             TOPK, dr.DR_F32, ctypes.c_void_p(ids.data_ptr()), None, None, None, 0, None)
     assert st == dr.DR_ERR_UNSUPPORTED
     assert "16777216" in L.dr_last_error().decode()
+
+
+@pytest.mark.parametrize("M", [8192, 300])  # the split and the narrow families
+def test_noalloc_captured_in_a_graph(M):
+    """The caller the entry point is for: code under HIP graph capture.  With
+    every output preallocated, the captured call allocates nothing (torch's
+    allocated bytes are unchanged across the captured call), and each replay after
+    new inputs are copied in gives dr_route's bits on those inputs, with eager
+    work and synchronisations between the replays."""
+    dr = require_gpu()
+    W = dev(wl.router_weights(K, E))
+    x_static = dev(wl.sweep_x(M, K))
+    out = (torch.empty((M, TOPK), dtype=torch.int32, device="cuda"),
+           torch.empty((M, TOPK), dtype=torch.float32, device="cuda"), None,
+           torch.empty((M, 4), dtype=torch.int32, device="cuda"))
+    dr.route_noalloc(x_static, W, TOPK, out)  # warm
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    note(f"noalloc graph capture M={M}")
+    with torch.cuda.graph(g):
+        # measured inside the capture: torch's own capture state is set up
+        # when the context opens
+        before = torch.cuda.memory_allocated()
+        dr.route_noalloc(x_static, W, TOPK, out)
+        after = torch.cuda.memory_allocated()
+    torch.cuda.synchronize()
+    assert after == before
+    rng = np.random.default_rng(M + 7)
+    replays = 0
+    for rep in range(3):
+        x_static.copy_(torch.from_numpy(wl.bf16_valued(rng.standard_normal((M, K)).astype(np.float32))))
+        torch.cuda.synchronize()
+        note(f"noalloc graph replay {rep} M={M}")
+        g.replay()
+        torch.cuda.synchronize()
+        rids, rw, _, rmg = dr.route(x_static, W, TOPK)
+        torch.cuda.synchronize()
+        assert torch.equal(out[0], rids), f"replay {rep}: ids"
+        assert torch.equal(out[1].view(torch.int32), rw.view(torch.int32)), f"replay {rep}: weights"
+        assert torch.equal(out[3], rmg), f"replay {rep}: margins"
+        replays += 1
+    assert replays == 3
