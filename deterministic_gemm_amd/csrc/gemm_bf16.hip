@@ -13,18 +13,24 @@
 // product within a tolerance, and with themselves across M bit for bit.
 //
 // Data movement: x and W tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, 16 bytes per lane) through a ring of S stages of
-// BK steps of K, in their natural layouts -- x as [row][k], W as [k][n].  The
-// x operand of a 16x16x32 step is eight consecutive k of one row (one 16-byte
-// LDS read); the W operand is eight consecutive k of one column, which the
-// [k][n] layout stores 2N bytes apart, so it is read with the LDS transpose
-// read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i receives
-// element i % 4 of the 8 bytes read by lane i / 4 + 4j, for j = 0..3.  With
-// lane i/4 + 4j reading row k0 + j at columns c0 + 4(i/4) .. +3, lane i gets
-// column c0 + i at rows k0 .. k0+3; two such reads give the eight k.  The
-// 16-byte units of each LDS row are XOR-swizzled by row so that the reads of
-// one instruction spread over the LDS banks; writer and readers apply the same
-// swizzle.
+// (16 bytes per lane, the LDS side written in order) through a ring of S
+// stages of BK steps of K.  The x operand of a 16x16x32 step is eight
+// consecutive k of one row: one 16-byte LDS read from x stored as [row][k],
+// its 16-byte units XOR-swizzled by row so that one instruction's reads
+// spread over the banks.  The W operand is eight consecutive k of one column,
+// which W's [k][n] layout keeps 2N bytes apart, so it is read with the LDS
+// transpose read (ds_read_b64_tr_b16): within each group of 16 lanes, lane i
+// receives element i % 4 of the 8 bytes read by lane i / 4 + 4j, j = 0..3.
+// With lane i/4 + 4j reading row k0 + j at columns c0 + 4(i/4) .. +3, lane i
+// gets column c0 + i at rows k0 .. k0+3; two such reads give the eight k.
+// Tiles of 128 columns or more keep W in LDS in 128-byte blocks of four K rows
+// by 16 columns, so each 16-lane group of a transpose read takes one whole
+// block and each 32-lane half of the instruction 256 contiguous bytes, all 64
+// banks once.  (In a microbenchmark, the same reads from row-major [k][n]
+// stages, four rows 512 bytes apart per group, ran at 55-75% of that rate.)
+// Each transfer lane fetches the 16-byte unit that its LDS position holds, so
+// global reads stay runs of 256 bytes per row.  Narrower tiles keep [k][n]
+// rows with XOR-swizzled units.
 #include <type_traits>
 #include <utility>
 
@@ -51,33 +57,62 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 static __device__ const Pad16 g_zero16 = {{0.0f, 0.0f, 0.0f, 0.0f}};
 
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_>
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int S_, bool ROT_ = false>
 struct GemmCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, S = S_;
+  static constexpr bool ROT = ROT_;  // the rotated loop (gemm_tile_rot)
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;  // rows, columns per wavefront
   static constexpr int FM = TM / 16, FN = TN / 16;  // 16x16 tiles per wavefront
   static constexpr int UA = BK / 8;                 // 16-byte units per x row of a stage
   static constexpr int UB = BN / 8;                 // 16-byte units per W row of a stage
+  static constexpr int NB = BN / 16;                // W blocks of 16 columns
   static constexpr int AU = BM * UA, BU = BK * UB;  // units per stage
   static constexpr int ABYTES = AU * 16, STAGE = (AU + BU) * 16;
   static constexpr int PER = (AU + BU) / 64 / NW;   // transfers per wavefront per stage
   static_assert(FM >= 1 && FN >= 1 && TM * WM == BM && TN * WN == BN, "wavefront tiles");
   static_assert(BK % 32 == 0 && (UA == 4 || UA == 8 || UA == 16 || UA == 32), "K steps per stage");
-  static_assert(UB == 2 || UB == 4 || UB == 8 || UB == 16 || UB == 32, "W row units");
+  static_assert(NB % 2 == 0 && (BN >= 128 || UB == 4 || UB == 8), "W layout");
   static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
   static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
   // x rows: unit u of row r sits at u ^ swa(r); 16 consecutive rows reading
   // the same unit then hit 16 distinct 16-byte bank groups.
   __host__ __device__ static constexpr int swa(int r) { return UA >= 16 ? r % 16 : (r / (16 / UA)) % UA; }
-  // W rows: the 16 rows one transpose read touches (k = 8g + j + c, g, j in
-  // 0..3) get distinct offsets within their bank-group classes.
+  // W, tiles of 128 columns or more (QB): rows 4q .. 4q+3 by columns
+  // 16b .. 16b+15 form a 128-byte block, row-major, at block
+  // q * NB + (b ^ ((q >> 1) & 1)).  The xor puts the blocks of groups g and
+  // g+1 of a read (q two apart) 128 bytes apart modulo 256, so the two
+  // halves of each 256-byte pass use distinct banks.  Narrower tiles keep W
+  // row-major ([k][n], unit u of row k at u ^ swb(k)): their transfers then
+  // read whole 64- or 128-byte row pieces with consecutive lanes, where the
+  // blocks would alternate rows every two lanes (measured 7% slower at
+  // M = 128, K = N = 4096).
+  static constexpr bool QB = BN >= 128;
   __host__ __device__ static constexpr int swb(int k) {
-    return UB >= 16 ? (k % 4) + 4 * ((k / 8) % 4)
-           : UB == 8 ? ((k % 4) >> 1) + 2 * ((k / 8) % 4)
-           : UB == 4 ? (k / 8) % 4
-                     : (k / 8) % 2;
+    return UB == 8 ? ((k % 4) >> 1) + 2 * ((k / 8) % 4) : (k / 8) % 4;
+  }
+  // Unit p of the stage's W part holds row kr, columns nc .. nc+7.
+  __host__ __device__ static constexpr void b_unit(int p, int &kr, int &nc) {
+    if (QB) {
+      const int q = p / (BN / 2), r = p % (BN / 2);
+      kr = 4 * q + (r % 8) / 2;
+      nc = 16 * ((r / 8) ^ ((q >> 1) & 1)) + 8 * (r % 2);
+    } else {
+      kr = p / UB;
+      nc = 8 * ((p % UB) ^ swb(kr));
+    }
+  }
+  // Byte offset of what lane (g4, tj, tq) of a transpose read takes for K
+  // step kk, half c (rows 4c .. 4c+3 of its group of 8) and column fragment
+  // b: row kk*32 + 8 g4 + 4 c + tj, columns 16 b + 4 tq .. +3.
+  __host__ __device__ static constexpr int b_off(int kk, int g4, int c, int tj, int tq, int b) {
+    if (QB) {
+      const int q = 8 * kk + 2 * g4 + c;
+      return (q * NB + (b ^ (g4 & 1))) * 128 + tj * 32 + tq * 8;
+    }
+    const int kr = kk * 32 + 8 * g4 + 4 * c + tj, col = b * 16 + 4 * tq;
+    return (kr * UB + ((col / 8) ^ swb(kr))) * 16 + (col % 8) * 2;
   }
 };
 
@@ -119,11 +154,10 @@ __device__ __forceinline__ void gemm_issue(const uint16_t *__restrict__ x, const
       const int k = k0 + 8 * u;
       if (live && arow[i] >= 0 && k < K) src = x + static_cast<int64_t>(arow[i]) * K + k;
     } else {
-      const int q = p - C::AU;
-      const int kr = q / C::UB, up = q % C::UB;
-      const int u = up ^ C::swb(kr);
+      int kr = 0, nc = 0;
+      C::b_unit(p - C::AU, kr, nc);
       const int k = k0 + kr;
-      if (live && k < K) src = W + static_cast<int64_t>(k) * N + n0 + 8 * u;
+      if (live && k < K) src = W + static_cast<int64_t>(k) * N + n0 + nc;
     }
     dma16(src, lds);
   }
@@ -149,10 +183,9 @@ __device__ __forceinline__ void gemm_voffs(const int32_t (&arow)[C::PER], int K,
       const int u = up ^ C::swa(r);
       voff[i] = arow[i] >= 0 ? static_cast<uint32_t>((static_cast<int64_t>(arow[i]) * K + 8 * u) * 2) : kBufFarOff;
     } else {
-      const int q = p - C::AU;
-      const int kr = q / C::UB, up = q % C::UB;
-      const int u = up ^ C::swb(kr);
-      voff[i] = static_cast<uint32_t>((static_cast<int64_t>(kr) * N + n0 + 8 * u) * 2);
+      int kr = 0, nc = 0;
+      C::b_unit(p - C::AU, kr, nc);
+      voff[i] = static_cast<uint32_t>((static_cast<int64_t>(kr) * N + n0 + nc) * 2);
     }
   }
 }
@@ -196,13 +229,10 @@ __device__ __forceinline__ void gemm_kstep(const char *As, const char *Bs, int k
   }
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int col = wn * C::TN + j * 16 + 4 * tq;  // first of the 4 columns this lane reads
     i16x4 h[2];
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int kr = kk * 32 + 8 * g4 + 4 * c + tj;
-      const int u = (col / 8) ^ C::swb(kr);
-      const char *a = Bs + (kr * C::UB + u) * 16 + (col % 8) * 2;
+      const char *a = Bs + C::b_off(kk, g4, c, tj, tq, wn * FN + j);
       h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
     }
     const i16x4 lo = h[0], hi = h[1];
@@ -239,13 +269,10 @@ __device__ __forceinline__ void gemm_stage_pipelined(const char *As, const char 
   const auto read_b = [&](int kk, bf16x8 (&dst)[FN]) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int col = wn * C::TN + j * 16 + 4 * tq;
       i16x4 h[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int kr = kk * 32 + 8 * g4 + 4 * c + tj;
-        const int u = (col / 8) ^ C::swb(kr);
-        const char *a = Bs + (kr * C::UB + u) * 16 + (col % 8) * 2;
+        const char *a = Bs + C::b_off(kk, g4, c, tj, tq, wn * FN + j);
         h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
       }
       const i16x4 lo = h[0], hi = h[1];
@@ -279,6 +306,173 @@ __device__ __forceinline__ void gemm_stage_pipelined(const char *As, const char 
   });
 }
 
+// Stores a wavefront's tile: rows [m0, mend) only, fp32 or rounded to bf16.
+template <class C, class OutT>
+__device__ __forceinline__ void gemm_store(const f32x4 (&acc)[C::FM][C::FN], OutT *__restrict__ out, int64_t m0,
+                                           int64_t mend, int N, int n0, int wm, int wn, int r16, int g4) {
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t m = m0 + wm * C::TM + i * 16 + g4 * 4 + q;
+      if (m >= mend) continue;
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        if constexpr (sizeof(OutT) == 2) out[m * N + n0 + wn * C::TN + j * 16 + r16] = gemm_f32_to_bf16(acc[i][j][q]);
+        else out[m * N + n0 + wn * C::TN + j * 16 + r16] = acc[i][j][q];
+      }
+    }
+}
+
+// s_waitcnt with only the LDS counter constrained, to zero (gfx9 encoding).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// The rotated loop, for stages of one 32-wide K step (BK = 32) in a ring of
+// S >= 3, W in 128-byte blocks and an even number of column fragments.  The
+// plain loop reads a stage's fragments right after its barrier, so every
+// wavefront of the workgroup reads at once while the matrix cores idle.
+// Here step t's matrix instructions run on fragments already in registers,
+// and step t+1's fragments are read between them: x fragment i right after
+// the FN matrix steps that use fragment i (into the same registers), the W
+// fragments of step t+1 into a second set over the first FN/2 rows.  Per
+// step: each wavefront waits for its own reads of stage t (lgkmcnt) and for
+// stage t+1's transfers (vmcnt), then the barrier makes stage t+1 visible
+// and frees stage t's buffer, which takes stage t+S's transfers at once.
+// The same instructions and operands per output as gemm_kstep, in the same
+// order per accumulator, so the bits are the same.
+template <class C, class OutT, bool SKIP, bool BUF>
+__device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
+                                              int64_t Mx, const uint16_t *__restrict__ W, OutT *__restrict__ out,
+                                              int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
+  constexpr int FM = C::FM, FN = C::FN, S = C::S;
+  static_assert(C::BK == 32 && S >= 3 && C::QB && FN % 2 == 0 && FN / 2 <= FM, "rotated loop");
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int ta = lane & 15, tj = ta >> 2, tq = ta & 3;
+  const int nk = K / 32;  // K steps, one per stage
+  const bool wlive =
+      !SKIP || __builtin_amdgcn_readfirstlane(static_cast<int>(m0 + static_cast<int64_t>(wm) * C::TM < mend)) != 0;
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  int32_t arow[C::PER];
+  gemm_arows<C>(rows, Mx, m0, mend, wave, lane, arow);
+  uint32_t voff[C::PER];
+  if constexpr (BUF) gemm_voffs<C>(arow, K, N, n0, wave, lane, voff);
+  const auto issue = [&](int st) {
+    char *stage = smem + (st % S) * C::STAGE;
+    if constexpr (BUF) gemm_issue_buf<C>(x, Mx, W, K, N, voff, st, nk, wave, stage);
+    else gemm_issue<C>(x, arow, W, K, N, n0, st, nk, wave, lane, stage);
+  };
+
+  // Per-lane byte offsets within a stage.  x fragment i of this wavefront is
+  // row wm*TM + 16i + r16, unit g4 ^ swa(row); with four units per row swa
+  // repeats every 16 rows, so fragment i sits i * 1024 bytes after fragment
+  // 0.  W fragment j of half c is block (2 g4 + c) * NB + ((wn*FN + j) ^ s),
+  // s = g4 & 1: even j at boff0 + 128 j, odd j at boff1 + 128 j.
+  static_assert(C::UA == 4 && C::swa(16) == C::swa(0), "x fragments 1024 bytes apart");
+  const int arow0 = wm * C::TM + r16;
+  const int aoff = (arow0 * C::UA + (g4 ^ C::swa(arow0))) * 16;
+  const int s1 = g4 & 1;
+  const int bbase = ((2 * g4) * C::NB + wn * FN) * 128 + tj * 32 + tq * 8;
+  const int boff0 = bbase + s1 * 128, boff1 = bbase - s1 * 128;
+  const auto read_a = [&](const char *st, int i) {
+    return *reinterpret_cast<const bf16x8 *>(st + aoff + i * 16 * C::UA * 16);
+  };
+  const auto read_bh = [&](const char *st, int j, int c) {
+    const char *a = st + C::ABYTES + ((j & 1) ? boff1 : boff0) + j * 128 + c * C::NB * 128;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
+  };
+  const auto join = [](i16x4 lo, i16x4 hi) {
+    return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){lo[0], lo[1], lo[2], lo[3], hi[0],
+                                                                                    hi[1], hi[2], hi[3]});
+  };
+
+  bf16x8 af[FM], b0[FN], b1[FN];
+  // matrix steps of one K step on af / bc, reading step t+1's fragments from
+  // stage nx between them
+  const auto mstep = [&](bf16x8(&bc)[FN], bf16x8(&bn)[FN], const char *nx) {
+    i16x4 bh[FN][2];
+    static_for<FM>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      // rows 0 .. FN/2 - 1 read four W halves each (two fragments), the rest none
+      constexpr int nb = i < FN / 2 ? 4 : 0;
+      static_for<FN>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bc[j], acc[i][j], 0, 0, 0);
+      });
+      if constexpr (nb > 0) {
+        static_for<2>([&](auto jc) {
+          constexpr int j = 2 * i + decltype(jc)::value;
+          bh[j][0] = read_bh(nx, j, 0);
+          bh[j][1] = read_bh(nx, j, 1);
+          bn[j] = join(bh[j][0], bh[j][1]);
+        });
+      }
+      af[i] = read_a(nx, i);
+      // one LDS read after each of the row's first matrix steps, the rest after
+      constexpr int nr = nb + 1;
+      constexpr int inter = nr < FN ? nr : FN;
+      static_for<inter>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      });
+      if constexpr (FN > inter) __builtin_amdgcn_sched_group_barrier(0x008, FN - inter, 0);
+      if constexpr (nr > inter) __builtin_amdgcn_sched_group_barrier(0x100, nr - inter, 0);
+      // nothing crosses a row: a new x fragment is never read while the
+      // old one still waits for its matrix steps
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  const auto read_first = [&]() {
+    if (!SKIP || wlive) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = read_a(smem, i);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b0[j] = join(read_bh(smem, j, 0), read_bh(smem, j, 1));
+    }
+  };
+  // this wavefront's LDS reads done, then the barrier
+  const auto sync = [&]() {
+    compiler_fence();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+  };
+  // wait for stage t+1 and this wavefront's reads of stage t, make stage t+1
+  // visible and stage t's buffer free, refill it with stage t+S.  The last
+  // step also reads "step nk": stage nk was issued (as zeros) and waited for
+  // like any other, and its fragments go unused; so there is one loop body
+  // and no tail copy.
+#pragma unroll
+  for (int i = 0; i < S; ++i) issue(i);
+  compiler_fence();
+  wait_vmcnt<C::PER * (S - 1)>();
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+  read_first();
+  for (int t = 0; t < nk; ++t) {
+    compiler_fence();
+    wait_vmcnt<C::PER * (S - 2)>();
+    sync();
+    issue(t + S);
+    if (!SKIP || wlive) {
+      mstep(b0, b1, smem + ((t + 1) % S) * C::STAGE);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b0[j] = b1[j];
+    }
+  }
+  // no transfer may still be writing this workgroup's LDS when it moves on
+  compiler_fence();
+  wait_vmcnt<0>();
+  gemm_store<C>(acc, out, m0, mend, N, n0, wm, wn, r16, g4);
+}
+
 // One output tile: rows [m0, min(m0 + BM, mend)) and columns [n0, n0 + BN) of
 // out = x[rows] . W, every output reduced by the same instruction sequence;
 // stored as fp32, or rounded to bf16 (OutT = uint16_t).  With SKIP, a
@@ -290,6 +484,10 @@ template <class C, class OutT = float, bool SKIP = false, bool BUF = false>
 __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
                                           int64_t Mx, const uint16_t *__restrict__ W, OutT *__restrict__ out,
                                           int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
+  if constexpr (C::ROT) {
+    gemm_tile_rot<C, OutT, SKIP, BUF>(x, rows, Mx, W, out, m0, mend, K, N, n0, smem);
+    return;
+  }
   constexpr int FM = C::FM, FN = C::FN, S = C::S;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
@@ -350,19 +548,7 @@ __device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const 
   // no transfer may still be writing this workgroup's LDS when it moves on
   compiler_fence();
   wait_vmcnt<0>();
-
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t m = m0 + wm * C::TM + i * 16 + g4 * 4 + q;
-      if (m >= mend) continue;
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        if constexpr (sizeof(OutT) == 2) out[m * N + n0 + wn * C::TN + j * 16 + r16] = gemm_f32_to_bf16(acc[i][j][q]);
-        else out[m * N + n0 + wn * C::TN + j * 16 + r16] = acc[i][j][q];
-      }
-    }
+  gemm_store<C>(acc, out, m0, mend, N, n0, wm, wn, r16, g4);
 }
 
 // Workgroups go to the eight XCDs in turn (linear index L to XCD L % 8).
@@ -493,7 +679,16 @@ struct SkinnyCfg {
   static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(S * STAGE <= 160 * 1024, "LDS");
   __host__ __device__ static constexpr int swa(int r) { return r % 16; }
-  __host__ __device__ static constexpr int swb(int k) { return (k / 8) % 2; }
+  // W: one 16-column strip, [k][16], the two 16-byte units of each row
+  // swapped on alternate groups of 8 rows
+  __host__ __device__ static constexpr void b_unit(int p, int &kr, int &nc) {
+    kr = p / 2;
+    nc = 8 * ((p % 2) ^ ((kr / 8) % 2));
+  }
+  __host__ __device__ static constexpr int b_off(int kk, int g4, int c, int tj, int tq, int b) {
+    const int kr = kk * 32 + 8 * g4 + 4 * c + tj, col = b * 16 + 4 * tq;
+    return (kr * 2 + ((col / 8) ^ ((kr / 8) % 2))) * 16 + (col % 8) * 2;
+  }
 };
 
 template <class C, class OutT>
@@ -676,7 +871,7 @@ static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *ou
   if (tiles(128, 128) <= cus) return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>, OutT>(x, W, out, M, K, N, stream);
   if (tiles(256, 128) <= cus || N % 256 != 0)
     return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>, OutT>(x, W, out, M, K, N, stream);
-  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2>, OutT>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 32, 4, true>, OutT>(x, W, out, M, K, N, stream);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K, int64_t N,

@@ -70,13 +70,14 @@ def test_gemm_small_shapes_close_to_exact():
     rng = np.random.default_rng(3)
     # partial K stages and ragged M tiles in every tile configuration (on a
     # 256-CU device: 32 x 32 for the first six, then 64 x 64, 64 x 64 with
-    # two stages, 128 x 128, 256 x 128, twice 256 x 256, and 64 x 128, which
+    # two stages, 128 x 128, 256 x 128, three times 256 x 256 (the last with
+    # a single K step), and 64 x 128, which
     # runs only where M > N: a ragged 48-row last tile and a partial K stage;
     # then the skinny strips (M <= 16) with a partial last K stage, and 32 x 32
     # tiles at N = 4096)
     shapes = ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
               (1500, 160, 256), (200, 160, 4096), (450, 96, 4096), (900, 224, 4096), (1800, 96, 4096),
-              (2100, 96, 4096), (4100, 160, 4096), (6000, 96, 256),
+              (2100, 96, 4096), (4100, 160, 4096), (2500, 32, 4096), (6000, 96, 256),
               (3, 96, 4096), (16, 288, 2048), (40, 224, 4096), (70, 160, 4096))
     worst = 0.0
     for (M, K, N) in shapes:
