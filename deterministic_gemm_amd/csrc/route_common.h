@@ -382,20 +382,45 @@ __device__ __forceinline__ uint32_t lane_or(const uint32_t (&a)[N]) {
   return t[0];
 }
 
-// Selection, weights and margin for four tokens per wavefront, one per row of
-// 16 lanes: the same results as route_token, with a token's rank rounds run by
-// 16 lanes instead of 64 so that four tokens' rounds proceed together.  Lane q
-// of row r holds in v the selection values of experts q*V .. q*V+V-1 of token
-// m (bf16-rounded already in bf16-logit mode); rp is the row's LDS scratch of
-// at least 68 floats: [0, 33) the winning ids by rank, [33, 66) their keys
-// (then their weights), 66 and 67 the exact values at ranks k-1 and k.  Rows
-// with live == false compute but store nothing.  Needs k <= 32.
-template <int E>
-__device__ void route_select_row16(const float (&v)[E / 16], float *rp, int64_t m, bool live,
-                                   const EpilogueArgs &a) {
-  constexpr int V = E / 16;
+// Maximum / pairwise tree sum over each half of 32 lanes, returned in every
+// lane of the half: the 16-lane step, then v_permlane16_swap of the value with
+// itself, which hands each lane of rows (0, 1) both rows' values as (row 0,
+// row 1), likewise rows (2, 3) -- the tree's next level, lower lanes left.
+__device__ __forceinline__ uint32_t row_max32(uint32_t x) {
+  x = row_max16(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1]));
+}
+
+__device__ __forceinline__ float row_tree_sum32(float s) {
+  s = row_tree_sum16(s);
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, s), __builtin_bit_cast(uint32_t, s),
+                                                  false, false);
+  return __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) + __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
+}
+
+// Selection, weights and margin for 64/LT tokens per wavefront, one per group
+// of LT = 16 or 32 lanes: the same results as route_token, with a token's
+// rank rounds run by LT lanes instead of 64 so that several tokens' rounds
+// proceed together.  Lane q of a group holds in v the selection values of
+// experts q*V .. q*V+V-1 (V = E/LT) of token m (bf16-rounded already in
+// bf16-logit mode); the lane-local tree over V terms and the tree over the
+// LT lanes together are the canonical tree over the E terms in index order
+// for either LT.  rp is the group's LDS scratch of at least 68 floats:
+// [0, 33) the winning ids by rank, [33, 66) their keys (then their weights),
+// 66 and 67 the exact values at ranks k-1 and k.  Groups with live == false
+// compute but store nothing.  Needs k <= 32.  Thirty-two lanes per token
+// give twice the wavefronts of sixteen for the same tokens, to hide more of
+// each round's dependent steps.
+template <int E, int LT>
+__device__ void route_select_rows(const float (&v)[E / LT], float *rp, int64_t m, bool live,
+                                  const EpilogueArgs &a) {
+  static_assert(LT == 16 || LT == 32, "lanes per token");
+  constexpr int V = E / LT;
   const int lane = threadIdx.x & 63;
-  const int q = lane & 15;
+  const int q = lane & (LT - 1);
+  const auto group_max = [](uint32_t x) { return LT == 16 ? row_max16(x) : row_max32(x); };
+  const auto group_sum = [](float x) { return LT == 16 ? row_tree_sum16(x) : row_tree_sum32(x); };
   const int k = a.k;
 
   uint32_t key[V];
@@ -403,11 +428,11 @@ __device__ void route_select_row16(const float (&v)[E / 16], float *rp, int64_t 
   for (int j = 0; j < V; ++j) key[j] = rank_key(v[j]) + 1u;
 
   uint32_t lm = lane_max<V>(key);
-  const uint32_t top = row_max16(lm);
+  const uint32_t top = group_max(lm);
   const float mx = key_value(top);
 
   // softmax denominator: the canonical tree over the E terms in index order
-  // is the tree over each lane's V consecutive terms, then over the 16 lanes
+  // is the tree over each lane's V consecutive terms, then over the LT lanes
   float s = 0.0f;
   if (a.weights) {
     float u[V];
@@ -418,7 +443,7 @@ __device__ void route_select_row16(const float (&v)[E / 16], float *rp, int64_t 
 #pragma unroll
       for (int i = 0; i < w / 2; ++i) u[i] = u[2 * i] + u[2 * i + 1];
     }
-    s = row_tree_sum16(u[0]);
+    s = group_sum(u[0]);
   }
 
   const int rounds = (k < E) ? k + 1 : k;
@@ -426,12 +451,12 @@ __device__ void route_select_row16(const float (&v)[E / 16], float *rp, int64_t 
   for (int r = 0; r < rounds; ++r) {
     if (r > 0) {
       lm = lane_max<V>(key);
-      rm = row_max16(lm);
+      rm = group_max(lm);
     }
-    // the row's lowest lane holding the maximum, then its lowest slot: the
-    // slots equal to the maximum as a bit mask, its lowest set bit
+    // the group's lowest lane holding the maximum, then its lowest slot:
+    // the slots equal to the maximum as a bit mask, its lowest set bit
     const uint64_t bal = __builtin_amdgcn_ballot_w64(lm == rm);
-    const uint32_t bits = static_cast<uint32_t>(bal >> (lane & 48)) & 0xFFFFu;
+    const uint32_t bits = static_cast<uint32_t>(bal >> (lane & (64 - LT))) & static_cast<uint32_t>((1ull << LT) - 1);
     const bool win = q == static_cast<int>(__builtin_ctz(bits));
     uint32_t hit[V];
 #pragma unroll
@@ -452,17 +477,17 @@ __device__ void route_select_row16(const float (&v)[E / 16], float *rp, int64_t 
   }
 
   if (!live) return;
-  // ranks j = q, q + 16, ... of the row's token
-  for (int j = q; j < k; j += 16) a.ids[m * k + j] = __builtin_bit_cast(int32_t, rp[j]);
+  // ranks j = q, q + LT, ... of the group's token
+  for (int j = q; j < k; j += LT) a.ids[m * k + j] = __builtin_bit_cast(int32_t, rp[j]);
   if (a.weights) {
-    for (int j = q; j < k; j += 16)
+    for (int j = q; j < k; j += LT)
       rp[33 + j] = route_exp(key_value(__builtin_bit_cast(uint32_t, rp[33 + j])) - mx) / s;
     if (a.flags & DR_ROUTE_RENORMALIZE) {
       float rs = rp[33];
       for (int j = 1; j < k; ++j) rs = rs + rp[33 + j];
-      for (int j = q; j < k; j += 16) a.weights[m * k + j] = rp[33 + j] / rs;
+      for (int j = q; j < k; j += LT) a.weights[m * k + j] = rp[33 + j] / rs;
     } else {
-      for (int j = q; j < k; j += 16) a.weights[m * k + j] = rp[33 + j];
+      for (int j = q; j < k; j += LT) a.weights[m * k + j] = rp[33 + j];
     }
   }
   if (a.margins && q == 0) {
@@ -527,7 +552,7 @@ __device__ void route_tokens_row16(float *lg, int pitch, int64_t m0, int64_t M, 
       for (int j4 = 0; j4 < V / 4; ++j4) o[j4] = make_float4(v[4 * j4], v[4 * j4 + 1], v[4 * j4 + 2], v[4 * j4 + 3]);
     }
   }
-  route_select_row16<E>(v, rp, m, live, a);
+  route_select_rows<E, 16>(v, rp, m, live, a);
 }
 
 }  // namespace drk
