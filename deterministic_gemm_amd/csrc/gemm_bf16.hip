@@ -25,12 +25,11 @@
 // gets column c0 + i at rows k0 .. k0+3; two such reads give the eight k.
 // Tiles of 128 columns or more keep W in LDS in 128-byte blocks of four K rows
 // by 16 columns, so each 16-lane group of a transpose read takes one whole
-// block and each 32-lane half of the instruction 256 contiguous bytes, all 64
-// banks once.  (In a microbenchmark, the same reads from row-major [k][n]
-// stages, four rows 512 bytes apart per group, ran at 55-75% of that rate.)
-// Each transfer lane fetches the 16-byte unit that its LDS position holds, so
-// global reads stay runs of 256 bytes per row.  Narrower tiles keep [k][n]
-// rows with XOR-swizzled units.
+// 128-byte block instead of four 32-byte pieces of rows 2N bytes apart (the
+// GEMM gained 1-5% at M = 512-4096, K = N = 4096).  Each transfer lane
+// fetches the 16-byte unit that its LDS position holds, so global reads stay
+// runs of 256 bytes per row.  Narrower tiles keep [k][n] rows with
+// XOR-swizzled units.
 #include <type_traits>
 #include <utility>
 
@@ -81,9 +80,9 @@ struct GemmCfg {
   __host__ __device__ static constexpr int swa(int r) { return UA >= 16 ? r % 16 : (r / (16 / UA)) % UA; }
   // W, tiles of 128 columns or more (QB): rows 4q .. 4q+3 by columns
   // 16b .. 16b+15 form a 128-byte block, row-major, at block
-  // q * NB + (b ^ ((q >> 1) & 1)).  The xor puts the blocks of groups g and
-  // g+1 of a read (q two apart) 128 bytes apart modulo 256, so the two
-  // halves of each 256-byte pass use distinct banks.  Narrower tiles keep W
+  // q * NB + (b ^ ((q >> 1) & 1)).  The xor puts the blocks that groups g
+  // and g+1 of one read take (q two apart) on alternate 128-byte halves of
+  // each 256 bytes, as a contiguous 512-byte read would be.  Narrower tiles keep W
   // row-major ([k][n], unit u of row k at u ^ swb(k)): their transfers then
   // read whole 64- or 128-byte row pieces with consecutive lanes, where the
   // blocks would alternate rows every two lanes (measured 7% slower at
