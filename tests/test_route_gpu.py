@@ -201,6 +201,28 @@ def test_every_supported_e(dr, Ex, kx):
         assert_route_equal(got, ref, what=f"E={Ex} k={kx} {variant}")
 
 
+@pytest.mark.parametrize("Ex,kx,mode", [(256, 1, "f32"), (256, 32, "f32"), (256, 8, "bf16_logits"),
+                                         (512, 10, "renormalize"), (512, 32, "bf16_logits"), (128, 5, "f32")])
+def test_large_batch_selection(dr, Ex, kx, mode):
+    """Batches above 1024 tokens select with two tokens per wavefront (32
+    lanes each; 16 lanes per token below 256 experts): k from 1 to 32, both
+    logit modes and renormalisation, against the oracle, at a batch that is
+    not a multiple of a workgroup's 8 (or 16) tokens."""
+    rng = np.random.default_rng(Ex * 100 + kx)
+    Kx, M = 256, 1100
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    x = rng.standard_normal((M, Kx)).astype(np.float32)
+    x[5] = 0.0  # every logit +0: all ties, lowest indices win
+    kw = {"logit_dtype": "bf16"} if mode == "bf16_logits" else ({"renormalize": True} if mode == "renormalize" else {})
+    ref = oracle_route(x, W, kx, logits_bf16=(mode == "bf16_logits"), renormalize=(mode == "renormalize"))
+    for variant in ("auto", "split", "narrow"):
+        if variant == "split" and Ex not in (256, 512):
+            continue
+        note(f"large-batch selection E={Ex} k={kx} {mode} {variant}")
+        got = gpu_route_np(dr, dev(x), dev(W), kx, variant=variant, **kw)
+        assert_route_equal(got, ref, what=f"E={Ex} k={kx} {mode} {variant}")
+
+
 @pytest.mark.parametrize("mode", ["bf16_logits", "renormalize"])
 def test_modes(dr, router_w, sweep, mode):
     x, _ = sweep
