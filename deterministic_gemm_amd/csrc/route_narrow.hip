@@ -306,7 +306,9 @@ static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t slots = 2 * static_cast<int64_t>(device_cus());
   const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
   if (wgs(16, 16) <= slots) {
-    if (G == 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2, XB>>(L);
+    // three groups take four parts too (the fourth empty): with two, one
+    // part runs two groups in sequence (K = 3072, E = 256, M = 100: 30 us)
+    if (G >= 3) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2, XB>>(L);
     return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4, XB>>(L);
   }
   if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, 16, 3, XB>>(L);
