@@ -318,12 +318,16 @@ static hipError_t launch_narrow_e(const RouteLaunch &L) {
 // The largest batch the narrow family takes before the split kernels: at
 // 1024 < K <= 4096 with E in {256, 512}, as long as its 32 x 32 tiles fit on
 // the CUs at once (M = 2048 at E = 256, 1024 at E = 512 on 256 CUs; measured
-// crossovers at K = 2048 and 4096); otherwise 1280, measured at K = 2048, E =
-// 256 with 16 x 16 tiles.
+// crossovers at K = 2048 and 4096); 2048 for one K-group at E = 256;
+// otherwise 1280, measured at K = 2048, E = 256 with 16 x 16 tiles.
 int64_t narrow_max_m(int64_t E, int64_t K) {
   const int64_t nb = (K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
   if (G >= 2 && G <= 4 && (E == 256 || E == 512)) return 2 * static_cast<int64_t>(device_cus()) * 32 / (E / 32);
+  // one K-group at E = 256: the two-kernel family cannot split K into parts
+  // there and runs a few dozen workgroups (K = 768 and 1024: 45-48 us for
+  // M = 1300-2000 against 32-33 with the 16 x 16 tiles; level from ~2300)
+  if (G == 1 && E == 256) return 2048;
   return 1280;
 }
 

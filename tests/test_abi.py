@@ -227,7 +227,8 @@ def test_auto_variant_is_a_function_of_shape(L):
     assert [dr.auto_variant(M, 2048, 512) for M in (1024, 1025)] == ["narrow", "split"]
     assert [dr.auto_variant(M, 4096, 512) for M in (240, 1024, 1025)] == ["narrow", "narrow", "split"]
     assert [dr.auto_variant(M, 8192, 256) for M in (1280, 1281)] == ["narrow", "split"]
-    assert [dr.auto_variant(M, 1024, 256) for M in (1280, 1281)] == ["narrow", "split"]
+    assert [dr.auto_variant(M, 1024, 256) for M in (2048, 2049)] == ["narrow", "split"]
+    assert [dr.auto_variant(M, 1024, 512) for M in (1280, 1281)] == ["narrow", "split"]
     assert dr.auto_variant(8192, 2048, 256, logits=False) == "tiled"
     assert dr.auto_variant(8192, 2048, 256, x_dtype="bf16") == "split"  # bf16 x staged as it is
     assert dr.auto_variant(8192, 8192, 256, x_dtype="bf16") == "tiled"

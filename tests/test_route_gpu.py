@@ -110,11 +110,11 @@ def test_sweep_forced_variants(dr, router_w, sweep, variant):
 @pytest.mark.parametrize("Kx,Ex,M", [(2048, 256, 600), (2048, 256, 1500), (2048, 256, 2048), (2048, 512, 300),
                                      (2048, 512, 700), (2048, 128, 2000), (2048, 64, 3000), (4096, 512, 240),
                                      (4096, 512, 500), (4096, 512, 1000), (4096, 256, 1000), (3072, 256, 100),
-                                     (3000, 256, 700)])
+                                     (3000, 256, 700), (1024, 256, 2000), (768, 256, 1999)])
 def test_narrow_tiles_match_oracle(dr, Kx, Ex, M):
-    """The narrow family's tiles (16 x 16 with two or four parts, 32 x 16 and
-    32 x 32 tokens x experts, picked by how many workgroups fit on the CUs),
-    each with a ragged last token tile, at two, three and four K-groups: every
+    """The narrow family's tiles (16 x 16 with one, two or four parts, 32 x 16
+    and 32 x 32 tokens x experts, picked by how many workgroups fit on the
+    CUs), each with a ragged last token tile, at one to four K-groups: every
     output equals the oracle's, and the split family's where it exists."""
     rng = np.random.default_rng(Kx + Ex)
     W = wl.router_weights(Kx, Ex) if Ex == E else (rng.standard_normal((Kx, Ex)) * 0.02).astype(np.float32)
