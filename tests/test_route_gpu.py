@@ -182,6 +182,26 @@ def test_ragged_k_split(dr, Kx):
         assert_route_equal(got, ref, what=f"K={Kx} {variant}")
 
 
+@pytest.mark.parametrize("Kx", [8, 256, 264, 1000, 2048, 3080, 4096])
+@pytest.mark.parametrize("Ex", [64, 256, 512, 1024])
+def test_tiny_few_tokens(dr, Kx, Ex):
+    """A few tokens in the vector-ALU family, which spreads W over sixteen
+    K-block slots (the slots past the last block hold -0) while its
+    workgroups fill at most half the CUs, and uses the fewest slots above
+    that: 1 to 16 K-blocks, 1 to 8 tokens, fp32 and bf16 x, against the
+    oracle."""
+    rng = np.random.default_rng(Kx * 7 + Ex)
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    xb = torch.from_numpy(rng.standard_normal((8, Kx)).astype(np.float32)).to(torch.bfloat16)
+    x = xb.float().numpy()  # bf16-valued, so both storages hold the same values
+    ref = oracle_route(x, W, 8)
+    for M in (1, 3, 8):
+        for xd, name in ((dev(x[:M]), "f32"), (xb[:M].contiguous().cuda(), "bf16")):
+            note(f"tiny K={Kx} E={Ex} M={M} x {name}")
+            got = gpu_route_np(dr, xd, dev(W), 8, variant="tiny")
+            assert_route_equal(got, tuple(r[:M] for r in ref), what=f"tiny K={Kx} E={Ex} M={M} x {name}")
+
+
 @pytest.mark.parametrize("Ex,kx", [(64, 1), (64, 32), (128, 5), (256, 32), (512, 10), (1024, 8), (1024, 32)])
 def test_every_supported_e(dr, Ex, kx):
     rng = np.random.default_rng(Ex + kx)
