@@ -400,9 +400,10 @@ __device__ __forceinline__ float row_tree_sum32(float s) {
 }
 
 // Selection, weights and margin for 64/LT tokens per wavefront, one per group
-// of LT = 16 or 32 lanes: the same results as route_token, with a token's
-// rank rounds run by LT lanes instead of 64 so that several tokens' rounds
-// proceed together.  Lane q of a group holds in v the selection values of
+// of LT = 16, 32 or 64 lanes: the same results as route_token; with 16 or 32
+// lanes several tokens' rank rounds proceed together, and with 64 a round
+// takes a balanced lane maximum and one ballot instead of route_token's
+// per-slot ballots.  Lane q of a group holds in v the selection values of
 // experts q*V .. q*V+V-1 (V = E/LT) of token m (bf16-rounded already in
 // bf16-logit mode); the lane-local tree over V terms and the tree over the
 // LT lanes together are the canonical tree over the E terms in index order
@@ -415,12 +416,21 @@ __device__ __forceinline__ float row_tree_sum32(float s) {
 template <int E, int LT>
 __device__ void route_select_rows(const float (&v)[E / LT], float *rp, int64_t m, bool live,
                                   const EpilogueArgs &a) {
-  static_assert(LT == 16 || LT == 32, "lanes per token");
+  static_assert(LT == 16 || LT == 32 || LT == 64, "lanes per token");
   constexpr int V = E / LT;
   const int lane = threadIdx.x & 63;
   const int q = lane & (LT - 1);
-  const auto group_max = [](uint32_t x) { return LT == 16 ? row_max16(x) : row_max32(x); };
-  const auto group_sum = [](float x) { return LT == 16 ? row_tree_sum16(x) : row_tree_sum32(x); };
+  const auto group_max = [](uint32_t x) -> uint32_t {
+    if constexpr (LT == 16) return row_max16(x);
+    if constexpr (LT == 32) return row_max32(x);
+    x = row_max32(x);
+    return max(static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 0)), static_cast<uint32_t>(__builtin_amdgcn_readlane(x, 32)));
+  };
+  const auto group_sum = [](float x) -> float {
+    if constexpr (LT == 16) return row_tree_sum16(x);
+    if constexpr (LT == 32) return row_tree_sum32(x);
+    return wave_tree_sum(x);
+  };
   const int k = a.k;
 
   uint32_t key[V];
@@ -456,8 +466,13 @@ __device__ void route_select_rows(const float (&v)[E / LT], float *rp, int64_t m
     // the group's lowest lane holding the maximum, then its lowest slot:
     // the slots equal to the maximum as a bit mask, its lowest set bit
     const uint64_t bal = __builtin_amdgcn_ballot_w64(lm == rm);
-    const uint32_t bits = static_cast<uint32_t>(bal >> (lane & (64 - LT))) & static_cast<uint32_t>((1ull << LT) - 1);
-    const bool win = q == static_cast<int>(__builtin_ctz(bits));
+    bool win;
+    if constexpr (LT == 64) {
+      win = lane == static_cast<int>(__builtin_ctzll(bal));
+    } else {
+      const uint32_t bits = static_cast<uint32_t>(bal >> (lane & (64 - LT))) & static_cast<uint32_t>((1ull << LT) - 1);
+      win = q == static_cast<int>(__builtin_ctz(bits));
+    }
     uint32_t hit[V];
 #pragma unroll
     for (int j = 0; j < V; ++j) hit[j] = (key[j] == rm) ? (1u << j) : 0u;

@@ -492,11 +492,14 @@ __global__ __launch_bounds__(256) void route_split_epilogue32_kernel(int64_t M, 
   route_select_rows<E, 32>(v, scr[slot], m, live, ea);
 }
 
-// Small batches: one wavefront per token (the row-wise kernel's epilogue),
-// which finishes a token in fewer dependent steps than four tokens sharing a
-// wavefront; four tokens per workgroup.  The token's logits are widened into
-// an LDS row first; the epilogue then sees the values as given and writes no
-// logits.
+// Small batches: one wavefront per token, which finishes a token in fewer
+// dependent steps than several tokens sharing a wavefront; four tokens per
+// workgroup.  The token's logits are widened into an LDS row first; the
+// selection then sees the values as given and writes no logits.  Up to 256
+// experts (four values per lane) the row-wise kernel's per-slot ballots take
+// the fewest steps; from 512, route_select_rows on all 64 lanes (measured,
+// selection alone at E = 512, k = 10: 5.7-6.9 against 6.6-7.6 us for M = 1
+// .. 1024; at E = 256 it was 0.1-0.2 us slower).
 template <int E>
 __global__ __launch_bounds__(256) void route_select_wave_kernel(int64_t M, EpilogueArgs ea) {
   __shared__ __attribute__((aligned(16))) float rows[4][E + 4];
@@ -511,7 +514,15 @@ __global__ __launch_bounds__(256) void route_select_wave_kernel(int64_t M, Epilo
   EpilogueArgs a = ea;
   a.logits = nullptr;
   a.logit_bf16 = 0;
-  route_token<E>(row, m, a);
+  if constexpr (E >= 512) {
+    constexpr int V = E / 64;
+    float v[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) v[j] = row[lane * V + j];
+    route_select_rows<E, 64>(v, row, m, true, a);  // the row becomes the token's scratch
+  } else {
+    route_token<E>(row, m, a);
+  }
 }
 
 template <class C, int MAXL>
