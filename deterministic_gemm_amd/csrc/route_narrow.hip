@@ -28,12 +28,18 @@ namespace drk {
 
 // XB: x holds bf16 bits (K % 8 == 0), staged as they are, 8 values per
 // 16-byte unit, and widened exactly when read; else fp32, 4 per unit.
-template <int E_, int AT_, int BT_, int KG_, int KC_, int S_, bool XB_ = false>
+// TX = 8 (with AT = 1): a workgroup takes 8 tokens, staged as 8 rows; the
+// matrix steps' rows 8 .. 15 read a 16-byte zero unit at the end of the
+// wavefront's ring, so their chains only ever add fmaf(+0, w, .) and are
+// never stored.  Twice the workgroups for the same batch, each staging a
+// quarter fewer bytes.
+template <int E_, int AT_, int BT_, int KG_, int KC_, int S_, bool XB_ = false, int TX_ = 0>
 struct NarrowCfg {
   static constexpr int E = E_, AT = AT_, BT = BT_, KG = KG_, KC = KC_, S = S_;
   static constexpr bool XB = XB_;
   static constexpr int XV = XB ? 8 : 4;       // x values per 16-byte unit
-  static constexpr int TT = 16 * AT, ET = 16 * BT;  // tokens, experts per workgroup
+  static constexpr int TT = TX_ ? TX_ : 16 * AT, ET = 16 * BT;  // tokens, experts per workgroup
+  static_assert(TT == 16 * AT || (AT == 1 && TT == 8), "token rows");
   static constexpr int NT = 64 * KG;
   static constexpr int NET = E / ET;
   static constexpr int HU = KC / XV;          // 16-byte x units per (slot, token) row
@@ -51,7 +57,8 @@ struct NarrowCfg {
   static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
   static_assert(KC % XV == 0 && 256 % KC == 0, "chunking");
   static_assert(KG == 1 || KG == 2 || KG == 4, "parts");
-  static_assert((KG * S * STG + (KG - 1) * 64 * NQ) * 4 <= 160 * 1024, "LDS");
+  static constexpr int RING = S * STG + (TT < 16 * AT ? 4 : 0);  // floats per wavefront (+ the zero unit)
+  static_assert((KG * RING + (KG - 1) * 64 * NQ) * 4 <= 160 * 1024, "LDS");
   __host__ __device__ static constexpr int swz(int tok) { return (tok * HU / 16) % HU; }
 };
 
@@ -102,7 +109,7 @@ __global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const void *
                                                                     void *logits, int logit_bf16) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, TT = C::TT, S = C::S, KC = C::KC, HU = C::HU;
   constexpr int NQ = C::NQ;
-  __shared__ __attribute__((aligned(16))) float ring[C::KG * S * C::STG];
+  __shared__ __attribute__((aligned(16))) float ring[C::KG * C::RING];
   __shared__ __attribute__((aligned(16))) float parts[C::KG > 1 ? (C::KG - 1) * 64 * NQ : 4];
 
   const int64_t bid = blockIdx.x;
@@ -119,7 +126,12 @@ __global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const void *
   const int g0 = min(G, wave * span), g1 = min(G, (wave + 1) * span);
   const int ng = g1 - g0;
   const int nch = ng * C::CPG;
-  float *my = ring + wave * S * C::STG;
+  float *my = ring + wave * C::RING;
+  // rows of the matrix tile past the staged tokens read this zero unit
+  [[maybe_unused]] const float *zero = my + S * C::STG;
+  if constexpr (TT < 16 * AT) {
+    if (lane < 4) my[S * C::STG + lane] = 0.0f;
+  }
 
   f32x16 acc[AT][BT];
   float stk[MAXL][NQ];
@@ -159,11 +171,15 @@ __global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const void *
       for (int a = 0; a < AT; ++a) {
         const int tok = a * 16 + r_l;
         if constexpr (C::XB) {
-          if ((c4 & 1) == 0)
-            ux[(c4 >> 1) & 1][a] =
-                *reinterpret_cast<const uint4 *>(xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
+          if ((c4 & 1) == 0) {
+            const float *src = xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4;
+            if constexpr (TT < 16 * AT) src = tok < TT ? src : zero;
+            ux[(c4 >> 1) & 1][a] = *reinterpret_cast<const uint4 *>(src);
+          }
         } else {
-          av[r][a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+          const float *src = xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4;
+          if constexpr (TT < 16 * AT) src = tok < TT ? src : zero;
+          av[r][a] = *reinterpret_cast<const float4 *>(src);
         }
       }
 #pragma unroll
@@ -253,7 +269,7 @@ __global__ __launch_bounds__(C::NT) void route_narrow_logits_kernel(const void *
       for (int q = 0; q < 4; ++q) {
         const int64_t m = m0 + a * 16 + 4 * s_l + q;
         const float val = part[(a * BT + b) * 4 + q];
-        if (m < M) {
+        if (m < M && a * 16 + 4 * s_l + q < TT) {
           const int64_t idx = m * C::E + e0 + b * 16 + r_l;
           if (logit_bf16) static_cast<uint16_t *>(logits)[idx] = f32_to_bf16(val);
           else static_cast<float *>(logits)[idx] = val;
@@ -301,10 +317,16 @@ template <int E, bool XB>
 static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
   const int64_t G = (nb + 3) / 4;
+  const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
+  // 8 x 16 tiles while their workgroups all fit on the CUs at once
+  if (G <= 4 && wgs(8, 16) <= device_cus()) {
+    if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4, XB, 8>>(L);
+    if (G == 2) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4, XB, 8>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4, XB, 8>>(L);
+  }
   if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4, XB>>(L);
   if (G > 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4, XB>>(L);
   const int64_t slots = 2 * static_cast<int64_t>(device_cus());
-  const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
   if (wgs(16, 16) <= slots) {
     // three groups take four parts too (the fourth empty): with two, one
     // part runs two groups in sequence (K = 3072, E = 256, M = 100: 30 us)

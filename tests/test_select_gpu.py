@@ -51,10 +51,12 @@ def _special_logits(rng, M, E):
 
 
 @pytest.mark.parametrize("E,k,M", [(64, 1, 90), (64, 32, 90), (128, 8, 90), (256, 8, 90), (256, 32, 90),
-                                   (512, 10, 90), (1024, 8, 90), (256, 8, 1100), (64, 32, 1100), (512, 10, 1100)])
+                                   (512, 10, 90), (1024, 8, 90), (256, 8, 1100), (64, 32, 1100), (512, 10, 1100),
+                                   (512, 1, 90), (512, 32, 90), (1024, 32, 90)])
 def test_route_select_matches_oracle(dr, E, k, M):
-    """One wavefront per token (M <= 1024, and E = 1024) and four tokens per
-    wavefront (larger M) against the oracle."""
+    """One wavefront per token (M <= 1024, and E = 1024; from 512 experts the
+    64-lane rounds, at k = 1, 10 and 32) and several tokens per wavefront
+    (larger M) against the oracle."""
     rng = np.random.default_rng(7 * E + k + M)
     lg = _special_logits(rng, M, E)
     for renorm in (False, True):
