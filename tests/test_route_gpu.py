@@ -182,6 +182,24 @@ def test_ragged_k_split(dr, Kx):
         assert_route_equal(got, ref, what=f"K={Kx} {variant}")
 
 
+@pytest.mark.parametrize("Kx,Ex,M", [(2048, 256, 65), (2048, 256, 200), (2048, 256, 700), (2048, 256, 1500),
+                                     (3072, 256, 100), (264, 256, 130), (2048, 512, 60), (4096, 512, 240)])
+def test_narrow_tiles_bf16_x(dr, Kx, Ex, M):
+    """The narrow family on bf16 x staged as it is (8 values per 16-byte
+    unit, widened when read) and on the same values as fp32, across its tile
+    shapes -- 8 staged token rows, 16 x 16, 32 x 16 and 32 x 32 -- with one to
+    four K-groups and a ragged K, against the oracle."""
+    rng = np.random.default_rng(Kx * 3 + Ex + M)
+    W = (rng.standard_normal((Kx, Ex)) * 0.05).astype(np.float32)
+    xb = torch.from_numpy(rng.standard_normal((M, Kx)).astype(np.float32)).to(torch.bfloat16)
+    x = xb.float().numpy()
+    ref = oracle_route(x, W, 8)
+    for xd, name in ((xb.cuda(), "bf16"), (dev(x), "f32")):
+        note(f"narrow K={Kx} E={Ex} M={M} x {name}")
+        got = gpu_route_np(dr, xd, dev(W), 8, variant="narrow")
+        assert_route_equal(got, ref, what=f"narrow K={Kx} E={Ex} M={M} x {name}")
+
+
 @pytest.mark.parametrize("Kx", [8, 256, 264, 1000, 2048, 3080, 4096])
 @pytest.mark.parametrize("Ex", [64, 256, 512, 1024])
 def test_tiny_few_tokens(dr, Kx, Ex):
