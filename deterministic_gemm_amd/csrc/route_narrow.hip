@@ -312,6 +312,13 @@ static hipError_t launch_narrow_c(const RouteLaunch &L) {
 // 24 us (16 x 16 tiles: 30), 2048 38 us (the split kernels: 44); K = 4096, E =
 // 512: M = 240 22 us (four parts with four stages: 31), 512 40 us (59), 1024
 // 65 us (115).  More groups keep one part per group and four stages.
+// bf16 x (8 values per 16-byte unit) takes chunks twice as long where LDS
+// allows -- 32 steps on the 8-row and 16 x 16 tiles (three stages where two
+// workgroups share a CU), 32 steps in two stages on 32 x 16, 16 in three on
+// 32 x 32 -- so that a token's row piece of a chunk is 64 bytes, as with fp32
+// x.  Whole call, K = 2048, E = 256, bf16 x: M = 300-500 17.3-18.1 against
+// 23.3-23.9 us, 600 23.3-24.3 against 35.2-36.9, 1024 26.3-27.0 against
+// 37.2-37.7 (fp32 x: 29.4), 2048 36.5-37.2 against 40.4-40.8.
 template <int E, bool XB>
 static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
@@ -319,21 +326,21 @@ static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
   // 8 x 16 tiles while their workgroups all fit on the CUs at once
   if (G <= 4 && wgs(8, 16) <= device_cus()) {
-    if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4, XB, 8>>(L);
-    if (G == 2) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4, XB, 8>>(L);
-    return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4, XB, 8>>(L);
+    if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, XB ? 32 : 16, 4, XB, 8>>(L);
+    if (G == 2) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, XB ? 32 : 16, 4, XB, 8>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 4, XB ? 32 : 16, XB ? 3 : 4, XB, 8>>(L);
   }
-  if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 16, 4, XB>>(L);
+  if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, XB ? 32 : 16, 4, XB>>(L);
   if (G > 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4, XB>>(L);
   const int64_t slots = 2 * static_cast<int64_t>(device_cus());
   if (wgs(16, 16) <= slots) {
     // three groups take four parts too (the fourth empty): with two, one
     // part runs two groups in sequence (K = 3072, E = 256, M = 100: 30 us)
     if (G >= 3) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2, XB>>(L);
-    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 16, 4, XB>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, XB ? 32 : 16, XB ? 3 : 4, XB>>(L);
   }
-  if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, 16, 3, XB>>(L);
-  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, 8, 4, XB>>(L);
+  if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, XB ? 32 : 16, XB ? 2 : 3, XB>>(L);
+  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, XB ? 16 : 8, XB ? 3 : 4, XB>>(L);
 }
 
 // The largest batch the narrow family takes before the split kernels: at
