@@ -653,95 +653,241 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
                                  (slot % ncol) * C::BN, smem);
 }
 
-// Skinny batches (M <= 16): every row of the batch in one workgroup, against
-// a 16-column strip of W.  With few rows the product is bound by streaming W
-// (32 MiB at K = N = 4096) from HBM; 16-column strips put a workgroup on every
-// CU (256 at N = 4096) and a ring of eight 16 KiB stages keeps 56 KiB of W in
-// flight per CU.  Four wavefronts share the transfers; wavefront w runs the
-// 16-row fragment w (the configuration allows up to NW of them).  Each output is still reduced by the dense
-// kernel's instruction sequence -- one v_mfma_f32_16x16x32_bf16 per 32-wide K
-// step, k ascending, one accumulator from zero, the same operand placement in
-// the lanes (the same stage layout, swizzles and reads, through gemm_kstep) --
-// so rows are bit-identical to every other tile configuration.
-template <int MR_, int BK_, int S_, int NW_>
-struct SkinnyCfg {
-  static constexpr int BM = MR_, BN = 16, BK = BK_, S = S_, NW = NW_, NT = 64 * NW;
-  static constexpr int TM = 16, TN = 16, FM = 1, FN = 1;  // one 16x16 fragment per computing wavefront
-  static constexpr int FMT = MR_ / 16;                    // computing wavefronts
-  static constexpr int UA = BK / 8, UB = 2;
-  static constexpr int AU = BM * UA, BU = BK * UB;
-  static constexpr int ABYTES = AU * 16, STAGE = (AU + BU) * 16;
-  static constexpr int PER = (AU + BU) / 64 / NW;
-  static_assert(MR_ % 16 == 0 && FMT <= NW, "a wavefront per row fragment");
-  static_assert(BK % 32 == 0 && (UA == 16 || UA == 32), "K steps per stage");
-  static_assert(AU % 64 == 0 && BU % 64 == 0 && PER * 64 * NW == AU + BU, "transfers split evenly");
-  static_assert(PER * (S - 1) <= 63 && S >= 2, "vmcnt range");
-  static_assert(S * STAGE <= 160 * 1024, "LDS");
-  __host__ __device__ static constexpr int swa(int r) { return r % 16; }
-  // W: one 16-column strip, [k][16], the two 16-byte units of each row
-  // swapped on alternate groups of 8 rows
+// Small batches (M <= 128): one workgroup per 16-column strip of W, holding
+// every row of the batch.  At these sizes W (32 MiB at K = N = 4096) is read
+// once and every CU also reads all of x (up to 1 MiB) from L2; each path
+// needs many bytes in flight per CU, and one 16-row fragment's accumulator
+// is a chain of K/32 dependent matrix steps.  The operands take separate
+// routes.  NP producer wavefronts only move W into a deep LDS ring (S stages
+// of BK K rows x 16 columns) and count their own transfers.  Each of the NC
+// compute wavefronts owns one 16-row fragment of x: it loads the fragment
+// into registers in chunks of four K steps, R - 1 chunks ahead, 256
+// contiguous bytes per row per chunk (one row per 16 lanes, so each load
+// touches few cache lines), writes each chunk into a private pair of LDS
+// buffers, and reads the matrix core's A operand back from there.  Its loads
+// are the compiler's, so keeping the two kinds of memory operation in
+// different wavefronts keeps each wavefront's in-order wait counter exact
+// for what it waits on.  The W stages are long (BK = 512) so that the
+// workgroup meets at few barriers.  Each output is reduced by the dense
+// kernel's instruction sequence -- one v_mfma_f32_16x16x32_bf16 per 32-wide
+// K step, k ascending, one accumulator from zero, row r16 / column r16 and
+// k = 32t + 8 g4 .. +7 in lane (g4, r16) -- so rows are bit-identical to
+// every other tile configuration.
+template <int NC_, int NP_, int S_, int R_>
+struct StripCfg {
+  static constexpr int NC = NC_, NP = NP_, S = S_, R = R_;
+  static constexpr int BK = 512, KS = BK / 32;  // K rows, 32-wide K steps per W stage
+  static constexpr int CH = 4;                  // K steps per x chunk
+  static constexpr int CPS = KS / CH;           // x chunks per W stage
+  static constexpr int NW = NC + NP, NT = 64 * NW;
+  static constexpr int STAGE = BK * 32;    // bytes of W per stage: BK rows of 16 bf16
+  static constexpr int DI = STAGE / 1024;  // transfers (64 lanes x 16 bytes) per stage
+  static constexpr int PW = DI / NP;       // ... per producer wavefront
+  static constexpr int XB = 16 * CH * 64;  // bytes of one x fragment per chunk
+  static constexpr int XBASE = S * STAGE;  // compute wavefront w's buffers at XBASE + 2 XB w
+  static constexpr int U = R > CPS ? R / CPS : 1;  // W stages per unrolled loop body
+  static constexpr int LDS = XBASE + 2 * XB * NC;
+  static_assert(NC >= 1 && NW <= 16, "wavefronts");
+  static_assert(PW * NP == DI && PW >= 1, "transfers split evenly");
+  static_assert(PW * (S - 2) <= 63 && S >= 3, "vmcnt range");
+  static_assert(R >= 2 && (R % CPS == 0 || CPS % R == 0) && CPS % 2 == 0, "x ring: whole bodies");
+  static_assert(LDS <= 160 * 1024, "LDS");
+  // W in a stage: [k][16], 16-byte unit p (LDS byte 16 p) holds row p / 2,
+  // columns nc .. nc+7; the two units of a row swap on alternate groups of 8
+  // rows, so the transpose reads of one instruction spread over the banks.
   __host__ __device__ static constexpr void b_unit(int p, int &kr, int &nc) {
     kr = p / 2;
     nc = 8 * ((p % 2) ^ ((kr / 8) % 2));
   }
-  __host__ __device__ static constexpr int b_off(int kk, int g4, int c, int tj, int tq, int b) {
-    const int kr = kk * 32 + 8 * g4 + 4 * c + tj, col = b * 16 + 4 * tq;
+  // Byte offset of what lane (g4, tj, tq) of a transpose read takes for K
+  // step kk of the stage, half c: row 32 kk + 8 g4 + 4 c + tj, columns 4 tq .. +3.
+  __host__ __device__ static constexpr int b_off(int kk, int g4, int c, int tj, int tq) {
+    const int kr = kk * 32 + 8 * g4 + 4 * c + tj, col = 4 * tq;
     return (kr * 2 + ((col / 8) ^ ((kr / 8) % 2))) * 16 + (col % 8) * 2;
   }
 };
 
 template <class C, class OutT>
-__global__ __launch_bounds__(C::NT) void gemm_skinny_kernel(const uint16_t *__restrict__ x,
-                                                           const uint16_t *__restrict__ W,
-                                                           OutT *__restrict__ out, int64_t M, int K, int N) {
-  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
-  // XCD j takes the j-th contiguous eighth of the strips (as in the dense
-  // kernel), so the four strips of a 128-byte line of W share one L2
+__global__ __launch_bounds__(C::NT) void gemm_strip_kernel(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ W,
+                                                          OutT *__restrict__ out, int M, int K, int N) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  // XCD j takes the j-th contiguous eighth of the strips, so the four strips
+  // of a 128-byte line of W read it through one L2
   const int nx = gridDim.x;
   const int bx = (nx % 8 == 0) ? (blockIdx.x % 8) * (nx / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int n0 = bx * C::BN;
-  constexpr int S = C::S;
+  const int n0 = bx * 16;
+  constexpr int S = C::S, KS = C::KS, CH = C::CH, CPS = C::CPS, U = C::U, R = C::R;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nk = K / 32;               // K steps
+  const int nst = (nk + KS - 1) / KS;  // W stages
+  const int nch = (nk + CH - 1) / CH;  // x chunks
+
+  if (wave >= C::NC) {
+    // producer: W stages into the ring, S - 1 ahead of the compute wavefronts.
+    // Stages past the last read zeros through an empty range, so every stage
+    // issues the same number of transfers and the wait below stays exact.
+    const int p = wave - C::NC;
+    uint32_t voff[C::PW];
+#pragma unroll
+    for (int i = 0; i < C::PW; ++i) {
+      int kr = 0, nc = 0;
+      C::b_unit((p * C::PW + i) * 64 + lane, kr, nc);
+      voff[i] = static_cast<uint32_t>((static_cast<int64_t>(kr) * N + n0 + nc) * 2);
+    }
+    const auto issue = [&](int st) {
+      const int64_t k0 = static_cast<int64_t>(st) * C::BK;
+      const u32x4 wr = buf_rsrc(W + k0 * N, st < nst ? (K - k0) * static_cast<int64_t>(N) * 2 : 0);
+      char *stage = smem + (st % S) * C::STAGE;
+#pragma unroll
+      for (int i = 0; i < C::PW; ++i) {
+        const uint32_t lds = __builtin_amdgcn_readfirstlane(
+            static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage + (p * C::PW + i) * 1024)));
+        dma16_buf(voff[i], wr, lds);
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i) issue(i);
+    for (int st = 0; st < nst; ++st) {
+      // this wavefront's transfers of stage st are done; after the barrier
+      // all are, and stage st - 1's buffer has been read by everyone
+      compiler_fence();
+      wait_vmcnt<C::PW * (S - 2)>();
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      issue(st + S - 1);
+    }
+    // no transfer may still be writing this workgroup's LDS when it ends
+    compiler_fence();
+    wait_vmcnt<0>();
+    return;
+  }
+
+  // compute wavefront `wave`: rows 16 wave .. +15; rows past M read zeros
+  // through the range of x's descriptor and are not stored.  Loads past the
+  // last K step read the next row's data or zeros and are never consumed, so
+  // whole loop bodies carry no per-step branch (the compiler's waits on the
+  // loads stay counts, not full drains); a ragged remainder runs the same
+  // body with guards.
   const int r16 = lane & 15, g4 = lane >> 4;
   const int ta = lane & 15, tj = ta >> 2, tq = ta & 3;
-  const int nst = (K + C::BK - 1) / C::BK;
-  const bool computes = wave < C::FMT && static_cast<int64_t>(wave) * 16 < M;
-
-  f32x4 acc[1][1];
-  acc[0][0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  int32_t arow[C::PER];
-  gemm_arows<C>(nullptr, M, 0, M, wave, lane, arow);
-  uint32_t voff[C::PER];
-  gemm_voffs<C>(arow, K, N, n0, wave, lane, voff);
-  const auto issue = [&](int st) {
-    gemm_issue_buf<C>(x, M, W, K, N, voff, st, nst, wave, smem + (st % S) * C::STAGE);
-  };
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(x), static_cast<short>(0), M * K * 2, 0x00020000);
+  // load j (0..3) of a chunk: row 4j + lane / 16, bytes 16 (lane % 16) of the
+  // row's 256 for the chunk; written to the fragment buffer [16 rows][16
+  // units] with unit u of row r at u ^ r (the writes and the A reads below
+  // then take distinct banks within each 16 lanes)
+  const int lr = lane >> 4, lu = lane & 15;
+  uint32_t xoff[4];
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i) issue(i);
-  for (int st = 0; st < nst; ++st) {
+  for (int j = 0; j < 4; ++j) {
+    const int row = wave * 16 + 4 * j + lr;
+    xoff[j] = static_cast<uint32_t>(row < M ? (row * K + 8 * lu) * 2 : 0x7FFFFFF0);
+  }
+  char *xl = smem + C::XBASE + wave * 2 * C::XB;
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  u4 xg[R][4];
+  const auto load_chunk = [&](int c, u4(&dst)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dst[j] = __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[j] + c * 256, 0, 0);
+  };
+  const auto write_chunk = [&](const u4(&src)[4], int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + lr;
+      *reinterpret_cast<u4 *>(xl + buf * C::XB + r * 256 + ((lu ^ r) * 16)) = src[j];
+    }
+  };
+  bf16x8 af[CH];
+  const auto read_a = [&](int buf) {
+#pragma unroll
+    for (int kk = 0; kk < CH; ++kk)
+      af[kk] = *reinterpret_cast<const bf16x8 *>(xl + buf * C::XB + r16 * 256 + (((kk * 4 + g4) ^ r16) * 16));
+  };
+  const auto read_b = [&](const char *Bs, int kk) {
+    i16x4 h[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      h[c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4 *)(Bs + C::b_off(kk, g4, c, tj, tq)));
+    return __builtin_bit_cast(bf16x8, (short __attribute__((ext_vector_type(8)))){h[0][0], h[0][1], h[0][2], h[0][3],
+                                                                                  h[1][0], h[1][1], h[1][2], h[1][3]});
+  };
+  const auto sync = [&]() {
+    // this wavefront's LDS reads so far are done before the barrier lets a
+    // producer refill a stage buffer they read
     compiler_fence();
-    wait_vmcnt<C::PER * (S - 2)>();
+    wait_lgkm0();
     __builtin_amdgcn_s_barrier();
     compiler_fence();
-    issue(st + S - 1);
-    const char *As = smem + (st % S) * C::STAGE;
-    const char *Bs = As + C::ABYTES;
-    const int nsub = (K - st * C::BK) < C::BK ? (K - st * C::BK) / 32 : C::BK / 32;
-    if (computes) {
+  };
+  // The operands of chunk c + 1 (W fragments, x chunk written and read back)
+  // are read while chunk c's matrix steps run; the barrier that makes W
+  // stage s + 1 visible comes at the start of stage s's last chunk, whose
+  // fragments are already in registers.  Chunks 0 .. R-2 are in flight
+  // before the loop.
 #pragma unroll
-      for (int kk = 0; kk < C::BK / 32; ++kk)
-        if (kk < nsub) gemm_kstep<C>(As, Bs, kk, wave, 0, r16, g4, tj, tq, acc);
-    }
-  }
-  compiler_fence();
-  wait_vmcnt<0>();
-  if (!computes) return;
+  for (int i = 0; i < R - 1; ++i) load_chunk(i, xg[i]);
+  sync();
+  bf16x8 bc[CH], ac[CH];
+  static_for<CH>([&](auto kc) { bc[decltype(kc)::value] = read_b(smem, decltype(kc)::value); });
+  write_chunk(xg[0], 0);
+  read_a(0);
+#pragma unroll
+  for (int kk = 0; kk < CH; ++kk) ac[kk] = af[kk];
+  f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // U W stages; st0 is a multiple of U, so chunk c = st * CPS + cs has
+  // c % R == (su * CPS + cs) % R and c % 2 == cs % 2.  Reads for a chunk
+  // past the last are left unguarded in whole bodies (in-bounds LDS, never
+  // consumed).
+  const auto body = [&](int st0, auto guarded) {
+    constexpr bool G = decltype(guarded)::value;
+    static_for<U>([&](auto uc) {
+      constexpr int su = decltype(uc)::value;
+      const int st = st0 + su;
+      if (!G || st < nst) {
+        static_for<CPS>([&](auto ccs) {
+          constexpr int cs = decltype(ccs)::value;
+          constexpr int cl = su * CPS + cs;  // chunk within the body
+          const int c = st * CPS + cs;
+          if (!G || c < nch) {
+            constexpr bool last = cs == CPS - 1;  // chunk c + 1 is in the next stage
+            if (last && st + 1 < nst) sync();
+            bf16x8 bn[CH];
+            if (!G || c + 1 < nch) {
+              const char *Bn = smem + ((last ? st + 1 : st) % S) * C::STAGE;
+              static_for<CH>([&](auto kc) {
+                constexpr int kk = decltype(kc)::value;
+                bn[kk] = read_b(Bn, ((cs + 1) % CPS) * CH + kk);
+              });
+              write_chunk(xg[(cl + 1) % R], (cs + 1) % 2);
+              read_a((cs + 1) % 2);
+            }
+            // chunk c + R - 1 into the registers chunk c - 1 freed
+            if (!G || c + R - 1 < nch) load_chunk(c + R - 1, xg[(cl + R - 1) % R]);
+            static_for<CH>([&](auto kc) {
+              constexpr int kk = decltype(kc)::value;
+              if (!G || c * CH + kk < nk) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ac[kk], bc[kk], acc, 0, 0, 0);
+            });
+#pragma unroll
+            for (int kk = 0; kk < CH; ++kk) {
+              bc[kk] = bn[kk];
+              ac[kk] = af[kk];
+            }
+          }
+        });
+      }
+    });
+  };
+  const int nfull = nk / (U * KS);
+  for (int b = 0; b < nfull; ++b) body(b * U, std::false_type{});
+  if (nfull * U * KS < nk) body(nfull * U, std::true_type{});
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int64_t m = wave * 16 + g4 * 4 + q;
+    const int m = wave * 16 + g4 * 4 + q;
     if (m >= M) continue;
-    if constexpr (sizeof(OutT) == 2) out[m * N + n0 + r16] = gemm_f32_to_bf16(acc[0][0][q]);
-    else out[m * N + n0 + r16] = acc[0][0][q];
+    if constexpr (sizeof(OutT) == 2) out[static_cast<int64_t>(m) * N + n0 + r16] = gemm_f32_to_bf16(acc[q]);
+    else out[static_cast<int64_t>(m) * N + n0 + r16] = acc[q];
   }
 }
 
@@ -787,12 +933,35 @@ static hipError_t launch_gemm_c(const uint16_t *x, const uint16_t *W, OutT *out,
   return hipGetLastError();
 }
 
-template <class C, class OutT>
-static hipError_t launch_skinny_c(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
+template <int NC, class OutT>
+static hipError_t launch_strip_nc(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
                                   hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<C, OutT>), dim3(static_cast<uint32_t>(N / C::BN)), dim3(C::NT), 0, stream,
-                     x, W, out, M, static_cast<int>(K), static_cast<int>(N));
+  constexpr int S = NC <= 4 ? 8 : (160 * 1024 - NC * 8192) / 16384;
+  using C = StripCfg<NC, 2, S, NC + 2 <= 8 ? 8 : 4>;
+  hipLaunchKernelGGL((gemm_strip_kernel<C, OutT>), dim3(static_cast<uint32_t>(N / 16)), dim3(C::NT), 0, stream, x,
+                     W, out, static_cast<int>(M), static_cast<int>(K), static_cast<int>(N));
   return hipGetLastError();
+}
+
+// Batches of 1 .. 128 rows: one compute wavefront per 16-row fragment.
+constexpr int64_t kStripMaxM = 128;
+static bool strip_ok(int64_t M, int64_t K, int64_t N) {
+  return M >= 1 && M <= kStripMaxM && M * K * 2 < 0x7FFFFFF0LL && gemm_buf_ok(M, K, N);
+}
+
+template <class OutT>
+static hipError_t launch_strip(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
+                               hipStream_t stream) {
+  switch ((M + 15) / 16) {
+    case 1: return launch_strip_nc<1, OutT>(x, W, out, M, K, N, stream);
+    case 2: return launch_strip_nc<2, OutT>(x, W, out, M, K, N, stream);
+    case 3: return launch_strip_nc<3, OutT>(x, W, out, M, K, N, stream);
+    case 4: return launch_strip_nc<4, OutT>(x, W, out, M, K, N, stream);
+    case 5: return launch_strip_nc<5, OutT>(x, W, out, M, K, N, stream);
+    case 6: return launch_strip_nc<6, OutT>(x, W, out, M, K, N, stream);
+    case 7: return launch_strip_nc<7, OutT>(x, W, out, M, K, N, stream);
+    default: return launch_strip_nc<8, OutT>(x, W, out, M, K, N, stream);
+  }
 }
 
 template <class C>
@@ -841,22 +1010,21 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
 // = 4096, N = 256..14336): within ~1 us or 2% everywhere; e.g. K = N = 4096:
 // M = 256 38 us, 512 43, 1024 56, 2048 90, 3072 124, 4096 142; K = 2048, N =
 // 256: M = 1024 13 us, 8192 25.
-// Measured at K = N = 4096 (graph replay): 13.2 us at M = 1 and 14.3 at M =
-// 16 against 14.5-15 for 32 x 32 tiles; with 32, 64 or 80 rows per strip it
-// lost (16.1-16.5 us at M = 19-32, 19-20.7 at M = 33-80, against 15.0 and
-// 18.3-18.5): the bytes in flight are not what caps these batches.
-constexpr int64_t kSkinnyMaxM = 16;
-
+// Small batches take the strip kernel (one 16-column strip of W with all
+// the rows per workgroup) while its strips cover at least half the CUs and
+// it measured faster: K = N = 4096, kernel time under a trace, M = 1 11.3
+// us and M = 16 13.3 against 13.3 and 14.2 for 16-row strips of the dense
+// stage layout; M = 112 and 128 20.7-21.3 against 22.2-22.6 for 32 x 32
+// tiles.  From 17 to 96 rows the 32 x 32 tiles win (14.4-17.2 against
+// 14.1-21.2 us): every strip reads all of x from L2, and at those sizes that
+// broadcast, not W, sets the time.
 template <class OutT>
 static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *out, int64_t M, int64_t K, int64_t N,
                                   hipStream_t stream) {
   const int64_t cus = device_cus();
   const auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * (N / bn); };
-  // skinny batches: all rows in one workgroup per 16-column strip, while the
-  // strips cover at least half the CUs and the operands fit buffer
-  // descriptors
-  if (M <= kSkinnyMaxM && N / 16 >= cus / 2 && gemm_buf_ok(M, K, N))
-    return launch_skinny_c<SkinnyCfg<16, 256, 8, 4>, OutT>(x, W, out, M, K, N, stream);
+  if ((M <= 16 || M > 96) && N / 16 >= cus / 2 && strip_ok(M, K, N))
+    return launch_strip<OutT>(x, W, out, M, K, N, stream);
   if (M <= 128 || tiles(32, 32) <= 2 * cus)
     return launch_gemm_c<GemmCfg<32, 32, 2, 2, 128, 4>, OutT>(x, W, out, M, K, N, stream);
   if (tiles(64, 64) <= cus) return launch_gemm_c<GemmCfg<64, 64, 2, 2, 128, 3>, OutT>(x, W, out, M, K, N, stream);

@@ -31,12 +31,14 @@ def test_gemm_rows_invariant_across_m_and_close_to_exact(dense):
     note("gemm M=4096")
     full = dr.gemm_bf16(xd, Wd).cpu().numpy()
     # the sweep sizes plus others so that, on a 256-CU device, every tile
-    # configuration N = 4096 reaches runs: the skinny 16-column strips (M =
-    # 1, 16), 32 x 32 (17 <= M <= 128), 64 x 64 (200,
-    # 256), 64 x 64 with two stages (300, 512), 128 x 128 (1000, 1024),
-    # 256 x 128 (2048), 256 x 256 (3000, 4096), several with a ragged last
-    # tile (64 x 128 runs where M > N: the bf16 router's logits GEMM)
-    for M in sorted(set(wl.DENSE_MS) | {1, 16, 17, 33, 64, 80, 81, 200, 256, 300, 1000, 1024, 2048, 3000}):
+    # configuration N = 4096 reaches runs: the 16-column strips with all rows
+    # (M <= 16 and 97..128: one to eight row fragments), 32 x 32 (17 <= M <=
+    # 96), 64 x 64 (200, 256), 64 x 64 with two stages (300, 512), 128 x 128
+    # (1000, 1024), 256 x 128 (2048), 256 x 256 (3000, 4096), several with a
+    # ragged last tile (64 x 128 runs where M > N: the bf16 router's logits
+    # GEMM)
+    for M in sorted(set(wl.DENSE_MS) | {1, 5, 16, 17, 33, 64, 80, 81, 96, 97, 100, 113, 128, 200, 256, 300, 1000,
+                                        1024, 2048, 3000}):
         note(f"gemm M={M}")
         out = dr.gemm_bf16(xd[:M].contiguous(), Wd).cpu().numpy()
         assert f32_equal_bits(out, full[:M]), f"M={M} rows differ from the M=4096 run"
@@ -73,12 +75,13 @@ def test_gemm_small_shapes_close_to_exact():
     # two stages, 128 x 128, 256 x 128, three times 256 x 256 (the last with
     # a single K step), and 64 x 128, which
     # runs only where M > N: a ragged 48-row last tile and a partial K stage;
-    # then the skinny strips (M <= 16) with a partial last K stage, and 32 x 32
-    # tiles at N = 4096)
+    # then the 16-column strips (M <= 16 and 97..128) with a partial last K
+    # stage, and 32 x 32 tiles at N = 4096)
     shapes = ((1, 32, 128), (3, 64, 256), (130, 96, 128), (300, 224, 384), (1100, 96, 128),
               (1500, 160, 256), (200, 160, 4096), (450, 96, 4096), (900, 224, 4096), (1800, 96, 4096),
               (2100, 96, 4096), (4100, 160, 4096), (2500, 32, 4096), (6000, 96, 256),
-              (3, 96, 4096), (16, 288, 2048), (40, 224, 4096), (70, 160, 4096))
+              (3, 96, 4096), (16, 288, 2048), (40, 224, 4096), (70, 160, 4096), (1, 32, 4096),
+              (100, 544, 4096), (128, 160, 2048))
     worst = 0.0
     for (M, K, N) in shapes:
         xb = wl.to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
@@ -90,6 +93,28 @@ def test_gemm_small_shapes_close_to_exact():
         worst = max(worst, err)
         assert err <= TOL, (M, K, N, err)
     print(f"small shapes: max |delta| vs exact {worst:.3e} over {len(shapes)} shapes")
+
+
+def test_gemm_strip_rows_match_other_tiles():
+    """The 16-column strip kernel (M <= 16 and 97..128 at N = 4096 on a
+    256-CU device: one to eight row fragments) against the 64 x 64 tiles of
+    a 300-row batch, bit for bit, at K with a partial last W stage (K % 512
+    != 0), a single K step, and a K that is a whole number of stages."""
+    dr = require_gpu()
+    rng = np.random.default_rng(11)
+    N = 4096
+    for K in (32, 96, 544, 1056, 2048, 4128):
+        xb = wl.to_bf16_bits(rng.standard_normal((300, K)).astype(np.float32))
+        Wb = wl.to_bf16_bits((rng.standard_normal((K, N)) * 0.02).astype(np.float32))
+        Wd = dev_bf16_bits(Wb)
+        note(f"gemm strip K={K} M=300")
+        full = dr.gemm_bf16(dev_bf16_bits(xb), Wd).cpu().numpy()
+        for M in (1, 2, 15, 16, 97, 104, 112, 121, 128):
+            note(f"gemm strip K={K} M={M}")
+            out = dr.gemm_bf16(dev_bf16_bits(xb[:M]), Wd).cpu().numpy()
+            assert f32_equal_bits(out, full[:M]), (K, M)
+        ref = oracle.gemm_bf16_ref(xb[:16], Wb)
+        assert float(np.abs(full[:16].astype(np.float64) - ref.astype(np.float64)).max()) <= TOL
 
 
 def test_gate_dot_bit_exact_and_m_invariant(dense):
