@@ -326,30 +326,36 @@ __device__ __forceinline__ void gemm_store(const f32x4 (&acc)[C::FM][C::FN], Out
 // s_waitcnt with only the LDS counter constrained, to zero (gfx9 encoding).
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// The rotated loop, for stages of one 32-wide K step (BK = 32) in a ring of
-// S >= 3, W in 128-byte blocks and an even number of column fragments.  The
-// plain loop reads a stage's fragments right after its barrier, so every
-// wavefront of the workgroup reads at once while the matrix cores idle.
-// Here step t's matrix instructions run on fragments already in registers,
-// and step t+1's fragments are read between them: x fragment i right after
-// the FN matrix steps that use fragment i (into the same registers), the W
-// fragments of step t+1 into a second set over the first FN/2 rows.  Per
-// step: each wavefront waits for its own reads of stage t (lgkmcnt) and for
-// stage t+1's transfers (vmcnt), then the barrier makes stage t+1 visible
-// and frees stage t's buffer, which takes stage t+S's transfers at once.
-// The same instructions and operands per output as gemm_kstep, in the same
-// order per accumulator, so the bits are the same.
+// The rotated loop, for stages of KK = BK / 32 K steps (one or two) in a
+// ring of S stages, W in 128-byte blocks and an even number of column
+// fragments.  The plain loop reads a stage's fragments right after its
+// barrier, so every wavefront of the workgroup reads at once while the
+// matrix cores idle.  Here step t's matrix instructions run on fragments
+// already in registers, and step t+1's fragments are read between them: x
+// fragment i right after the FN matrix steps that use fragment i (into the
+// same registers), the W fragments of step t+1 into a second set over the
+// first FN/2 rows.  When step t+1 lies in the next stage, step t first
+// waits for its own reads of the current stage (lgkmcnt) and for the next
+// stage's transfers (vmcnt); the barrier then makes the next stage visible
+// and frees the current stage's buffer, which takes stage s+S's transfers at
+// once.  Two-step stages read x in 128-byte row pieces, which the L2s serve
+// at a higher rate than 64-byte ones (the operand transfers of a 256 x 256
+// tile over K = 4096 alone: 57 against 75 us).  The same instructions and
+// operands per output as gemm_kstep, in the same order per accumulator, so
+// the bits are the same.
 template <class C, class OutT, bool SKIP, bool BUF>
 __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, const int32_t *__restrict__ rows,
                                               int64_t Mx, const uint16_t *__restrict__ W, OutT *__restrict__ out,
                                               int64_t m0, int64_t mend, int K, int N, int n0, char *smem) {
-  constexpr int FM = C::FM, FN = C::FN, S = C::S;
-  static_assert(C::BK == 32 && S >= 3 && C::QB && FN % 2 == 0 && FN / 2 <= FM, "rotated loop");
+  constexpr int FM = C::FM, FN = C::FN, S = C::S, KK = C::BK / 32;
+  static_assert((KK == 1 || KK == 2) && S >= 3 - (KK - 1) && C::QB && FN % 2 == 0 && FN / 2 <= FM,
+                "rotated loop");
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / C::WN, wn = wave % C::WN;
   const int r16 = lane & 15, g4 = lane >> 4;
   const int ta = lane & 15, tj = ta >> 2, tq = ta & 3;
-  const int nk = K / 32;  // K steps, one per stage
+  const int nk = K / 32;              // K steps
+  const int nst = (nk + KK - 1) / KK;  // stages
   const bool wlive =
       !SKIP || __builtin_amdgcn_readfirstlane(static_cast<int>(m0 + static_cast<int64_t>(wm) * C::TM < mend)) != 0;
 
@@ -365,26 +371,29 @@ __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, co
   if constexpr (BUF) gemm_voffs<C>(arow, K, N, n0, wave, lane, voff);
   const auto issue = [&](int st) {
     char *stage = smem + (st % S) * C::STAGE;
-    if constexpr (BUF) gemm_issue_buf<C>(x, Mx, W, K, N, voff, st, nk, wave, stage);
-    else gemm_issue<C>(x, arow, W, K, N, n0, st, nk, wave, lane, stage);
+    if constexpr (BUF) gemm_issue_buf<C>(x, Mx, W, K, N, voff, st, nst, wave, stage);
+    else gemm_issue<C>(x, arow, W, K, N, n0, st, nst, wave, lane, stage);
   };
 
-  // Per-lane byte offsets within a stage.  x fragment i of this wavefront is
-  // row wm*TM + 16i + r16, unit g4 ^ swa(row); with four units per row swa
-  // repeats every 16 rows, so fragment i sits i * 1024 bytes after fragment
-  // 0.  W fragment j of half c is block (2 g4 + c) * NB + ((wn*FN + j) ^ s),
-  // s = g4 & 1: even j at boff0 + 128 j, odd j at boff1 + 128 j.
-  static_assert(C::UA == 4 && C::swa(16) == C::swa(0), "x fragments 1024 bytes apart");
+  // Per-lane byte offsets within a stage.  x fragment i of this wavefront at
+  // step kk of the stage is row wm*TM + 16i + r16, unit (4 kk + g4) ^
+  // swa(row); swa repeats every 16 rows, so fragment i sits i * 16 UA * 16
+  // bytes after fragment 0.  W fragment j of half c at step kk is block
+  // (8 kk + 2 g4 + c) * NB + ((wn*FN + j) ^ s), s = g4 & 1: even j at
+  // boff0 + 128 j, odd j at boff1 + 128 j.
+  static_assert((C::UA == 4 || C::UA == 8) && C::swa(16) == C::swa(0), "x fragments 16 rows apart");
   const int arow0 = wm * C::TM + r16;
-  const int aoff = (arow0 * C::UA + (g4 ^ C::swa(arow0))) * 16;
+  int aoff[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) aoff[kk] = (arow0 * C::UA + ((4 * kk + g4) ^ C::swa(arow0))) * 16;
   const int s1 = g4 & 1;
   const int bbase = ((2 * g4) * C::NB + wn * FN) * 128 + tj * 32 + tq * 8;
   const int boff0 = bbase + s1 * 128, boff1 = bbase - s1 * 128;
-  const auto read_a = [&](const char *st, int i) {
-    return *reinterpret_cast<const bf16x8 *>(st + aoff + i * 16 * C::UA * 16);
+  const auto read_a = [&](const char *st, int kk, int i) {
+    return *reinterpret_cast<const bf16x8 *>(st + aoff[kk] + i * 16 * C::UA * 16);
   };
-  const auto read_bh = [&](const char *st, int j, int c) {
-    const char *a = st + C::ABYTES + ((j & 1) ? boff1 : boff0) + j * 128 + c * C::NB * 128;
+  const auto read_bh = [&](const char *st, int kk, int j, int c) {
+    const char *a = st + C::ABYTES + ((j & 1) ? boff1 : boff0) + j * 128 + (8 * kk + c) * C::NB * 128;
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4 *)(a));
   };
   const auto join = [](i16x4 lo, i16x4 hi) {
@@ -393,9 +402,9 @@ __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, co
   };
 
   bf16x8 af[FM], b0[FN], b1[FN];
-  // matrix steps of one K step on af / bc, reading step t+1's fragments from
-  // stage nx between them
-  const auto mstep = [&](bf16x8(&bc)[FN], bf16x8(&bn)[FN], const char *nx) {
+  // matrix steps of one K step on af / bc, reading the next step's fragments
+  // (step kn of stage buffer nx) between them
+  const auto mstep = [&](bf16x8(&bc)[FN], bf16x8(&bn)[FN], const char *nx, int kn) {
     i16x4 bh[FN][2];
     static_for<FM>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
@@ -408,12 +417,12 @@ __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, co
       if constexpr (nb > 0) {
         static_for<2>([&](auto jc) {
           constexpr int j = 2 * i + decltype(jc)::value;
-          bh[j][0] = read_bh(nx, j, 0);
-          bh[j][1] = read_bh(nx, j, 1);
+          bh[j][0] = read_bh(nx, kn, j, 0);
+          bh[j][1] = read_bh(nx, kn, j, 1);
           bn[j] = join(bh[j][0], bh[j][1]);
         });
       }
-      af[i] = read_a(nx, i);
+      af[i] = read_a(nx, kn, i);
       // one LDS read after each of the row's first matrix steps, the rest after
       constexpr int nr = nb + 1;
       constexpr int inter = nr < FN ? nr : FN;
@@ -431,9 +440,9 @@ __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, co
   const auto read_first = [&]() {
     if (!SKIP || wlive) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = read_a(smem, i);
+      for (int i = 0; i < FM; ++i) af[i] = read_a(smem, 0, i);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b0[j] = join(read_bh(smem, j, 0), read_bh(smem, j, 1));
+      for (int j = 0; j < FN; ++j) b0[j] = join(read_bh(smem, 0, j, 0), read_bh(smem, 0, j, 1));
     }
   };
   // this wavefront's LDS reads done, then the barrier
@@ -443,11 +452,12 @@ __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, co
     __builtin_amdgcn_s_barrier();
     compiler_fence();
   };
-  // wait for stage t+1 and this wavefront's reads of stage t, make stage t+1
-  // visible and stage t's buffer free, refill it with stage t+S.  The last
-  // step also reads "step nk": stage nk was issued (as zeros) and waited for
-  // like any other, and its fragments go unused; so there is one loop body
-  // and no tail copy.
+  // At the last step of stage s: wait for stage s+1 and this wavefront's
+  // reads of stage s, make stage s+1 visible and stage s's buffer free,
+  // refill it with stage s+S.  The last step also reads "step nk" (of the
+  // last stage, or of stage nst, issued as zeros and waited for like any
+  // other); its fragments go unused, so there is one loop body and no tail
+  // copy.
 #pragma unroll
   for (int i = 0; i < S; ++i) issue(i);
   compiler_fence();
@@ -455,16 +465,25 @@ __device__ __forceinline__ void gemm_tile_rot(const uint16_t *__restrict__ x, co
   __builtin_amdgcn_s_barrier();
   compiler_fence();
   read_first();
-  for (int t = 0; t < nk; ++t) {
-    compiler_fence();
-    wait_vmcnt<C::PER * (S - 2)>();
-    sync();
-    issue(t + S);
-    if (!SKIP || wlive) {
-      mstep(b0, b1, smem + ((t + 1) % S) * C::STAGE);
+  for (int s = 0; s < nst; ++s) {
+    static_for<KK>([&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      const int t = s * KK + kk;
+      if (t < nk) {
+        if constexpr (kk == KK - 1) {
+          compiler_fence();
+          wait_vmcnt<C::PER * (S - 2)>();
+          sync();
+          issue(s + S);
+        }
+        if (!SKIP || wlive) {
+          if constexpr (kk == KK - 1) mstep(b0, b1, smem + ((s + 1) % S) * C::STAGE, 0);
+          else mstep(b0, b1, smem + (s % S) * C::STAGE, kk + 1);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b0[j] = b1[j];
-    }
+          for (int j = 0; j < FN; ++j) b0[j] = b1[j];
+        }
+      }
+    });
   }
   // no transfer may still be writing this workgroup's LDS when it moves on
   compiler_fence();
@@ -992,9 +1011,10 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
   // here).  Below that the weights dominate and 128 x 128 tiles stream them
   // faster: 22 vs 36 us at 8 rows, 169 vs 200 us at 512 rows (864 MiB of
   // weights, 5.3 TB/s), 220 vs 236 us at 16384 rows; at 32768 the large tile
-  // wins (271 vs 289 us).
+  // wins (271 vs 289 us).  The large tile runs the rotated loop over
+  // two-step stages: 416 against 430 us for the plain loop at 65536 rows.
   if (N % 256 == 0 && P >= 128 * E)
-    return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
+    return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2, true>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
   return launch_grouped_c<GemmCfg<128, 128, 4, 2, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
 }
 
@@ -1005,7 +1025,9 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
 // stages of 128 x 4) while there are at most two tiles per CU; 64 x 64 (4
 // wavefronts, 128 x 3), 64 x 128 (8 wavefronts of 16 x 64, 64 x 2), 128 x
 // 128 (8 of 32 x 64, 128 x 2) and 256 x 128 (8 of 64 x 64, 64 x 3) while
-// their tiles fit the CUs once; else 256 x 256 (8 of 128 x 64, 64 x 2).
+// their tiles fit the CUs once; else 256 x 256 (8 of 128 x 64, 64 x 2, the
+// rotated loop: 121.6 against 130.4 us at M = K = N = 4096 with one-step
+// stages in a ring of four, 219 against 241 at M = 8192).
 // Measured against the best of the six at 30 shapes (M = 192..6144 at K = N
 // = 4096, N = 256..14336): within ~1 us or 2% everywhere; e.g. K = N = 4096:
 // M = 256 38 us, 512 43, 1024 56, 2048 90, 3072 124, 4096 142; K = 2048, N =
@@ -1038,7 +1060,7 @@ static hipError_t launch_gemm_any(const uint16_t *x, const uint16_t *W, OutT *ou
   if (tiles(128, 128) <= cus) return launch_gemm_c<GemmCfg<128, 128, 4, 2, 128, 2>, OutT>(x, W, out, M, K, N, stream);
   if (tiles(256, 128) <= cus || N % 256 != 0)
     return launch_gemm_c<GemmCfg<256, 128, 4, 2, 64, 3>, OutT>(x, W, out, M, K, N, stream);
-  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 32, 4, true>, OutT>(x, W, out, M, K, N, stream);
+  return launch_gemm_c<GemmCfg<256, 256, 2, 4, 64, 2, true>, OutT>(x, W, out, M, K, N, stream);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t *x, const uint16_t *W, float *out, int64_t M, int64_t K, int64_t N,
