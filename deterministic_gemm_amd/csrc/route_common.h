@@ -126,6 +126,7 @@ __device__ __forceinline__ void tree_final(float (&stk)[MAXL][N], int nb, float 
 // output; the additions are elementwise fp32 adds).  Kernels keep their group
 // stack as vectors so it stays in registers.
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x32 __attribute__((ext_vector_type(32)));
 
 template <int L, int MAXL>
 __device__ __forceinline__ void tree_push_vec_level(f32x16 (&stk)[MAXL], f32x16 &p, int b) {

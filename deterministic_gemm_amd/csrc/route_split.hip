@@ -26,7 +26,8 @@
 
 namespace drk {
 
-// A wavefront owns 16*AT tokens x 16*BT experts as AT x BT tiles of 16x16.
+// A wavefront owns 16*AT tokens x 16*BT experts, as (AT/2) x (BT/2) tiles of
+// 32 x 32 for the two-slot matrix instruction.
 // With KP = 2 the workgroup's wavefronts form two parts that run the two
 // halves of the canonical tree over K-groups (groups padded to P =
 // 2^ceil(log2 G) leaves, part q taking groups [qP/2, (q+1)P/2)), each part on
@@ -40,6 +41,7 @@ struct SplitCfg {
   static constexpr int E = E_, ET = ET_, AT = AT_, BT = BT_, WT = WT_, KC = KC_, S = S_, KP = KP_;
   static constexpr bool LATE = LATE_;  // refill the freed stage after the chunk's matrix steps
   static constexpr bool XB = XB_;
+  static_assert(AT % 2 == 0 && BT % 2 == 0, "32 x 32 wavefront sub-tiles");
   static constexpr int XV = XB ? 8 : 4;       // x values per 16-byte unit
   static constexpr int EW = 16 * BT;          // experts per wavefront
   static constexpr int NWE = ET / EW;         // wavefronts across the expert tile
@@ -142,16 +144,24 @@ __device__ __forceinline__ void split_issue(const void *__restrict__ xv, const f
   }
 }
 
+// A wavefront's chains: v[a][b][p][r] is slot 2p + r / 16 of the group,
+// token 32a + 8 ((r % 16) / 4) + 4 (lane >> 5) + r % 4, expert 32b + (lane &
+// 31) -- the output order of v_mfma_f32_32x32x1_2b_f32, whose two blocks are
+// two K-block slots.
+template <class C>
+struct SplitAcc {
+  f32x32 v[C::AT / 2][C::BT / 2][2];
+};
+
 // One chunk: retire its transfers, publish them, refill the stage freed by
 // the previous chunk, then 4 slots x KC chain steps on the matrix cores; at
 // the end of a group of four K-blocks, fold the group's partials.
 template <class C, int MAXL>
 __device__ __forceinline__ void split_step(const void *__restrict__ xf, const float *__restrict__ W, int64_t M,
                                            int K, int64_t m0, int e0, int nb, int nchunks, int span, int wave,
-                                           int lane, int ci, const float *cur, float *refill,
-                                           f32x16 (&acc)[C::AT][C::BT], f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
+                                           int lane, int ci, const float *cur, float *refill, SplitAcc<C> &acc,
+                                           f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
   constexpr int ET = C::ET, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, S = C::S, HU = C::HU;
-  const int s_l = lane >> 4, r_l = lane & 15;
   const int part = wave / C::NWP, wp = wave % C::NWP;
   const int tb = (wp / C::NWE) * C::TW;
   const int eb = (wp % C::NWE) * C::EW;
@@ -161,15 +171,13 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
   cur += part * C::PST;
   if (cg == 0) {
 #pragma unroll
-    for (int a = 0; a < AT; ++a)
+    for (int a = 0; a < AT / 2; ++a)
 #pragma unroll
-      for (int b = 0; b < BT; ++b)
+      for (int b = 0; b < BT / 2; ++b)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float init = (4 * g + s < nb) ? 0.0f : -0.0f;
+        for (int p = 0; p < 2; ++p)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[a][b][4 * s + q] = init;
-        }
+          for (int r = 0; r < 32; ++r) acc.v[a][b][p][r] = (4 * g + 2 * p + r / 16 < nb) ? 0.0f : -0.0f;
   }
   compiler_fence();
   if (wp < C::XW)
@@ -180,34 +188,47 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
   compiler_fence();
   if constexpr (!C::LATE) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
 
-  // Operands of step group c4 + 1 are read from LDS while the matrix steps
-  // of c4 run, into a second register set, one read after each of the first
-  // six matrix steps.  Left to itself the scheduler reads each step's W
-  // values just before their use and waits for them every four matrix
-  // steps.  Measured at M = 8192, K = 2048, E = 256 in one process: the
-  // logits kernel 76.9 us against 78.3, bf16 x 91.1 against 96.8 (reading
-  // all six first, behind a scheduling barrier, was slower: 79.9).
   const float *xs = cur + C::WST;
-  float4 av[2][AT];
-  float bw[2][BT][4];
-  [[maybe_unused]] uint4 ux[2][AT];  // bf16 x: one 16-byte unit feeds two step groups
+  // Matrix steps: v_mfma_f32_32x32x1_2b_f32, two K-block slots per
+  // instruction (32 x 32 outputs each); every output still gets one fused
+  // multiply-add per k onto its slot's chain.  On random fp32 operands this
+  // form sustains more of the matrix peak than the four-slot 16 x 16 one
+  // (132 against 120 TFLOP/s in a register-operand microbenchmark, 8
+  // wavefronts per CU): the chip holds a higher clock for the same work.
+  // The logits kernel measured 84.2 against 85.3 us per call at M = 8192, K =
+  // 2048, E = 256 (bf16 x 89.8 against 91.1, K = 4096, E = 512 154.9 against
+  // 158.3).  Operands of step group c4 + 1 are read from LDS while the matrix
+  // steps of c4 run, into a second register set, one read after each matrix
+  // step; left to itself the scheduler reads each step's W values just before
+  // their use and waits for them every few matrix steps.
+  // lane l: slot 2p + (l >> 5) of pair p, token tb + 32a + (l & 31), expert
+  // eb + 32b + (l & 31); per pair AT/2 16-byte x reads and 4 BT/2 W reads
+  // per step group of four k
+  constexpr int A2 = AT / 2, B2 = BT / 2;
+  const int hl = lane >> 5, il = lane & 31;
+  float4 av[2][A2][2];
+  float bw[2][B2][2][4];
+  [[maybe_unused]] uint4 ux[2][A2][2];
   const auto read_ops = [&](int c4, int r) {
 #pragma unroll
-    for (int a = 0; a < AT; ++a) {
-      const int tok = tb + a * 16 + r_l;
-      if constexpr (C::XB) {
-        // unit c4 / 2 of the row holds 8 values, read whole at even groups
-        if ((c4 & 1) == 0)
-          ux[(c4 >> 1) & 1][a] =
-              *reinterpret_cast<const uint4 *>(xs + ((s_l * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
-      } else {
-        av[r][a] = *reinterpret_cast<const float4 *>(xs + ((s_l * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+    for (int p = 0; p < 2; ++p) {
+      const int sl = 2 * p + hl;
+#pragma unroll
+      for (int a = 0; a < A2; ++a) {
+        const int tok = tb + a * 32 + il;
+        if constexpr (C::XB) {
+          if ((c4 & 1) == 0)
+            ux[(c4 >> 1) & 1][a][p] =
+                *reinterpret_cast<const uint4 *>(xs + ((sl * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
+        } else {
+          av[r][a][p] = *reinterpret_cast<const float4 *>(xs + ((sl * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+        }
       }
+#pragma unroll
+      for (int b = 0; b < B2; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bw[r][b][p][q] = cur[sl * C::SW + (4 * c4 + q) * ET + eb + b * 32 + il];
     }
-#pragma unroll
-    for (int b = 0; b < BT; ++b)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) bw[r][b][q] = cur[s_l * C::SW + (4 * c4 + q) * ET + eb + b * 16 + r_l];
   };
   read_ops(0, 0);
 #pragma unroll
@@ -215,36 +236,36 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
     const int r = c4 & 1;
     if (c4 + 1 < KC / 4) read_ops(c4 + 1, r ^ 1);
     if constexpr (C::XB) {
-      // this group's 4 values are half c4 % 2 of the unit, widened exactly
 #pragma unroll
-      for (int a = 0; a < AT; ++a) {
-        const uint4 u = ux[(c4 >> 1) & 1][a];
-        const uint32_t lo = (c4 & 1) ? u.z : u.x, hi = (c4 & 1) ? u.w : u.y;
-        av[r][a] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
-      }
+      for (int a = 0; a < A2; ++a)
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+          const uint4 u = ux[(c4 >> 1) & 1][a][p];
+          const uint32_t lo = (c4 & 1) ? u.z : u.x, hi = (c4 & 1) ? u.w : u.y;
+          av[r][a][p] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
+        }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int a = 0; a < AT; ++a)
+      for (int a = 0; a < A2; ++a)
 #pragma unroll
-        for (int b = 0; b < BT; ++b) {
-          const float aval = (q == 0) ? av[r][a].x : (q == 1) ? av[r][a].y : (q == 2) ? av[r][a].z : av[r][a].w;
-          acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x1f32(aval, bw[r][b][q], acc[a][b], 0, 0, 0);
-        }
-    // issue order: the next group's NR operand reads (AT 16-byte x reads,
-    // BT * 2 paired W reads) one by one between the first NR matrix steps,
-    // then the remaining steps
-    constexpr int NR = AT + 2 * BT, NM = 4 * AT * BT;
-    static_assert(NR <= NM, "reads fit between the matrix steps");
+        for (int b = 0; b < B2; ++b)
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+          for (int p = 0; p < 2; ++p) {
+            const float aval = (q == 0) ? av[r][a][p].x : (q == 1) ? av[r][a][p].y : (q == 2) ? av[r][a][p].z : av[r][a][p].w;
+            acc.v[a][b][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(aval, bw[r][b][p][q], acc.v[a][b][p], 0, 0, 0);
+          }
+    constexpr int NR = 2 * A2 + 4 * B2, NM = 4 * A2 * B2 * 2;
+    constexpr int NI = NR < NM ? NR : NM;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix step
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - NR, 0);
+    if constexpr (NM > NI) __builtin_amdgcn_sched_group_barrier(0x008, NM - NI, 0);
+    if constexpr (NR > NI) __builtin_amdgcn_sched_group_barrier(0x100, NR - NI, 0);
   }
-
   if constexpr (C::LATE) {
     compiler_fence();
     split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
@@ -255,15 +276,15 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
     // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
     constexpr int NV = AT * BT * 4 / 16;
     f32x16 qv[NV];
+    // vector a * (BT/2) + b holds sub-tile (a, b) in the 32 x 32 lane order
 #pragma unroll
-    for (int a = 0; a < AT; ++a)
+    for (int a = 0; a < AT / 2; ++a)
 #pragma unroll
-      for (int b = 0; b < BT; ++b)
+      for (int b = 0; b < BT / 2; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int o = (a * BT + b) * 4 + q;
-          qv[o / 16][o % 16] = (acc[a][b][q] + acc[a][b][4 + q]) + (acc[a][b][8 + q] + acc[a][b][12 + q]);
-        }
+        for (int r = 0; r < 16; ++r)
+          qv[a * (BT / 2) + b][r] =
+              (acc.v[a][b][0][r] + acc.v[a][b][0][16 + r]) + (acc.v[a][b][1][r] + acc.v[a][b][1][16 + r]);
 #pragma unroll
     for (int v = 0; v < NV; ++v) tree_push_vec<MAXL>(stk[v], qv[v], gi);
   }
@@ -290,7 +311,6 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *_
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int s_l = lane >> 4, r_l = lane & 15;
   const int part = wave / C::NWP, wp = wave % C::NWP;
   const int tb = (wp / C::NWE) * C::TW;
   const int eb = (wp % C::NWE) * C::EW;
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *_
   const int span = C::KP == 1 ? G : P / 2;
   const int nchunks = span * C::CPG;
 
-  f32x16 acc[AT][BT];
+  SplitAcc<C> acc;
   f32x16 stk[AT * BT * 4 / 16][MAXL];
 
 #pragma unroll
@@ -344,17 +364,17 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *_
         for (int j = 0; j < 16; ++j) outv[v][j] = outv[v][j] + comb[((wp * NV + v) * 16 + j) * 64 + lane];
     }
   }
-  // lane (s_l, r_l) holds token tb + 16a + 4s_l + q at expert eb + 16b + r_l
+  // vector a * (BT/2) + b, element r: token tb + 32a + 8 (r / 4) + 4 (lane
+  // >> 5) + r % 4 at expert eb + 32b + (lane & 31)
   if (part == 0) {
 #pragma unroll
-    for (int a = 0; a < AT; ++a)
+    for (int a = 0; a < AT / 2; ++a)
 #pragma unroll
-      for (int b = 0; b < BT; ++b)
+      for (int b = 0; b < BT / 2; ++b)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tok = tb + a * 16 + 4 * s_l + q;
-          const int o = (a * BT + b) * 4 + q;
-          lg[tok * C::LGP + eb + b * 16 + r_l] = outv[o / 16][o % 16];
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tb + a * 32 + 8 * (r / 4) + 4 * (lane >> 5) + r % 4;
+          lg[tok * C::LGP + eb + b * 32 + (lane & 31)] = outv[a * (BT / 2) + b][r];
         }
   }
   __syncthreads();
@@ -604,25 +624,25 @@ hipError_t launch_route_logits(const RouteLaunch &L) {
         if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
         return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
       }
-      if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true>>(L);
-      if (L.K > 4096) return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4, 1, true>>(L);
-      return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
+      if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true, false>>(L);
+      if (L.K > 4096) return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4, 1, true, false>>(L);
+      return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true, false>, 3>(L);
     case 512:
       if (!L.xf) {
         if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
         return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
       }
-      if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true>>(L);
-      if (L.K > 4096) return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4, 1, true>>(L);
-      return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
+      if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true, false>>(L);
+      if (L.K > 4096) return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4, 1, true, false>>(L);
+      return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true, false>, 3>(L);
     case 1024:
       if (!L.xf) {
         if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
         return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
       }
-      if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true>>(L);
-      if (L.K > 4096) return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 8, 4, 1, true>>(L);
-      return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true>, 3>(L);
+      if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true, false>>(L);
+      if (L.K > 4096) return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 8, 4, 1, true, false>>(L);
+      return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true, false>, 3>(L);
     default: return hipErrorInvalidValue;
   }
 }
@@ -646,7 +666,7 @@ bool fused_supports(int64_t E, int64_t K, bool x_f32) {
 hipError_t launch_route_fused(const RouteLaunch &L) {
   if (L.E != 256) return hipErrorInvalidValue;
   if (!L.xf) return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true, true>>(L);
-  return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true>>(L);
+  return launch_logits_c<SplitCfg<256, 256, 2, 2, 1, 8, 4, 1, true, false>>(L);
 }
 
 hipError_t launch_route_split(const RouteLaunch &L) {
