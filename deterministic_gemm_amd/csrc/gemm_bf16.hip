@@ -323,9 +323,6 @@ __device__ __forceinline__ void gemm_store(const f32x4 (&acc)[C::FM][C::FN], Out
     }
 }
 
-// s_waitcnt with only the LDS counter constrained, to zero (gfx9 encoding).
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
 // The rotated loop, for stages of KK = BK / 32 K steps (one or two) in a
 // ring of S stages, W in 128-byte blocks and an even number of column
 // fragments.  The plain loop reads a stage's fragments right after its

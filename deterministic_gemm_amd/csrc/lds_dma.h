@@ -26,6 +26,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// s_waitcnt with only the LDS counter constrained, to zero (gfx9 encoding).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 // One global -> LDS transfer: every active lane moves the 16 bytes at `src`
 // to LDS address lds_base + 16 * lane.  Written as inline assembly so that
 // the compiler's wait-count pass does not treat it as an LDS write to be

@@ -153,15 +153,91 @@ struct SplitAcc {
   f32x32 v[C::AT / 2][C::BT / 2][2];
 };
 
-// One chunk: retire its transfers, publish them, refill the stage freed by
-// the previous chunk, then 4 slots x KC chain steps on the matrix cores; at
-// the end of a group of four K-blocks, fold the group's partials.
-template <class C, int MAXL>
+// A wavefront's operand registers for one step group of four k, two sets
+// (the group being multiplied and the next): per pair p of slots, lane l
+// holds x at slot 2p + (l >> 5), token tb + 32a + (l & 31) (bf16 x: a whole
+// 16-byte unit of 8 values, read at even groups) and W at that slot, expert
+// eb + 32b + (l & 31), four k each.
+template <class C>
+struct SplitOps {
+  float4 av[2][C::AT / 2][2];
+  float bw[2][C::BT / 2][2][4];
+  uint4 ux[2][C::AT / 2][2];
+};
+
+// Reads step group c4's operands from a stage (the part's half) into set r.
+template <class C>
+__device__ __forceinline__ void split_read_ops(const float *cur, int c4, int r, int tb, int eb, int lane,
+                                               SplitOps<C> &o) {
+  constexpr int ET = C::ET, TT = C::TT, HU = C::HU, A2 = C::AT / 2, B2 = C::BT / 2;
+  const float *xs = cur + C::WST;
+  const int hl = lane >> 5, il = lane & 31;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int sl = 2 * p + hl;
+#pragma unroll
+    for (int a = 0; a < A2; ++a) {
+      const int tok = tb + a * 32 + il;
+      if constexpr (C::XB) {
+        if ((c4 & 1) == 0)
+          o.ux[(c4 >> 1) & 1][a][p] =
+              *reinterpret_cast<const uint4 *>(xs + ((sl * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
+      } else {
+        o.av[r][a][p] = *reinterpret_cast<const float4 *>(xs + ((sl * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B2; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o.bw[r][b][p][q] = cur[sl * C::SW + (4 * c4 + q) * ET + eb + b * 32 + il];
+  }
+}
+
+// One chunk, 4 slots x KC chain steps on the matrix cores, at the end of a
+// group of four K-blocks folding the group's partials.  Without ROT a chunk
+// starts by publishing itself (each wavefront waits for its own transfers,
+// then the barrier) and reading its first step group, and after its matrix
+// steps refills the stage the previous chunk freed.  With ROT the chunk's
+// first step group was read by the previous chunk (or before the loop), and
+// its last step group publishes the next chunk first: each wavefront waits
+// for its own transfers of chunk ci + 1 and for its reads of this chunk's
+// stage, then the barrier makes chunk ci + 1 visible to all and frees this
+// chunk's stage; the next chunk's first operands are read while this chunk's
+// last matrix steps run, and the freed stage is refilled with chunk ci + S
+// after them, so no wavefront waits for an LDS read at the start of a chunk.
+// Measured in one process against the plain order (whole call): M = 8192, K
+// = 2048, E = 256 82.1 against 83.7 us; K = 6144 217.3 against 226.9; the
+// one-launch family 84.6 against 90.4; but bf16 x 93.4 against 89.7 and K =
+// 4096, E = 512 (16-step chunks with a three-level counter stack, which then
+// spills) 170.3 against 154.1, so those keep the plain order.
+//
+// Matrix steps: v_mfma_f32_32x32x1_2b_f32, two K-block slots per
+// instruction (32 x 32 outputs each); every output still gets one fused
+// multiply-add per k onto its slot's chain.  On random fp32 operands this
+// form sustains more of the matrix peak than the four-slot 16 x 16 one (132
+// against 120 TFLOP/s in a register-operand microbenchmark, 8 wavefronts per
+// CU): the chip holds a higher clock for the same work.  The logits kernel
+// measured 84.2 against 85.3 us per call at M = 8192, K = 2048, E = 256 (bf16
+// x 89.8 against 91.1, K = 4096, E = 512 154.9 against 158.3).  Operands of
+// step group c4 + 1 are read from LDS while the matrix steps of c4 run, into
+// the second register set, one read after each matrix step; left to itself
+// the scheduler reads each step's W values just before their use and waits
+// for them every few matrix steps.
+template <class C, int MAXL, bool ROT>
 __device__ __forceinline__ void split_step(const void *__restrict__ xf, const float *__restrict__ W, int64_t M,
                                            int K, int64_t m0, int e0, int nb, int nchunks, int span, int wave,
-                                           int lane, int ci, const float *cur, float *refill, SplitAcc<C> &acc,
+                                           int lane, int ci, const float *cur, const float *nxt, float *refill,
+                                           SplitAcc<C> &acc, SplitOps<C> &ops_carried,
                                            f32x16 (&stk)[C::AT * C::BT * 4 / 16][MAXL]) {
-  constexpr int ET = C::ET, AT = C::AT, BT = C::BT, KC = C::KC, TT = C::TT, S = C::S, HU = C::HU;
+  // without ROT the operand registers live within the chunk only
+  SplitOps<C> ops_local;
+  SplitOps<C> &ops = ROT ? ops_carried : ops_local;
+  constexpr int AT = C::AT, BT = C::BT, KC = C::KC, S = C::S;
+  constexpr int A2 = AT / 2, B2 = BT / 2;
+  static_assert(C::LATE && (KC / 4) % 2 == 0, "the chunk's last step group reads into set 0");
+  // with ROT the next chunk's first bf16 unit could land in registers this
+  // chunk's last group still widens from (8-step chunks)
+  static_assert(!(ROT && C::XB), "bf16 x takes the plain order");
   const int part = wave / C::NWP, wp = wave % C::NWP;
   const int tb = (wp / C::NWE) * C::TW;
   const int eb = (wp % C::NWE) * C::EW;
@@ -169,80 +245,53 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
   const int g = part * span + gi;
   const int cg = ci % C::CPG;
   cur += part * C::PST;
+  nxt += part * C::PST;
   if (cg == 0) {
 #pragma unroll
-    for (int a = 0; a < AT / 2; ++a)
+    for (int a = 0; a < A2; ++a)
 #pragma unroll
-      for (int b = 0; b < BT / 2; ++b)
+      for (int b = 0; b < B2; ++b)
 #pragma unroll
         for (int p = 0; p < 2; ++p)
 #pragma unroll
           for (int r = 0; r < 32; ++r) acc.v[a][b][p][r] = (4 * g + 2 * p + r / 16 < nb) ? 0.0f : -0.0f;
   }
-  compiler_fence();
-  if (wp < C::XW)
-    wait_vmcnt<C::PER_X * (S - 2)>();
-  else
-    wait_vmcnt<C::PER_W * (S - 2)>();
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-  if constexpr (!C::LATE) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
-
-  const float *xs = cur + C::WST;
-  // Matrix steps: v_mfma_f32_32x32x1_2b_f32, two K-block slots per
-  // instruction (32 x 32 outputs each); every output still gets one fused
-  // multiply-add per k onto its slot's chain.  On random fp32 operands this
-  // form sustains more of the matrix peak than the four-slot 16 x 16 one
-  // (132 against 120 TFLOP/s in a register-operand microbenchmark, 8
-  // wavefronts per CU): the chip holds a higher clock for the same work.
-  // The logits kernel measured 84.2 against 85.3 us per call at M = 8192, K =
-  // 2048, E = 256 (bf16 x 89.8 against 91.1, K = 4096, E = 512 154.9 against
-  // 158.3).  Operands of step group c4 + 1 are read from LDS while the matrix
-  // steps of c4 run, into a second register set, one read after each matrix
-  // step; left to itself the scheduler reads each step's W values just before
-  // their use and waits for them every few matrix steps.
-  // lane l: slot 2p + (l >> 5) of pair p, token tb + 32a + (l & 31), expert
-  // eb + 32b + (l & 31); per pair AT/2 16-byte x reads and 4 BT/2 W reads
-  // per step group of four k
-  constexpr int A2 = AT / 2, B2 = BT / 2;
-  const int hl = lane >> 5, il = lane & 31;
-  float4 av[2][A2][2];
-  float bw[2][B2][2][4];
-  [[maybe_unused]] uint4 ux[2][A2][2];
-  const auto read_ops = [&](int c4, int r) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int sl = 2 * p + hl;
-#pragma unroll
-      for (int a = 0; a < A2; ++a) {
-        const int tok = tb + a * 32 + il;
-        if constexpr (C::XB) {
-          if ((c4 & 1) == 0)
-            ux[(c4 >> 1) & 1][a][p] =
-                *reinterpret_cast<const uint4 *>(xs + ((sl * TT + tok) * HU + ((c4 >> 1) ^ C::swz(tok))) * 4);
-        } else {
-          av[r][a][p] = *reinterpret_cast<const float4 *>(xs + ((sl * TT + tok) * HU + (c4 ^ C::swz(tok))) * 4);
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < B2; ++b)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bw[r][b][p][q] = cur[sl * C::SW + (4 * c4 + q) * ET + eb + b * 32 + il];
-    }
-  };
-  read_ops(0, 0);
+  if constexpr (!ROT) {
+    // publish this chunk, then read its first step group
+    compiler_fence();
+    if (wp < C::XW)
+      wait_vmcnt<C::PER_X * (S - 2)>();
+    else
+      wait_vmcnt<C::PER_W * (S - 2)>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    split_read_ops<C>(cur, 0, 0, tb, eb, lane, ops);
+  }
 #pragma unroll
   for (int c4 = 0; c4 < KC / 4; ++c4) {
     const int r = c4 & 1;
-    if (c4 + 1 < KC / 4) read_ops(c4 + 1, r ^ 1);
+    if (c4 + 1 < KC / 4) {
+      split_read_ops<C>(cur, c4 + 1, r ^ 1, tb, eb, lane, ops);
+    } else if constexpr (ROT) {
+      compiler_fence();
+      if (wp < C::XW)
+        wait_vmcnt<C::PER_X * (S - 2)>();
+      else
+        wait_vmcnt<C::PER_W * (S - 2)>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      compiler_fence();
+      split_read_ops<C>(nxt, 0, r ^ 1, tb, eb, lane, ops);
+    }
     if constexpr (C::XB) {
+      // this group's 4 values are half c4 % 2 of the unit, widened exactly
 #pragma unroll
       for (int a = 0; a < A2; ++a)
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-          const uint4 u = ux[(c4 >> 1) & 1][a][p];
+          const uint4 u = ops.ux[(c4 >> 1) & 1][a][p];
           const uint32_t lo = (c4 & 1) ? u.z : u.x, hi = (c4 & 1) ? u.w : u.y;
-          av[r][a][p] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
+          ops.av[r][a][p] = make_float4(u2f(lo << 16), u2f(lo & 0xFFFF0000u), u2f(hi << 16), u2f(hi & 0xFFFF0000u));
         }
     }
 #pragma unroll
@@ -253,8 +302,9 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
         for (int b = 0; b < B2; ++b)
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
-            const float aval = (q == 0) ? av[r][a][p].x : (q == 1) ? av[r][a][p].y : (q == 2) ? av[r][a][p].z : av[r][a][p].w;
-            acc.v[a][b][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(aval, bw[r][b][p][q], acc.v[a][b][p], 0, 0, 0);
+            const float4 av = ops.av[r][a][p];
+            const float aval = (q == 0) ? av.x : (q == 1) ? av.y : (q == 2) ? av.z : av.w;
+            acc.v[a][b][p] = __builtin_amdgcn_mfma_f32_32x32x1f32(aval, ops.bw[r][b][p][q], acc.v[a][b][p], 0, 0, 0);
           }
     constexpr int NR = 2 * A2 + 4 * B2, NM = 4 * A2 * B2 * 2;
     constexpr int NI = NR < NM ? NR : NM;
@@ -266,11 +316,11 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
     if constexpr (NM > NI) __builtin_amdgcn_sched_group_barrier(0x008, NM - NI, 0);
     if constexpr (NR > NI) __builtin_amdgcn_sched_group_barrier(0x100, NR - NI, 0);
   }
-  if constexpr (C::LATE) {
-    compiler_fence();
-    split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + S - 1, refill);
-    compiler_fence();
-  }
+  // refill: with ROT this chunk's stage with chunk ci + S, else the stage the
+  // previous chunk freed with chunk ci + S - 1
+  compiler_fence();
+  split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ROT ? ci + S : ci + S - 1, refill);
+  compiler_fence();
 
   if (cg == C::CPG - 1) {
     // levels 1 and 2 of the tree inside the group: (p0 + p1) + (p2 + p3)
@@ -278,12 +328,12 @@ __device__ __forceinline__ void split_step(const void *__restrict__ xf, const fl
     f32x16 qv[NV];
     // vector a * (BT/2) + b holds sub-tile (a, b) in the 32 x 32 lane order
 #pragma unroll
-    for (int a = 0; a < AT / 2; ++a)
+    for (int a = 0; a < A2; ++a)
 #pragma unroll
-      for (int b = 0; b < BT / 2; ++b)
+      for (int b = 0; b < B2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          qv[a * (BT / 2) + b][r] =
+          qv[a * B2 + b][r] =
               (acc.v[a][b][0][r] + acc.v[a][b][0][16 + r]) + (acc.v[a][b][1][r] + acc.v[a][b][1][16 + r]);
 #pragma unroll
     for (int v = 0; v < NV; ++v) tree_push_vec<MAXL>(stk[v], qv[v], gi);
@@ -326,15 +376,33 @@ __global__ __launch_bounds__(C::NT) void route_split_logits_kernel(const void *_
   SplitAcc<C> acc;
   f32x16 stk[AT * BT * 4 / 16][MAXL];
 
+  SplitOps<C> ops;
+  constexpr bool ROT = !C::XB && !(C::KC == 16 && MAXL >= 3);
+  if constexpr (ROT) {
+    // all S stages in flight; chunk 0 published and its first operands read
 #pragma unroll
-  for (int i = 0; i < S - 1; ++i) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, i, smem + i * STG);
+    for (int i = 0; i < S; ++i) split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, i, smem + i * STG);
+    compiler_fence();
+    if (wp < C::XW)
+      wait_vmcnt<C::PER_X * (S - 1)>();
+    else
+      wait_vmcnt<C::PER_W * (S - 1)>();
+    __builtin_amdgcn_s_barrier();
+    compiler_fence();
+    split_read_ops<C>(smem + part * C::PST, 0, 0, tb, eb, lane, ops);
+  } else {
+#pragma unroll
+    for (int i = 0; i < S - 1; ++i)
+      split_issue<C>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, i, smem + i * STG);
+  }
   // unrolled by S so that every stage address is a compile-time constant
   for (int ci = 0; ci < nchunks; ci += S) {
 #pragma unroll
     for (int j = 0; j < S; ++j)
       if (ci + j < nchunks)
-        split_step<C, MAXL>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + j, smem + j * STG,
-                            smem + ((j + S - 1) % S) * STG, acc, stk);
+        split_step<C, MAXL, ROT>(xf, W, M, K, m0, e0, nb, nchunks, span, wave, lane, ci + j, smem + j * STG,
+                                 smem + ((j + 1) % S) * STG, smem + (ROT ? j : (j + S - 1) % S) * STG, acc, ops,
+                                 stk);
   }
 
   constexpr int NV = AT * BT * 4 / 16;
