@@ -303,22 +303,28 @@ static hipError_t launch_narrow_c(const RouteLaunch &L) {
 // whose workgroups all fit on the CUs at once, two per CU (66-76 KiB of LDS
 // each) --
 //   16 x 16 tokens x experts: one part per group (two, or four with a
-//     two-stage ring), 16-step chunks;
+//     two-stage ring);
 //   32 x 16: two parts, 16-step chunks, three stages;
-//   32 x 32: two parts, 8-step chunks, four stages (also for larger batches).
+//   32 x 32: two parts, 16-step chunks, two stages (also for larger batches).
 // A larger tile gives each wavefront two or four independent chains and reads
 // fewer operand bytes per product; a smaller one fills the CUs sooner.  Logits
 // kernel alone, bits identical across the tiles: K = 2048, E = 256: M = 1024
 // 24 us (16 x 16 tiles: 30), 2048 38 us (the split kernels: 44); K = 4096, E =
 // 512: M = 240 22 us (four parts with four stages: 31), 512 40 us (59), 1024
 // 65 us (115).  More groups keep one part per group and four stages.
-// bf16 x (8 values per 16-byte unit) takes chunks twice as long where LDS
-// allows -- 32 steps on the 8-row and 16 x 16 tiles (three stages where two
-// workgroups share a CU), 32 steps in two stages on 32 x 16, 16 in three on
-// 32 x 32 -- so that a token's row piece of a chunk is 64 bytes, as with fp32
-// x.  Whole call, K = 2048, E = 256, bf16 x: M = 300-500 17.3-18.1 against
-// 23.3-23.9 us, 600 23.3-24.3 against 35.2-36.9, 1024 26.3-27.0 against
-// 37.2-37.7 (fp32 x: 29.4), 2048 36.5-37.2 against 40.4-40.8.
+// Chunk lengths are chosen so that a token's row piece of a chunk is 64 or
+// 128 bytes, which the L2s serve faster than 32-byte pieces: fp32 x takes
+// 32 steps on the 8-row and two-part 16 x 16 tiles and 16 on 32 x 32; bf16 x
+// (8 values per 16-byte unit) 32 steps on the 8-row and 16 x 16 tiles (three
+// stages where two workgroups share a CU), 32 in two stages on 32 x 16, 16 in
+// three on 32 x 32.  Whole call, K = 2048, E = 256, bf16 x: M = 300-500
+// 17.3-18.1 against 23.3-23.9 us with 16-step chunks, 600 23.3-24.3 against
+// 35.2-36.9, 1024 26.3-27.0 against 37.2-37.7, 2048 36.5-37.2 against
+// 40.4-40.8.  fp32 x, 32 against 16 steps: M = 65-128 16.9 against 18.0 us,
+// 200-400 17.8-18.2 against 18.8-19.3; 32 x 32 tiles, 16 steps in two stages
+// against 8 in four: M = 1500 36.0 against 38.5 us, 2048 38.5 against 41.8, K
+// = 4096 and E = 512 at M = 600-1000 63.5-64.6 against 68.2-69.4, K = 3072 at
+// M = 1500 61.3 against 66.6.
 template <int E, bool XB>
 static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const int64_t nb = (L.K + 255) / 256;
@@ -326,9 +332,9 @@ static hipError_t launch_narrow_e(const RouteLaunch &L) {
   const auto wgs = [&](int64_t tt, int64_t et) { return (L.M + tt - 1) / tt * (E / et); };
   // 8 x 16 tiles while their workgroups all fit on the CUs at once
   if (G <= 4 && wgs(8, 16) <= device_cus()) {
-    if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, XB ? 32 : 16, 4, XB, 8>>(L);
-    if (G == 2) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, XB ? 32 : 16, 4, XB, 8>>(L);
-    return launch_narrow_c<NarrowCfg<E, 1, 1, 4, XB ? 32 : 16, XB ? 3 : 4, XB, 8>>(L);
+    if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, 32, 4, XB, 8>>(L);
+    if (G == 2) return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 32, 4, XB, 8>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 32, 3, XB, 8>>(L);
   }
   if (G == 1) return launch_narrow_c<NarrowCfg<E, 1, 1, 1, XB ? 32 : 16, 4, XB>>(L);
   if (G > 4) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 4, XB>>(L);
@@ -337,10 +343,10 @@ static hipError_t launch_narrow_e(const RouteLaunch &L) {
     // three groups take four parts too (the fourth empty): with two, one
     // part runs two groups in sequence (K = 3072, E = 256, M = 100: 30 us)
     if (G >= 3) return launch_narrow_c<NarrowCfg<E, 1, 1, 4, 16, 2, XB>>(L);
-    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, XB ? 32 : 16, XB ? 3 : 4, XB>>(L);
+    return launch_narrow_c<NarrowCfg<E, 1, 1, 2, 32, XB ? 3 : 2, XB>>(L);
   }
   if (wgs(32, 16) <= slots) return launch_narrow_c<NarrowCfg<E, 2, 1, 2, XB ? 32 : 16, XB ? 2 : 3, XB>>(L);
-  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, XB ? 16 : 8, XB ? 3 : 4, XB>>(L);
+  return launch_narrow_c<NarrowCfg<E, 2, 2, 2, 16, XB ? 3 : 2, XB>>(L);
 }
 
 // The largest batch the narrow family takes before the split kernels: at
