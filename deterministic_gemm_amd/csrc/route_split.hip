@@ -77,7 +77,7 @@ struct SplitCfg {
   static_assert(!FUSED || (KP == 1 && TT % (4 * NW) == 0 && ET + 4 >= 68), "fused: whole tokens per wavefront row");
   static_assert((KC * ET / 4) % 64 == 0, "a W transfer stays inside one slot");
   static_assert(PER_X * (S - 1) <= 63, "vmcnt range");
-  static_assert(KC % XV == 0 && 256 % KC == 0 && (S == 3 || S == 4), "chunking");
+  static_assert(KC % XV == 0 && 256 % KC == 0 && S >= 2 && S <= 4, "chunking");
   static_assert(TT * LGP + (KP - 1) * NWP * AT * BT * 4 * 64 <= S * STG, "the logit tile fits in the stages");
   static_assert(E % ET == 0, "whole expert tiles");
   static_assert(S * STG * 4 <= 160 * 1024, "LDS");
@@ -686,29 +686,32 @@ hipError_t launch_route_logits(const RouteLaunch &L) {
   switch (L.E) {
     // chunk length, stage count and refill order as measured fastest; chunks
     // of 16 steps need too many registers for the deeper counter stacks of
-    // K > 4096
+    // K > 4096.  The two-part 64 x 64 tiles take 16-step chunks (x row pieces
+    // of 64 bytes for fp32, 32 for bf16) in two stages (three for bf16 x):
+    // 48.7 against 49.4 us at M = 4096, K = 2048, E = 256 for 8-step chunks in
+    // four stages (bf16 x 51.4 against 52.1), E = 512 and 1024 0.5-1.7 us less
     case 256:
       if (!L.xf) {
-        if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
+        if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 16, 3, 2, true, true>>(L);
         return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
       }
-      if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 8, 4, 2, true, false>>(L);
+      if (two) return launch_logits_c<SplitCfg<256, 64, 2, 2, 2, 16, 2, 2, true, false>>(L);
       if (L.K > 4096) return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 8, 4, 1, true, false>>(L);
       return launch_logits_c<SplitCfg<256, 128, 2, 2, 2, 16, 3, 1, true, false>, 3>(L);
     case 512:
       if (!L.xf) {
-        if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
+        if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 16, 3, 2, true, true>>(L);
         return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
       }
-      if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 8, 4, 2, true, false>>(L);
+      if (two) return launch_logits_c<SplitCfg<512, 64, 2, 2, 2, 16, 2, 2, true, false>>(L);
       if (L.K > 4096) return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 8, 4, 1, true, false>>(L);
       return launch_logits_c<SplitCfg<512, 128, 2, 2, 2, 16, 3, 1, true, false>, 3>(L);
     case 1024:
       if (!L.xf) {
-        if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true, true>>(L);
+        if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 16, 3, 2, true, true>>(L);
         return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true, true>, 3>(L);
       }
-      if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 8, 4, 2, true, false>>(L);
+      if (two) return launch_logits_c<SplitCfg<1024, 64, 2, 2, 2, 16, 2, 2, true, false>>(L);
       if (L.K > 4096) return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 8, 4, 1, true, false>>(L);
       return launch_logits_c<SplitCfg<1024, 128, 2, 2, 2, 16, 3, 1, true, false>, 3>(L);
     default: return hipErrorInvalidValue;
