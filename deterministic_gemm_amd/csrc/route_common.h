@@ -19,6 +19,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <type_traits>
 
 #include "../../include/dr.h"
 
@@ -75,6 +76,64 @@ __device__ __forceinline__ uint32_t rank_key(float v) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
   if ((u & 0x7FFFFFFFu) == 0u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// rank_key(v) + 1 in fewer steps: adding +0 turns -0 into +0 (and leaves
+// every other value, subnormals included, as it is), the sign bit spread by an
+// arithmetic shift and or-ed with the top bit is the mask that flips a
+// negative value whole and a positive one's top bit, and NaN gets 1.
+__device__ __forceinline__ uint32_t select_key(float v) {
+  const uint32_t u = f2u(v + 0.0f);
+  const uint32_t flip = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u;
+  return (v != v) ? 1u : (u ^ flip) + 1u;
+}
+
+// Batcher's odd-even merge sort on N = 2^p elements as a list of
+// compare-exchange pairs (a < b), built at compile time.
+template <int N>
+struct OddEvenNet {
+  static constexpr int count() {
+    int c = 0;
+    for (int p = 1; p < N; p <<= 1)
+      for (int k = p; k >= 1; k >>= 1)
+        for (int j = k % p; j + k < N; j += 2 * k)
+          for (int i = 0; i < k && i + j + k < N; ++i)
+            if ((i + j) / (2 * p) == (i + j + k) / (2 * p)) ++c;
+    return c;
+  }
+  static constexpr int C = count();
+  struct Pairs {
+    int a[C > 0 ? C : 1], b[C > 0 ? C : 1];
+  };
+  static constexpr Pairs make() {
+    Pairs t{};
+    int c = 0;
+    for (int p = 1; p < N; p <<= 1)
+      for (int k = p; k >= 1; k >>= 1)
+        for (int j = k % p; j + k < N; j += 2 * k)
+          for (int i = 0; i < k && i + j + k < N; ++i)
+            if ((i + j) / (2 * p) == (i + j + k) / (2 * p)) {
+              t.a[c] = i + j;
+              t.b[c] = i + j + k;
+              ++c;
+            }
+    return t;
+  }
+  static constexpr Pairs pairs = make();
+};
+
+// Sorts N 64-bit words in descending order, each compare-exchange one 64-bit
+// comparison and two selects per word.
+template <int N, int I = 0>
+__device__ __forceinline__ void sort_desc(uint64_t (&c)[N]) {
+  if constexpr (I < OddEvenNet<N>::C) {
+    constexpr int a = OddEvenNet<N>::pairs.a[I], b = OddEvenNet<N>::pairs.b[I];
+    const uint64_t x = c[a], y = c[b];
+    const bool sw = x < y;
+    c[a] = sw ? y : x;
+    c[b] = sw ? x : y;
+    sort_desc<N, I + 1>(c);
+  }
 }
 
 // ---------------------------------------------------------------- tree
@@ -434,11 +493,66 @@ __device__ void route_select_rows(const float (&v)[E / LT], float *rp, int64_t m
   };
   const int k = a.k;
 
-  uint32_t key[V];
+  // The lowest lane of the group holding the maximum x == rm.
+  const auto first_lane = [&](uint32_t x, uint32_t rm) -> bool {
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(x == rm);
+    if constexpr (LT == 64) {
+      return lane == static_cast<int>(__builtin_ctzll(bal));
+    } else {
+      const uint32_t bits = static_cast<uint32_t>(bal >> (lane & (64 - LT))) & static_cast<uint32_t>((1ull << LT) - 1);
+      return q == static_cast<int>(__builtin_ctz(bits));
+    }
+  };
+  // the winner's records for rank r: expert q*V + slot, its key, and from
+  // rank k-1 on its exact value, assembled from the values' bits under masks
+  // the compiler cannot see through (a select chain over v becomes an
+  // indexed read of v, which it serves from LDS addressed by the linear
+  // thread id -- read from the dispatch packet in every wavefront)
+  const auto record = [&](int r, int slot, uint32_t rm) {
+    rp[r] = __builtin_bit_cast(float, q * V + slot);
+    rp[33 + r] = __builtin_bit_cast(float, rm);
+    if (r >= k - 1) {
+      uint32_t e = 0;
 #pragma unroll
-  for (int j = 0; j < V; ++j) key[j] = rank_key(v[j]) + 1u;
+      for (int j = 0; j < V; ++j) {
+        uint32_t mj = (j == slot) ? ~0u : 0u;
+        asm volatile("" : "+v"(mj));
+        e |= f2u(v[j]) & mj;
+      }
+      rp[66 + (r - (k - 1))] = u2f(e);
+    }
+  };
+  const int rounds = (k < E) ? k + 1 : k;
 
-  uint32_t lm = lane_max<V>(key);
+  // Up to 16 values per lane: each lane sorts its (key, slot) pairs once --
+  // larger key first, equal keys by ascending slot, as one 64-bit word of
+  // key and V-1-slot -- so a round compares the lanes' heads and the winner
+  // pops its head: the winner is the group's lowest lane whose head is the
+  // maximum, and its head is its lowest slot holding that key, which is the
+  // larger-value-first, lower-index-first order over the group.  The slots
+  // follow the keys as a packed list of log2(V)-bit fields.  With more values
+  // per lane a round scans the lane's keys instead.
+  constexpr bool SORTED = V >= 2 && V <= 16;
+  constexpr int SB = V >= 16 ? 4 : V >= 8 ? 3 : V >= 4 ? 2 : 1;
+  using PackT = typename std::conditional<(SB * V > 32), uint64_t, uint32_t>::type;
+  uint32_t key[V];
+  PackT slots = 0;
+  if constexpr (SORTED) {
+    uint64_t c[V];
+#pragma unroll
+    for (int j = 0; j < V; ++j) c[j] = (static_cast<uint64_t>(select_key(v[j])) << 32) | static_cast<uint32_t>(V - 1 - j);
+    sort_desc<V>(c);
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      key[j] = static_cast<uint32_t>(c[j] >> 32);
+      slots |= static_cast<PackT>(static_cast<uint32_t>(c[j])) << (SB * j);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < V; ++j) key[j] = select_key(v[j]);
+  }
+
+  uint32_t lm = SORTED ? key[0] : lane_max<V>(key);
   const uint32_t top = group_max(lm);
   const float mx = key_value(top);
 
@@ -457,38 +571,39 @@ __device__ void route_select_rows(const float (&v)[E / LT], float *rp, int64_t m
     s = group_sum(u[0]);
   }
 
-  const int rounds = (k < E) ? k + 1 : k;
   uint32_t rm = top;
-  for (int r = 0; r < rounds; ++r) {
-    if (r > 0) {
-      lm = lane_max<V>(key);
-      rm = group_max(lm);
+  if constexpr (SORTED) {
+    for (int r = 0; r < rounds; ++r) {
+      if (r > 0) rm = group_max(key[0]);
+      const bool win = first_lane(key[0], rm);
+      if (win) record(r, V - 1 - static_cast<int>(slots & static_cast<PackT>(V - 1)), rm);
+      // the pop as bit selects under an all-ones / all-zeros mask the
+      // compiler cannot see through: as plain selects it rewrites key[j] as
+      // the sorted list indexed by the lane's pop count, a chain of compares
+      // and selects per element
+      uint32_t wm = win ? ~0u : 0u;
+      asm volatile("" : "+v"(wm));
+#pragma unroll
+      for (int j = 0; j + 1 < V; ++j) key[j] = (key[j + 1] & wm) | (key[j] & ~wm);
+      key[V - 1] = key[V - 1] & ~wm;
+      slots = win ? static_cast<PackT>(slots >> SB) : slots;
     }
-    // the group's lowest lane holding the maximum, then its lowest slot:
-    // the slots equal to the maximum as a bit mask, its lowest set bit
-    const uint64_t bal = __builtin_amdgcn_ballot_w64(lm == rm);
-    bool win;
-    if constexpr (LT == 64) {
-      win = lane == static_cast<int>(__builtin_ctzll(bal));
-    } else {
-      const uint32_t bits = static_cast<uint32_t>(bal >> (lane & (64 - LT))) & static_cast<uint32_t>((1ull << LT) - 1);
-      win = q == static_cast<int>(__builtin_ctz(bits));
-    }
-    uint32_t hit[V];
-#pragma unroll
-    for (int j = 0; j < V; ++j) hit[j] = (key[j] == rm) ? (1u << j) : 0u;
-    const int li = static_cast<int>(__builtin_ctz(lane_or<V>(hit) | (1u << (V - 1))));
-#pragma unroll
-    for (int j = 0; j < V; ++j) key[j] = (win && j == li) ? 0u : key[j];
-    if (win) {
-      rp[r] = __builtin_bit_cast(float, q * V + li);
-      rp[33 + r] = __builtin_bit_cast(float, rm);
-      if (r >= k - 1) {
-        float exact = v[0];
-#pragma unroll
-        for (int j = 1; j < V; ++j) exact = (j == li) ? v[j] : exact;
-        rp[66 + (r - (k - 1))] = exact;
+  } else {
+    for (int r = 0; r < rounds; ++r) {
+      if (r > 0) {
+        lm = lane_max<V>(key);
+        rm = group_max(lm);
       }
+      // the group's lowest lane holding the maximum, then its lowest slot:
+      // the slots equal to the maximum as a bit mask, its lowest set bit
+      const bool win = first_lane(lm, rm);
+      uint32_t hit[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) hit[j] = (key[j] == rm) ? (1u << j) : 0u;
+      const int li = static_cast<int>(__builtin_ctz(lane_or<V>(hit) | (1u << (V - 1))));
+#pragma unroll
+      for (int j = 0; j < V; ++j) key[j] = (win && j == li) ? 0u : key[j];
+      if (win) record(r, li, rm);
     }
   }
 

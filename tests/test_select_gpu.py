@@ -47,16 +47,22 @@ def _special_logits(rng, M, E):
     lg[4, E - 1] = -1.0
     lg[5, 1::3] = lg[5, 0]                 # many exact ties
     lg[6] = np.round(lg[6] * 4) / 4        # coarse values, ties throughout
+    # signed zeros on top, tied by index: the margin's exact values keep
+    # their signs
+    lg[7] = -(np.abs(lg[7]) + 0.5)
+    lg[7, 3::9] = -0.0
+    lg[7, 7::9] = 0.0
     return lg
 
 
 @pytest.mark.parametrize("E,k,M", [(64, 1, 90), (64, 32, 90), (128, 8, 90), (256, 8, 90), (256, 32, 90),
                                    (512, 10, 90), (1024, 8, 90), (256, 8, 1100), (64, 32, 1100), (512, 10, 1100),
-                                   (512, 1, 90), (512, 32, 90), (1024, 32, 90)])
+                                   (512, 1, 90), (512, 32, 90), (1024, 32, 90), (128, 8, 1100), (1024, 10, 1100)])
 def test_route_select_matches_oracle(dr, E, k, M):
     """One wavefront per token (M <= 1024, and E = 1024; from 512 experts the
     64-lane rounds, at k = 1, 10 and 32) and several tokens per wavefront
-    (larger M) against the oracle."""
+    (larger M: 4 to 16 values per lane, whose lanes sort their values once,
+    and 32 at E = 1024, whose rounds scan them) against the oracle."""
     rng = np.random.default_rng(7 * E + k + M)
     lg = _special_logits(rng, M, E)
     for renorm in (False, True):
