@@ -597,7 +597,9 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 
 // Grouped (per-expert) product: expert e owns output rows [offsets[e],
 // offsets[e+1]) and multiplies them by W[e].  Row tiles never straddle two
-// experts: expert e has ceil(count_e / BM) of them, numbered after those of
+// experts: expert e has ceil(count_e / BM) of them -- or one of the taller
+// tile when BM < count_e <= its height, which streams W[e]'s column strip
+// once where a full and a ragged tile would stream it twice -- numbered after those of
 // experts < e, T in all; a workgroup finds the expert of its row tile by a
 // scan of the tile counts in LDS.  Workgroups go to the eight XCDs in turn
 // (linear index L to XCD L % 8); XCD c takes the c-th contiguous eighth of
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 // or position, and the same bits as dr_gemm_bf16 of that row with W[e].
 constexpr int GG_EMAX = 1024;
 
-template <class C, bool BUF>
+template <class C, class CT, bool BUF>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t *__restrict__ x, int64_t Mx,
                                                                  const int32_t *__restrict__ rows,
                                                                  const uint16_t *__restrict__ W,
@@ -618,7 +620,12 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
                                                                  int64_t P, float *__restrict__ out, int K, int N,
                                                                  int ncol) {
   constexpr int EPL = (GG_EMAX + C::NT - 1) / C::NT;  // experts per lane in the scan
-  __shared__ __attribute__((aligned(16))) char smem[C::S * C::STAGE];
+  // CT: the taller tile, for an expert of more than C::BM and at most CT::BM
+  // rows (CT = C: none)
+  constexpr bool TALL = CT::BM > C::BM;
+  static_assert(CT::NT == C::NT && CT::BN == C::BN && CT::BM >= C::BM, "tile pair");
+  constexpr int SMEM = C::S * C::STAGE > CT::S * CT::STAGE ? C::S * C::STAGE : CT::S * CT::STAGE;
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int32_t tstart[GG_EMAX + 1];
   __shared__ int32_t wsum[C::NW];
   __shared__ int32_t found;
@@ -628,7 +635,8 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = EPL * t + i;
-    cnt[i] = (e < E) ? (offsets[e + 1] - offsets[e] + C::BM - 1) / C::BM : 0;
+    const int c = (e < E) ? offsets[e + 1] - offsets[e] : 0;
+    cnt[i] = (TALL && c > C::BM && c <= CT::BM) ? 1 : (c + C::BM - 1) / C::BM;
     v += cnt[i];
   }
   const int mine = v;
@@ -665,8 +673,11 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   const int64_t lo = offsets[e], mend = offsets[e + 1];
   if (lo < 0 || mend > P || mend < lo) return;  // inconsistent offsets: nothing is written outside out
   const int64_t m0 = lo + static_cast<int64_t>(tile - tstart[e]) * C::BM;
-  gemm_tile<C, float, true, BUF>(x, rows, Mx, W + static_cast<int64_t>(e) * K * N, out, m0, mend, K, N,
-                                 (slot % ncol) * C::BN, smem);
+  const uint16_t *We = W + static_cast<int64_t>(e) * K * N;
+  if (TALL && mend - lo > C::BM && mend - lo <= CT::BM)
+    gemm_tile<CT, float, true, BUF>(x, rows, Mx, We, out, lo, mend, K, N, (slot % ncol) * C::BN, smem);
+  else
+    gemm_tile<C, float, true, BUF>(x, rows, Mx, We, out, m0, mend, K, N, (slot % ncol) * C::BN, smem);
 }
 
 // Small batches (M <= 128): one workgroup per 16-column strip of W, holding
@@ -980,21 +991,27 @@ static hipError_t launch_strip(const uint16_t *x, const uint16_t *W, OutT *out, 
   }
 }
 
-template <class C>
+// CT: a taller tile for experts of C::BM + 1 .. CT::BM rows, which then take
+// one row tile instead of a full one and a ragged one (buffer-descriptor path
+// only: with 64-bit addresses its registers spill)
+template <class C, class CT = C>
 static hipError_t launch_grouped_c(const uint16_t *x, int64_t Mx, const int32_t *rows, const uint16_t *W,
                                    const int32_t *offsets, int64_t E, int64_t P, int64_t K, int64_t N, float *out,
                                    hipStream_t stream) {
   // enough row tiles for any split of P rows over E experts, in eight
-  // equal shares, each with all its column tiles
+  // equal shares, each with all its column tiles (a tall tile takes the
+  // place of two)
   const int64_t tiles = (P + C::BM - 1) / C::BM + E;
   const int64_t ncol = N / C::BN;
   const dim3 grid(static_cast<uint32_t>(8 * ((tiles + 7) / 8) * ncol));
   if (gemm_buf_ok(Mx, K, N))
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C, true>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
-                       static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N), static_cast<int>(ncol));
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C, CT, true>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W,
+                       offsets, static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N),
+                       static_cast<int>(ncol));
   else
-    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C, false>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W, offsets,
-                       static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N), static_cast<int>(ncol));
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<C, C, false>), grid, dim3(C::NT), 0, stream, x, Mx, rows, W,
+                       offsets, static_cast<int>(E), P, out, static_cast<int>(K), static_cast<int>(N),
+                       static_cast<int>(ncol));
   return hipGetLastError();
 }
 
@@ -1011,7 +1028,8 @@ hipError_t launch_grouped_gemm_bf16(const uint16_t *x, int64_t Mx, const int32_t
   // wins (271 vs 289 us).  The large tile runs the rotated loop over
   // two-step stages: 416 against 430 us for the plain loop at 65536 rows.
   if (N % 256 == 0 && P >= 128 * E)
-    return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2, true>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
+    return launch_grouped_c<GemmCfg<256, 256, 2, 4, 64, 2, true>, GemmCfg<320, 256, 2, 4, 64, 2, true>>(
+        x, Mx, rows, W, offsets, E, P, K, N, out, stream);
   return launch_grouped_c<GemmCfg<128, 128, 4, 2, 64, 2>>(x, Mx, rows, W, offsets, E, P, K, N, out, stream);
 }
 

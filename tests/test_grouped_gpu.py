@@ -33,7 +33,8 @@ def _routes_and_groups(dr, M, k, E, seed):
 
 
 # 128 x 128 tiles below 128 rows per expert on average, 256 x 256 from there
-# (the last case: ragged groups of ~300 rows and a partial K stage)
+# (the last case: groups of ~300 rows, most in one 320-row tile, some in a
+# full and a ragged 256-row tile, and a partial K stage)
 @pytest.mark.parametrize("M,k,E,K,N", [(1, 1, 1, 32, 128), (5, 2, 8, 96, 128), (300, 4, 16, 256, 256),
                                        (700, 8, 64, 160, 384), (2048, 8, 256, 2048, 256), (1200, 8, 32, 160, 256)])
 def test_grouped_matches_dense_rows_and_oracle(M, k, E, K, N):
@@ -118,9 +119,45 @@ def test_grouped_out_of_range_rows_read_zero_rows():
     assert np.all(out[[0, 2, 4]] == K) and np.all(out[[1, 3]] == 0)
 
 
+def test_grouped_tall_tiles_at_their_bounds():
+    """From 256 rows per expert on average the 256 x 256 tile runs, and an
+    expert of 257 to 320 rows takes one 320-row tile instead of a full and a
+    ragged one: groups of exactly 256, 257, 288, 300, 320 and 321 rows (321:
+    a full tile and a one-row ragged tile), one row and none, with a partial
+    last K stage.  Every row equals the dense GEMM of that row with its
+    expert's weights, bit for bit; sampled rows lie within the tolerance of
+    the exact product."""
+    dr = require_gpu()
+    sizes = [257, 320, 321, 256, 1, 0, 300, 288]
+    E, K, N = len(sizes), 160, 512
+    off_h = np.r_[0, np.cumsum(sizes)].astype(np.int32)
+    P = int(off_h[-1])
+    g = np.random.default_rng(12)
+    xb = wl.to_bf16_bits(g.standard_normal((P, K)).astype(np.float32))
+    Wb = wl.to_bf16_bits((g.standard_normal((E, K, N)) * 0.02).astype(np.float32))
+    Wd = dev_bf16_bits(Wb)
+    note(f"grouped gemm tall tiles, groups {sizes}")
+    out = dr.grouped_gemm_bf16(dev_bf16_bits(xb), Wd, dev(off_h))
+    got = _u32(out)
+    for e in range(E):
+        if sizes[e] == 0:
+            continue
+        seg = slice(off_h[e], off_h[e + 1])
+        note(f"dense rows of expert {e} ({sizes[e]} rows)")
+        dense = dr.gemm_bf16(dev_bf16_bits(np.ascontiguousarray(xb[seg])), dev_bf16_bits(Wb[e]))
+        assert np.array_equal(got[seg], _u32(dense)), f"expert {e} ({sizes[e]} rows)"
+    sample = np.unique(np.r_[off_h[:-1][np.array(sizes) > 0], off_h[1:][np.array(sizes) > 0] - 1, g.integers(0, P, 32)])
+    e_of = np.searchsorted(off_h, sample, side="right") - 1
+    outh = out.cpu().numpy()
+    for p, e in zip(sample, e_of):
+        ref = oracle.gemm_bf16_ref(xb[p][None, :], Wb[e])[0]
+        assert np.abs(outh[p].astype(np.float64) - ref).max() <= TOL, (p, e)
+
+
 def test_grouped_full_size_sampled():
     """The routing workload's size: 8192 tokens, k=8 (65536 grouped rows, 193-324
-    per expert, so experts span one or two 256-row tiles), K=2048, N=1024,
+    per expert, so experts take one 256-row tile, one 320-row tile, or a
+    full and a ragged 256-row tile), K=2048, N=1024,
     E=256.  Sampled experts against the dense GEMM bit for bit, sampled rows
     against the oracle within the tolerance."""
     dr = require_gpu()
@@ -136,7 +173,11 @@ def test_grouped_full_size_sampled():
     got = _u32(out)
     off_h, rows_h = off.cpu().numpy(), rows.cpu().numpy()
     cnt = np.diff(off_h)
-    for e in sorted({int(np.argmax(cnt)), int(np.argmin(cnt)), 0, 77, E - 1}):
+    tall = np.nonzero((cnt > 256) & (cnt <= 320))[0]
+    picks = {int(np.argmax(cnt)), int(np.argmin(cnt)), 0, 77, E - 1}
+    if tall.size:
+        picks |= {int(tall[0]), int(tall[-1])}
+    for e in sorted(picks):
         seg = slice(off_h[e], off_h[e + 1])
         note(f"dense rows of expert {e} ({cnt[e]} rows)")
         dense = dr.gemm_bf16(dev_bf16_bits(np.ascontiguousarray(xb[rows_h[seg]])), Wd[e].contiguous())
