@@ -598,8 +598,9 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 // Grouped (per-expert) product: expert e owns output rows [offsets[e],
 // offsets[e+1]) and multiplies them by W[e].  Row tiles never straddle two
 // experts: expert e has ceil(count_e / BM) of them -- or one of the taller
-// tile when BM < count_e <= its height, which streams W[e]'s column strip
-// once where a full and a ragged tile would stream it twice -- numbered after those of
+// tile when BM < count_e <= its height (+ GG_TAIL rows, taken by a second
+// pass), which streams W[e]'s column strip once where a full and a ragged tile
+// would stream it twice -- numbered after those of
 // experts < e, T in all; a workgroup finds the expert of its row tile by a
 // scan of the tile counts in LDS.  Workgroups go to the eight XCDs in turn
 // (linear index L to XCD L % 8); XCD c takes the c-th contiguous eighth of
@@ -611,6 +612,12 @@ __global__ __launch_bounds__(C::NT) void gemm_bf16_kernel(const uint16_t *__rest
 // instruction sequence, so a row has the same bits whatever its group's size
 // or position, and the same bits as dr_gemm_bf16 of that row with W[e].
 constexpr int GG_EMAX = 1024;
+// An expert of up to this many rows past the taller tile's height takes the
+// taller tile and, in the same workgroup, a second pass over its last rows
+// (which streams the expert's weight strip again), instead of a second row
+// tile: with row tiles a multiple of the CUs, one more row tile is one more
+// round of workgroups.
+constexpr int GG_TAIL = 64;
 
 template <class C, class CT, bool BUF>
 __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t *__restrict__ x, int64_t Mx,
@@ -636,7 +643,7 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   for (int i = 0; i < EPL; ++i) {
     const int e = EPL * t + i;
     const int c = (e < E) ? offsets[e + 1] - offsets[e] : 0;
-    cnt[i] = (TALL && c > C::BM && c <= CT::BM) ? 1 : (c + C::BM - 1) / C::BM;
+    cnt[i] = (TALL && c > C::BM && c <= CT::BM + GG_TAIL) ? 1 : (c + C::BM - 1) / C::BM;
     v += cnt[i];
   }
   const int mine = v;
@@ -674,10 +681,20 @@ __global__ __launch_bounds__(C::NT) void grouped_gemm_bf16_kernel(const uint16_t
   if (lo < 0 || mend > P || mend < lo) return;  // inconsistent offsets: nothing is written outside out
   const int64_t m0 = lo + static_cast<int64_t>(tile - tstart[e]) * C::BM;
   const uint16_t *We = W + static_cast<int64_t>(e) * K * N;
-  if (TALL && mend - lo > C::BM && mend - lo <= CT::BM)
-    gemm_tile<CT, float, true, BUF>(x, rows, Mx, We, out, lo, mend, K, N, (slot % ncol) * C::BN, smem);
-  else
-    gemm_tile<C, float, true, BUF>(x, rows, Mx, We, out, m0, mend, K, N, (slot % ncol) * C::BN, smem);
+  const int n0 = (slot % ncol) * C::BN;
+  if (TALL && mend - lo > C::BM && mend - lo <= CT::BM + GG_TAIL) {
+    const int64_t mt = mend - lo <= CT::BM ? mend : lo + CT::BM;
+    gemm_tile<CT, float, true, BUF>(x, rows, Mx, We, out, lo, mt, K, N, n0, smem);
+    if (mt < mend) {
+      // the last rows, at most GG_TAIL (one wavefront band of the smaller
+      // tile holds them; the other skips): every wavefront is done with the
+      // LDS stages before the second pass refills them
+      __syncthreads();
+      gemm_tile<C, float, true, BUF>(x, rows, Mx, We, out, mt, mend, K, N, n0, smem);
+    }
+  } else {
+    gemm_tile<C, float, true, BUF>(x, rows, Mx, We, out, m0, mend, K, N, n0, smem);
+  }
 }
 
 // Small batches (M <= 128): one workgroup per 16-column strip of W, holding

@@ -120,15 +120,16 @@ def test_grouped_out_of_range_rows_read_zero_rows():
 
 
 def test_grouped_tall_tiles_at_their_bounds():
-    """From 256 rows per expert on average the 256 x 256 tile runs, and an
+    """From 256 rows per expert on average the 256 x 256 tile runs; an
     expert of 257 to 320 rows takes one 320-row tile instead of a full and a
-    ragged one: groups of exactly 256, 257, 288, 300, 320 and 321 rows (321:
-    a full tile and a one-row ragged tile), one row and none, with a partial
-    last K stage.  Every row equals the dense GEMM of that row with its
-    expert's weights, bit for bit; sampled rows lie within the tolerance of
-    the exact product."""
+    ragged one, and one of 321 to 384 rows that tile and a second pass over
+    its last rows in the same workgroup: groups of exactly 256, 257, 288,
+    300, 320, 321, 352 and 384 rows, 385 (a full and a ragged 256-row tile),
+    one row and none, with a partial last K stage.  Every row equals the
+    dense GEMM of that row with its expert's weights, bit for bit; sampled
+    rows lie within the tolerance of the exact product."""
     dr = require_gpu()
-    sizes = [257, 320, 321, 256, 1, 0, 300, 288]
+    sizes = [257, 320, 321, 256, 1, 0, 300, 288, 352, 384, 385]
     E, K, N = len(sizes), 160, 512
     off_h = np.r_[0, np.cumsum(sizes)].astype(np.int32)
     P = int(off_h[-1])
@@ -156,8 +157,8 @@ def test_grouped_tall_tiles_at_their_bounds():
 
 def test_grouped_full_size_sampled():
     """The routing workload's size: 8192 tokens, k=8 (65536 grouped rows, 193-324
-    per expert, so experts take one 256-row tile, one 320-row tile, or a
-    full and a ragged 256-row tile), K=2048, N=1024,
+    per expert, so experts take one 256-row tile, or one 320-row tile with a
+    second pass over their last rows past 320), K=2048, N=1024,
     E=256.  Sampled experts against the dense GEMM bit for bit, sampled rows
     against the oracle within the tolerance."""
     dr = require_gpu()
@@ -173,7 +174,7 @@ def test_grouped_full_size_sampled():
     got = _u32(out)
     off_h, rows_h = off.cpu().numpy(), rows.cpu().numpy()
     cnt = np.diff(off_h)
-    tall = np.nonzero((cnt > 256) & (cnt <= 320))[0]
+    tall = np.nonzero(cnt > 256)[0]
     picks = {int(np.argmax(cnt)), int(np.argmin(cnt)), 0, 77, E - 1}
     if tall.size:
         picks |= {int(tall[0]), int(tall[-1])}
