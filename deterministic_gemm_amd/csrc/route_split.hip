@@ -583,11 +583,12 @@ __global__ __launch_bounds__(256) void route_split_epilogue32_kernel(int64_t M, 
 // Small batches: one wavefront per token, which finishes a token in fewer
 // dependent steps than several tokens sharing a wavefront; four tokens per
 // workgroup.  The token's logits are widened into an LDS row first; the
-// selection then sees the values as given and writes no logits.  Up to 256
-// experts (four values per lane) the row-wise kernel's per-slot ballots take
-// the fewest steps; from 512, route_select_rows on all 64 lanes (measured,
-// selection alone at E = 512, k = 10: 5.7-6.9 against 6.6-7.6 us for M = 1
-// .. 1024; at E = 256 it was 0.1-0.2 us slower).
+// selection then sees the values as given and writes no logits.  From 256
+// experts, route_select_rows on all 64 lanes (each lane sorts its values
+// once, a round is a wavefront maximum of the lanes' heads and one ballot):
+// selection alone at E = 256, k = 8 4.0 against 4.3 us at M = 1 and 4.6
+// against 4.7-4.8 at M = 64-1024 for route_token's per-slot ballots, which
+// fewer experts keep.
 template <int E>
 __global__ __launch_bounds__(256) void route_select_wave_kernel(int64_t M, EpilogueArgs ea) {
   __shared__ __attribute__((aligned(16))) float rows[4][E + 4];
@@ -602,7 +603,7 @@ __global__ __launch_bounds__(256) void route_select_wave_kernel(int64_t M, Epilo
   EpilogueArgs a = ea;
   a.logits = nullptr;
   a.logit_bf16 = 0;
-  if constexpr (E >= 512) {
+  if constexpr (E >= 256) {
     constexpr int V = E / 64;
     float v[V];
 #pragma unroll
